@@ -1,0 +1,321 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+python bench.py [--steps K] [--warmup W] [--config NAME] [--seq S] [--no-cpu]
+
+One step is one pass of the hot path over resident synthetic inputs:
+  * dense configs: one attn_fwd call (all heads, all q-blocks);
+  * block-sparse: build the kept list, then attn_fwd_blocksparse;
+  * quantised: quantise Q, K (INT8 per block) and V (FP8 per channel), build
+    the kept list, then attn_fwd_qbsa.
+W untimed steps, then exactly K timed steps between two device
+synchronisations; HIP events on the launch stream give the per-step times.
+Prints one JSON line. The default workload is the dense B=1 N=40 S=8192 D=128
+operator shape, on which the headline metric is quoted.
+
+--copy-calibration BYTES runs a plain device copy of BYTES bytes (used to scale
+the FETCH_SIZE / WRITE_SIZE counters of a counter run to bytes).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS (executed + dense-equiv), % MFMA peak, S=8K–64K"
+PEAK_BF16 = 2500.0   # TFLOP/s, MI355X published dense bf16 MFMA
+PEAK_FP8 = 5000.0    # TFLOP/s (fp8) / TOP/s (int8), published dense
+HBM_PEAK = 8000.0    # GB/s
+KERNEL_SOURCES = {
+    "dense": ["attn_bf16.hip"], "blocksparse": ["attn_bf16.hip", "quant.hip"],
+    "qbsa": ["attn_qbsa.hip", "quant.hip"],
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "quantized_attention_tiled_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def flop_counts(w):
+    """(executed, useful, dense_equivalent) flop counts: 2 D flops per (q, k)
+    pair for Q.K^T and again for P.V. Executed counts the (row, key) pairs of
+    the tiles the kernel processes: whole kept 128-key blocks for block-sparse;
+    for causal masks, each 64-row wave slice runs over the keys up to the end
+    of the 64-key tile that holds its last row's diagonal."""
+    D = w.D
+    if w.layout == "TND":
+        lens = np.diff(w.cu_seqlens_q)
+        dense = useful = executed = 0
+        for L in lens:
+            L = int(L)
+            dense += L * L
+            if w.sparse_mode in (2, 3):          # Lq == Lkv here, so both causal modes coincide
+                useful += L * (L + 1) // 2
+                for r0 in range(0, L, 64):
+                    r1 = min(L, r0 + 64)
+                    executed += (r1 - r0) * min(L, ((r1 + 63) // 64) * 64)
+            else:
+                useful += L * L
+                executed += L * L
+        f = 4 * D * w.Nq
+        return f * executed, f * useful, f * dense
+    dense = w.B * w.Nq * w.Sq * w.Skv
+    if w.keep is not None:
+        blk = np.minimum(128, w.Skv - np.arange(w.keep.shape[3]) * 128)
+        rows = np.minimum(128, w.Sq - np.arange(w.keep.shape[2]) * 128)
+        per_row = (w.keep.astype(np.int64) * blk[None, None, None, :]).sum(axis=3)
+        pairs = int((per_row * rows[None, None, :]).sum())
+        return 4 * D * pairs, 4 * D * pairs, 4 * D * dense
+    return 4 * D * dense, 4 * D * dense, 4 * D * dense
+
+
+def algorithmic_bytes(w, kind):
+    """Minimum HBM bytes of one step: read every input once, write every output once."""
+    el = lambda a: int(np.prod(a.shape))  # noqa: E731
+    ml = 2 * 4 * w.Nq * w.Sq * (w.B if w.layout == "BNSD" else 1)
+    if kind == "dense":
+        return 2 * (el(w.q) + el(w.k) + el(w.v)) + 2 * el(w.q) + ml
+    if kind == "blocksparse":
+        return 2 * (el(w.q) + el(w.k) + el(w.v)) + 2 * el(w.q) + ml + el(w.keep) + 4 * el(w.keep)
+    # quantised: bf16 in, int8/fp8 codes out and read back, bf16 O
+    return (2 * (el(w.q) + el(w.k) + el(w.v)) + (el(w.q) + el(w.k) + el(w.v)) * 2 + 2 * el(w.q) + ml
+            + 5 * el(w.keep))
+
+
+def run_cpu_baseline(w, kind, budget_s: float):
+    """Time the oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from workloads import bf16_bits_to_f32
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    f64 = lambda x: bf16_bits_to_f32(x).astype(np.float64)  # noqa: E731
+    D = w.D
+    t0 = time.perf_counter()
+    flops = 0
+    done = []
+    if kind == "dense" and w.layout == "BNSD":
+        k0, v0 = f64(w.k[0, 0]), f64(w.v[0, 0])
+        q0 = f64(w.q[0, 0])
+        qb = 0
+        while time.perf_counter() - t0 < budget_s and qb * 128 < w.Sq:
+            rows = np.arange(qb * 128, min(w.Sq, qb * 128 + 128))
+            oracle.attention_rows(q0, k0, v0, w.scale, rows)
+            flops += 4 * D * len(rows) * w.Skv
+            qb += 1
+        sample = f"head 0, q-blocks 0..{qb - 1} ({qb * 128} rows x {w.Skv} keys), plain float64 score matrix"
+    elif kind == "dense":
+        cu = w.cu_seqlens_q
+        g = w.Nq // w.Nkv
+        b = h = 0
+        while time.perf_counter() - t0 < budget_s and b < w.B:
+            s0, s1 = int(cu[b]), int(cu[b + 1])
+            L = s1 - s0
+            for qb in range((L + 127) // 128):
+                rows = np.arange(qb * 128, min(L, qb * 128 + 128))
+                oracle.attention_rows(f64(w.q[s0:s1, h]), f64(w.k[s0:s1, h // g]), f64(w.v[s0:s1, h // g]), w.scale,
+                                      rows, sparse_mode=w.sparse_mode)
+                flops += 4 * D * len(rows) * min(L, int(rows[-1]) + 1)
+            done.append((b, h))
+            b += 1
+        sample = f"head 0 of sequences {[d[0] for d in done]}, causal rows (useful flops)"
+    elif kind == "blocksparse":
+        q0, k0, v0 = f64(w.q[0, 0]), f64(w.k[0, 0]), f64(w.v[0, 0])
+        qb = 0
+        while time.perf_counter() - t0 < budget_s and qb * 128 < w.Sq:
+            oracle.attention_block_sparse(q0, k0, v0, w.scale, w.keep[0, 0], qblocks=[qb])
+            flops += 4 * D * 128 * 128 * int(w.keep[0, 0, qb].sum())
+            qb += 1
+        sample = f"head 0, q-blocks 0..{qb - 1}, kept blocks gathered (executed flops)"
+    else:
+        qc, qs = oracle.quantize_qk_perblock_int8(f64(w.q[:, :1]))
+        kc, ks = oracle.quantize_qk_perblock_int8(f64(w.k[:, :1]))
+        vc, vs = oracle.quantize_v_perchannel_fp8(f64(w.v[:, :1]))
+        qb = 0
+        while time.perf_counter() - t0 < budget_s and qb * 128 < w.Sq:
+            kept = np.nonzero(w.keep[0, 0, qb])[0]
+            oracle.qbsa_qblock(qc[0, 0], kc[0, 0], vc[0, 0], qs[0, 0, qb], ks[0, 0], vs[0, 0], w.scale, kept, qb)
+            flops += 4 * D * 128 * 128 * len(kept)
+            qb += 1
+        sample = f"head 0: quantise Q/K/V, then q-blocks 0..{qb - 1} of the tiled FP8 schedule (executed ops)"
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": sample + f"; {flops / 1e9:.2f} GFLOP in {dt:.1f} s", "seconds": round(dt, 2)}
+
+
+def load_traffic(config_name: str, kind: str, launch_bytes_alg: float):
+    path = os.path.join(ROOT, "profiles", f"traffic_{config_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_sha") != source_hash(kind):
+        return None          # kernel changed since the counters were taken
+    return t.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2_dense_8k")
+    ap.add_argument("--seq", type=int, default=None, help="override S (dense BNSD configs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=None)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        return 2
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        print("bench.py runs as a single process on one GPU.", file=sys.stderr)
+        return 2
+    import torch
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return 0
+
+    import quantized_attention_tiled_amd as qa
+    from workloads import CONFIGS, make_workload
+
+    qa.load()
+    cfg = CONFIGS[a.config]
+    kind = cfg["kind"]
+    log(f"generating {a.config} {'S=' + str(a.seq) if a.seq else ''}")
+    w = make_workload(a.config, S=a.seq) if a.seq else make_workload(a.config)
+    name = a.config if not a.seq else f"{a.config}_S{a.seq}"
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(w.q), up(w.k), up(w.v)
+    o = torch.empty_like(q)
+    ml_shape = (w.B, w.Nq, w.Sq) if w.layout == "BNSD" else (w.Nq, w.Sq)
+    m = torch.empty(ml_shape, dtype=torch.float32, device=dev)
+    l = torch.empty(ml_shape, dtype=torch.float32, device=dev)
+    if kind == "dense":
+        cu = w.cu_seqlens_q.tolist() if w.layout == "TND" else None
+
+        def step():
+            qa.attn_fwd(q, k, v, scale=w.scale, layout=w.layout, sparse_mode=w.sparse_mode, cu_seqlens_q=cu,
+                        cu_seqlens_kv=cu, out=o, softmax_max=m, softmax_sum=l)
+        dtype, peak = "bf16", PEAK_BF16
+    elif kind == "blocksparse":
+        keep = torch.from_numpy(w.keep).to(dev)
+        counts = torch.empty(w.keep.shape[:3], dtype=torch.int32, device=dev)
+        idx = torch.empty(w.keep.shape, dtype=torch.int32, device=dev)
+
+        def step():
+            qa.build_kv_block_list(keep, counts, idx)
+            qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=w.scale, out=o, softmax_max=m, softmax_sum=l)
+        dtype, peak = "bf16", PEAK_BF16
+    else:
+        keep = torch.from_numpy(w.keep).to(dev)
+        counts = torch.empty(w.keep.shape[:3], dtype=torch.int32, device=dev)
+        idx = torch.empty(w.keep.shape, dtype=torch.int32, device=dev)
+        qq = torch.empty(q.shape, dtype=torch.int8, device=dev)
+        kq = torch.empty(k.shape, dtype=torch.int8, device=dev)
+        vq = torch.empty(v.shape, dtype=torch.uint8, device=dev)
+        nb = (w.Sq + 127) // 128
+        qs = torch.empty((w.B, w.Nq, nb), dtype=torch.float32, device=dev)
+        ks = torch.empty((w.B, w.Nkv, nb), dtype=torch.float32, device=dev)
+        vs = torch.empty((w.B, w.Nkv, w.D), dtype=torch.float32, device=dev)
+
+        def step():
+            qa.quantize_qk_perblock_int8(q, qq, qs)
+            qa.quantize_qk_perblock_int8(k, kq, ks)
+            qa.quantize_v_perchannel_fp8(v, vq, vs)
+            qa.build_kv_block_list(keep, counts, idx)
+            qa.attn_fwd_qbsa(qq, kq, vq, qs, ks, vs, counts, idx, scale=w.scale, out=o, softmax_max=m,
+                             softmax_sum=l)
+        dtype, peak = "int8/fp8", PEAK_FP8
+
+    log(f"warmup {a.warmup}")
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    log(f"timing {a.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(a.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)])
+    total_ms = ev[0].elapsed_time(ev[a.steps])
+    ms = total_ms / a.steps
+    ex, useful, dense = flop_counts(w)
+    value = ex / (ms * 1e-3) / 1e12
+    alg_bytes = algorithmic_bytes(w, kind)
+    traffic = load_traffic(name, kind, alg_bytes)
+    roof = {"bound": "mfma", "achieved": round(value, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(value / peak, 4), "traffic": traffic, "kernel": "attn_bf16_kernel" if kind != "qbsa"
+            else "attn_qbsa_kernel", "flop_per_launch": ex, "launch_ms": round(ms, 4)}
+    cpu = None
+    if not a.no_cpu:
+        log(f"cpu oracle baseline (~{a.cpu_seconds:.0f} s)")
+        cpu = run_cpu_baseline(w, kind, a.cpu_seconds)
+    if w.layout == "TND":
+        wl = f"{a.config}: {w.description}; T={w.Sq}"
+        conf = {"workload": wl, "layout": "TND", "sequences": int(w.B), "lengths": np.diff(w.cu_seqlens_q).tolist(),
+                "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D, "sparse_mode": w.sparse_mode}
+    else:
+        wl = f"{name}: {w.description}" + (f" (S overridden to {w.Sq})" if a.seq else "")
+        conf = {"workload": wl, "layout": "BNSD", "B": w.B, "N": w.Nq, "Nkv": w.Nkv, "S": w.Sq, "D": w.D}
+        if w.keep is not None:
+            conf["kept_fraction"] = round(float(w.keep.mean()), 4)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded, shapes of the pages' workloads)",
+        "config": conf, "roofline": roof, "cpu_baseline": cpu,
+        "detail": {"executed_tflops": round(value, 2), "dense_equiv_tflops": round(dense / (ms * 1e-3) / 1e12, 2),
+                   "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+                   "pct_mfma_peak": round(100 * value / peak, 2), "median_ms": round(float(np.median(per)), 4),
+                   "min_ms": round(float(per.min()), 4), "cv": round(float(per.std() / per.mean()), 4),
+                   "algorithmic_bytes": alg_bytes, "algorithmic_gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+                   "wall_s_timed": round(wall, 3), "kernel_source_sha": source_hash(kind)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,200 @@
+/*
+ * qattn.h -- C ABI of the fused, tiled attention forward for AMD MI355X (gfx950).
+ *
+ * What is computed (pages cited by title and section):
+ *   "Ascend NPU fused attention operator" guide (npu_fusion_attention),
+ *     section 2: O = Softmax(Mask(Q K^T * scale)) V, computed tile by tile with
+ *     an online softmax so the S x S score matrix is never stored;
+ *     section 3/4: head_num, input_layout (BNSD, TND), atten_mask with
+ *     1 = masked and shapes SS / B1SS / BNSS, scale, sparse_mode 2/3 causal,
+ *     cumulative sequence lengths for varlen;
+ *     section 5: outputs are the attention result plus softmax_max and
+ *     softmax_sum per query row;
+ *     section 7: GQA with Nq / Nkv an integer.
+ *   "EagleQBSA quantised block-sparse attention" article,
+ *     scheme-design section: Q/K INT8 per 128-token block, V FP8 E4M3 per
+ *     channel, P cast to FP8 before the P.V product;
+ *     the API call at its end: 128 x 128 block-sparse mask, per-tensor scale
+ *     arrays, num_key_value_heads, scale_value, bf16 output.
+ *   "MindIE SD FA_Power_Cap" page, InsertComm and BlockAttn steps: the same
+ *     attention is launched per head chunk and per query block; here every
+ *     launch over a head range and a q-block range writes exactly the bytes the
+ *     full call writes for that slice.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     allocates nothing, keeps no state between calls and keeps no pointer
+ *     after it returns. cu_seqlens arrays are HOST pointers, read during the
+ *     call only.
+ *   - Every call is asynchronous on the caller's HIP stream (`stream` is a
+ *     hipStream_t; NULL means the default stream). Buffers must stay alive
+ *     until the stream has passed the call.
+ *   - bf16 tensors are raw bfloat16 bits (uint16_t). Every pointer passed to a
+ *     kernel must be 16-byte aligned, and every innermost dimension is
+ *     contiguous.
+ *   - Validation happens on the host before any launch. On any error nothing
+ *     is launched and no output byte is written. Device data (mask contents,
+ *     NaN or Inf in inputs) is not inspected; kept-list entries outside
+ *     [0, KB) are skipped by the kernels, and counts are clamped to [0, KB].
+ *   - Return value: a QATTN_* status. qattn_last_error() returns a message
+ *     for the calling thread's most recent failure. Nothing throws across
+ *     the ABI.
+ *
+ * Layouts
+ *   BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D], o like q;
+ *         softmax_max / softmax_sum fp32 [B, Nq, Sq].
+ *   TND:  q [T, Nq, D], k/v [Tk, Nkv, D], o like q, with B sequences given
+ *         by host cumulative lengths (B + 1 entries, leading 0, non-
+ *         decreasing, last entry = T or Tk);
+ *         softmax_max / softmax_sum fp32 [Nq, T].
+ *   q-block: 128 consecutive query rows of one head. For TND, q-blocks are
+ *         numbered sequence by sequence: sequence b owns ceil(len_b / 128)
+ *         consecutive q-block numbers.
+ *   kv-block: 128 consecutive keys. QB = ceil(Sq / 128), KB = ceil(Skv / 128).
+ *
+ * Definitions fixed by this library where the pages are silent
+ *   - sparse_mode 2 keeps key j for query i when j <= i; sparse_mode 3 keeps it
+ *     when j <= i + Skv - Sq (i, j counted inside one sequence).
+ *   - softmax_max m_i = max over kept j of s_ij (s = q.k * scale); softmax_sum
+ *     l_i = sum over kept j of exp(s_ij - m_i). A row with no kept key gets
+ *     O = 0, m = -inf, l = 0.
+ *   - q-head h reads kv-head h / (Nq / Nkv).
+ *   - block keep masks use 1 = keep (the opposite of atten_mask).
+ *   - scale must be finite and > 0.
+ */
+#ifndef QATTN_H_
+#define QATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QATTN_OK 0
+#define QATTN_INVALID_ARGUMENT 1
+#define QATTN_UNSUPPORTED 2
+#define QATTN_MISALIGNED 3
+#define QATTN_HIP_ERROR 4
+
+#define QATTN_LAYOUT_BNSD 0
+#define QATTN_LAYOUT_TND 1
+
+#define QATTN_MASK_SS 0   /* atten_mask [Sq, Skv] shared by all batches and heads */
+#define QATTN_MASK_B1SS 1 /* atten_mask [B, 1, Sq, Skv] shared by heads */
+#define QATTN_MASK_BNSS 2 /* atten_mask [B, Nq, Sq, Skv] */
+
+#define QATTN_MAX_SEQS 256 /* TND: at most this many sequences per call */
+
+typedef uint16_t qattn_bf16; /* bfloat16 storage */
+
+/* Problem description shared by the three attention entry points. */
+typedef struct qattn_desc {
+  uint32_t struct_size;  /* sizeof(qattn_desc); checked for versioning */
+  int32_t layout;        /* QATTN_LAYOUT_BNSD or QATTN_LAYOUT_TND */
+  int32_t B;             /* batch (BNSD) or number of sequences (TND) */
+  int32_t Nq;            /* query heads (head_num) */
+  int32_t Nkv;           /* key/value heads; Nq % Nkv == 0 */
+  int32_t Sq;            /* BNSD: query length; TND: total query tokens T */
+  int32_t Skv;           /* BNSD: key length; TND: total key tokens Tk */
+  int32_t D;             /* head dimension: 64 or 128 */
+  float scale;           /* softmax scale, finite and > 0 */
+  int32_t sparse_mode;   /* 0: none / explicit mask; 2: causal top-left; 3: causal bottom-right */
+  const int32_t* cu_seqlens_q;  /* TND: host [B + 1] cumulative query lengths; else NULL */
+  const int32_t* cu_seqlens_kv; /* TND: host [B + 1] cumulative key lengths; else NULL */
+  const uint8_t* atten_mask;    /* BNSD only: device uint8, 1 = masked, 0 = kept; NULL = none */
+  int32_t mask_kind;            /* QATTN_MASK_SS / _B1SS / _BNSS when atten_mask != NULL */
+  int32_t head_begin;           /* subrange of q-heads [head_begin, head_end); -1, -1 = all */
+  int32_t head_end;
+  int32_t qblock_begin;         /* subrange of q-blocks [qblock_begin, qblock_end); -1, -1 = all */
+  int32_t qblock_end;
+} qattn_desc;
+
+/*
+ * attn_fwd -- dense bf16 attention forward (fused attention guide, sections
+ * 2-5 and 7; power-cap page, InsertComm/BlockAttn splitting).
+ *   q, k, v: bf16 in desc->layout; o: bf16, same shape as q.
+ *   softmax_max, softmax_sum: fp32 outputs (layouts above), each nullable.
+ *   Causal modes and an explicit atten_mask may be combined (a pair is kept
+ *   only when both keep it). atten_mask requires the BNSD layout.
+ *   Only rows of the requested head and q-block subrange are written.
+ */
+int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
+             qattn_bf16* o, float* softmax_max, float* softmax_sum, void* stream);
+
+/*
+ * build_kv_block_list -- compact a 128 x 128 block keep mask into, per
+ * (batch, q-head, q-block), the ascending kept kv-block indices (EagleQBSA
+ * article, API call: block_sparse_mask with block_shape [128, 128]).
+ *   keep:   device uint8 [B, N, QB, KB], nonzero = keep.
+ *   counts: device int32 [B, N, QB], number of kept blocks.
+ *   idx:    device int32 [B, N, QB, KB], kept indices ascending, then -1.
+ * The list is deterministic and reused by every subrange launch.
+ */
+int build_kv_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32_t* counts, int32_t* idx,
+                        void* stream);
+
+/*
+ * attn_fwd_blocksparse -- bf16 block-sparse attention (EagleQBSA article,
+ * BF16 BSA baseline; 128 x 128 blocks): each (batch, q-head, q-block) attends
+ * only to the keys of its kept kv-blocks, visited in list order; masked
+ * blocks are skipped, never computed.
+ *   desc: BNSD, sparse_mode 0, atten_mask NULL (else QATTN_UNSUPPORTED).
+ *   counts/idx: as produced by build_kv_block_list for [B, Nq, QB, KB].
+ */
+int attn_fwd_blocksparse(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k,
+                         const qattn_bf16* v, qattn_bf16* o, float* softmax_max, float* softmax_sum,
+                         const int32_t* counts, const int32_t* idx, void* stream);
+
+/*
+ * quantize_qk_perblock_int8 -- symmetric INT8 per (batch, head, 128-token
+ * block) (EagleQBSA article, scheme-design section):
+ *   scale = fp32(amax / 127); code = clamp(round_half_even(fp32(x / scale)), -127, 127);
+ *   both divisions IEEE binary32, correctly rounded; amax == 0 gives scale 0
+ *   and zero codes; a ragged last block uses only its rows.
+ *   x: bf16 BNSD [B, N, S, D]; x_q: int8 same shape; scale: fp32 [B, N, ceil(S/128)].
+ */
+int quantize_qk_perblock_int8(const qattn_bf16* x, int B, int N, int S, int D, int8_t* x_q, float* scale,
+                              void* stream);
+
+/*
+ * quantize_v_perchannel_fp8 -- E4M3FN per (batch, kv-head, channel) over all
+ * tokens (EagleQBSA article, scheme-design section):
+ *   scale = fp32(amax / 448); code = E4M3FN_round_half_even(clamp(fp32(v / scale), -448, 448)),
+ *   sign kept (a negative value rounding to zero gives 0x80); amax == 0 gives
+ *   scale 0 and zero codes.
+ *   v: bf16 BNSD [B, N, S, D]; v_q: E4M3FN bytes, same shape; scale: fp32 [B, N, D].
+ *   `scale` also holds the per-channel maximum between the kernels of one call.
+ */
+int quantize_v_perchannel_fp8(const qattn_bf16* v, int B, int N, int S, int D, uint8_t* v_q, float* scale,
+                              void* stream);
+
+/*
+ * attn_fwd_qbsa -- quantised block-sparse attention, EagleQBSA style
+ * (EagleQBSA article: scheme design, operator optimisation, API call).
+ * Per kept 128 x 128 block: s = (q_q . k_q^T) * q_scale[qb] * k_scale[kb] * scale
+ * with INT8 MFMA; online softmax in fp32; p cast to FP8 E4M3 (unscaled,
+ * round half even); acc += p8 . v_q with FP8 MFMA; O = acc * v_scale[d] / l,
+ * where l sums the unrounded p. Output bf16.
+ *   desc: BNSD, sparse_mode 0, atten_mask NULL.
+ *   q: int8 [B, Nq, Sq, D]; k: int8 [B, Nkv, Skv, D]; v: E4M3FN [B, Nkv, Skv, D];
+ *   q_scale: fp32 [B, Nq, QB]; k_scale: fp32 [B, Nkv, KB]; v_scale: fp32 [B, Nkv, D].
+ *   counts/idx: kept list [B, Nq, QB, KB]. softmax_max/sum nullable (the
+ *   article's softmax_lse_flag = 0 corresponds to NULL).
+ */
+int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, const uint8_t* v,
+                  const float* q_scale, const float* k_scale, const float* v_scale, const int32_t* counts,
+                  const int32_t* idx, qattn_bf16* o, float* softmax_max, float* softmax_sum, void* stream);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char* qattn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int qattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QATTN_H_ */

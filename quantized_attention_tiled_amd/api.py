@@ -1,0 +1,274 @@
+"""PyTorch-facing wrappers over the qattn C ABI.
+
+These functions only marshal arguments: they check dtypes, shapes and
+devices, allocate outputs with torch when the caller passes none, and call the
+library on the current HIP stream. Every step of the computation runs in the
+library's kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import LAYOUT_BNSD, LAYOUT_TND, MASK_B1SS, MASK_BNSS, MASK_SS, QattnDesc, check, load
+
+BLOCK = 128
+
+
+def _vp(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _cu(x) -> Optional[ctypes.Array]:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().tolist()
+    vals = [int(v) for v in x]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _ranges(head_range, qblock_range):
+    h = (-1, -1) if head_range is None else (int(head_range[0]), int(head_range[1]))
+    b = (-1, -1) if qblock_range is None else (int(qblock_range[0]), int(qblock_range[1]))
+    return h, b
+
+
+def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: int, scale: float,
+              sparse_mode: int = 0, cu_q=None, cu_kv=None, atten_mask: Optional[torch.Tensor] = None,
+              mask_kind: int = MASK_SS, head_range=None, qblock_range=None) -> QattnDesc:
+    d = QattnDesc()
+    d.struct_size = ctypes.sizeof(QattnDesc)
+    d.layout, d.B, d.Nq, d.Nkv, d.Sq, d.Skv, d.D = layout, B, Nq, Nkv, Sq, Skv, D
+    d.scale = float(scale)
+    d.sparse_mode = int(sparse_mode)
+    d.cu_seqlens_q = ctypes.cast(cu_q, ctypes.POINTER(ctypes.c_int32)) if cu_q is not None else None
+    d.cu_seqlens_kv = ctypes.cast(cu_kv, ctypes.POINTER(ctypes.c_int32)) if cu_kv is not None else None
+    d.atten_mask = atten_mask.data_ptr() if atten_mask is not None else None
+    d.mask_kind = int(mask_kind)
+    (d.head_begin, d.head_end), (d.qblock_begin, d.qblock_end) = _ranges(head_range, qblock_range)
+    return d
+
+
+def _mask_kind(mask: torch.Tensor, B: int, Nq: int, Sq: int, Skv: int) -> int:
+    if mask.dim() == 2 and tuple(mask.shape) == (Sq, Skv):
+        return MASK_SS
+    if mask.dim() == 4 and tuple(mask.shape) == (B, 1, Sq, Skv):
+        return MASK_B1SS
+    if mask.dim() == 4 and tuple(mask.shape) == (B, Nq, Sq, Skv):
+        return MASK_BNSS
+    raise ValueError(f"atten_mask shape {tuple(mask.shape)} is not SS, B1SS or BNSS for B={B} Nq={Nq} Sq={Sq} Skv={Skv}")
+
+
+def _outputs(q, out, softmax_max, softmax_sum, ml_shape):
+    if out is None:
+        out = torch.empty_like(q, dtype=torch.bfloat16)
+    if softmax_max is None:
+        softmax_max = torch.empty(ml_shape, dtype=torch.float32, device=q.device)
+    if softmax_sum is None:
+        softmax_sum = torch.empty(ml_shape, dtype=torch.float32, device=q.device)
+    return out, softmax_max, softmax_sum
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float = 1.0, layout: str = "BNSD",
+             sparse_mode: int = 0, atten_mask: Optional[torch.Tensor] = None,
+             cu_seqlens_q: Optional[Sequence[int]] = None, cu_seqlens_kv: Optional[Sequence[int]] = None,
+             head_range: Optional[Tuple[int, int]] = None, qblock_range: Optional[Tuple[int, int]] = None,
+             out: Optional[torch.Tensor] = None, softmax_max: Optional[torch.Tensor] = None,
+             softmax_sum: Optional[torch.Tensor] = None):
+    """Dense bf16 attention forward; returns (out, softmax_max, softmax_sum).
+
+    BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D]; m/l [B, Nq, Sq].
+    TND:  q [T, Nq, D], k/v [Tk, Nkv, D] plus cumulative lengths; m/l [Nq, T].
+    ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (BNSD only).
+    With a head or q-block range only that slice of the outputs is written.
+    """
+    lib = load()
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, torch.bfloat16, dev)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if layout == "BNSD":
+        B, Nq, Sq, D = q.shape
+        Nkv, Skv = k.shape[1], k.shape[2]
+        if k.shape[0] != B or k.shape[3] != D:
+            raise ValueError("k/v must be [B, Nkv, Skv, D] matching q")
+        lay, cu_q, cu_kv, ml_shape = LAYOUT_BNSD, None, None, (B, Nq, Sq)
+    elif layout == "TND":
+        Sq, Nq, D = q.shape
+        Skv, Nkv = k.shape[0], k.shape[1]
+        if k.shape[2] != D:
+            raise ValueError("k/v must be [Tk, Nkv, D] matching q")
+        cu_q, cu_kv = _cu(cu_seqlens_q), _cu(cu_seqlens_kv if cu_seqlens_kv is not None else cu_seqlens_q)
+        if cu_q is None:
+            raise ValueError("TND needs cu_seqlens_q")
+        if len(cu_q) != len(cu_kv):
+            raise ValueError("cu_seqlens_q and cu_seqlens_kv differ in length")
+        B = len(cu_q) - 1
+        lay, ml_shape = LAYOUT_TND, (Nq, Sq)
+    else:
+        raise ValueError("layout must be 'BNSD' or 'TND'")
+    kind = MASK_SS
+    if atten_mask is not None:
+        if atten_mask.dtype == torch.bool:
+            atten_mask = atten_mask.view(torch.uint8)
+        _require(atten_mask, "atten_mask", torch.uint8, dev)
+        if layout != "BNSD":
+            raise ValueError("atten_mask needs the BNSD layout")
+        kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)
+    out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, ml_shape)
+    for t, n, dt in ((out, "out", torch.bfloat16), (softmax_max, "softmax_max", torch.float32),
+                     (softmax_sum, "softmax_sum", torch.float32)):
+        _require(t, n, dt, dev)
+    if out.shape != q.shape or tuple(softmax_max.shape) != ml_shape or tuple(softmax_sum.shape) != ml_shape:
+        raise ValueError("output shapes do not match")
+    desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
+                     cu_q=cu_q, cu_kv=cu_kv, atten_mask=atten_mask, mask_kind=kind, head_range=head_range,
+                     qblock_range=qblock_range)
+    with torch.cuda.device(dev):
+        check(lib.attn_fwd(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max), _vp(softmax_sum),
+                           _stream(dev)))
+    return out, softmax_max, softmax_sum
+
+
+def build_kv_block_list(keep: torch.Tensor, counts: Optional[torch.Tensor] = None,
+                        idx: Optional[torch.Tensor] = None):
+    """Kept-block list of a block keep mask uint8 [B, N, QB, KB] (nonzero = keep).
+
+    Returns (counts int32 [B, N, QB], idx int32 [B, N, QB, KB])."""
+    lib = load()
+    if keep.dtype == torch.bool:
+        keep = keep.view(torch.uint8)
+    _require(keep, "keep", torch.uint8)
+    B, N, QB, KB = keep.shape
+    if counts is None:
+        counts = torch.empty((B, N, QB), dtype=torch.int32, device=keep.device)
+    if idx is None:
+        idx = torch.empty((B, N, QB, KB), dtype=torch.int32, device=keep.device)
+    _require(counts, "counts", torch.int32, keep.device)
+    _require(idx, "idx", torch.int32, keep.device)
+    with torch.cuda.device(keep.device):
+        check(lib.build_kv_block_list(_vp(keep), B, N, QB, KB, _vp(counts), _vp(idx), _stream(keep.device)))
+    return counts, idx
+
+
+def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range=None, qblock_range=None,
+                         out=None, softmax_max=None, softmax_sum=None):
+    """bf16 block-sparse attention over a kept-block list (BNSD); returns (out, m, l)."""
+    lib = load()
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, torch.bfloat16, dev)
+    _require(counts, "counts", torch.int32, dev)
+    _require(idx, "idx", torch.int32, dev)
+    B, Nq, Sq, D = q.shape
+    Nkv, Skv = k.shape[1], k.shape[2]
+    QB, KB = (Sq + BLOCK - 1) // BLOCK, (Skv + BLOCK - 1) // BLOCK
+    if tuple(counts.shape) != (B, Nq, QB) or tuple(idx.shape) != (B, Nq, QB, KB):
+        raise ValueError("counts/idx must be [B, Nq, QB] and [B, Nq, QB, KB]")
+    out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, (B, Nq, Sq))
+    desc = make_desc(layout=LAYOUT_BNSD, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
+                     head_range=head_range, qblock_range=qblock_range)
+    with torch.cuda.device(dev):
+        check(lib.attn_fwd_blocksparse(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max),
+                                       _vp(softmax_sum), _vp(counts), _vp(idx), _stream(dev)))
+    return out, softmax_max, softmax_sum
+
+
+def quantize_qk_perblock_int8(x: torch.Tensor, x_q: Optional[torch.Tensor] = None,
+                              scale: Optional[torch.Tensor] = None):
+    """INT8 per (batch, head, 128-token block); returns (codes int8, scale fp32 [B, N, ceil(S/128)])."""
+    lib = load()
+    _require(x, "x", torch.bfloat16)
+    B, N, S, D = x.shape
+    if x_q is None:
+        x_q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((B, N, (S + BLOCK - 1) // BLOCK), dtype=torch.float32, device=x.device)
+    _require(x_q, "x_q", torch.int8, x.device)
+    _require(scale, "scale", torch.float32, x.device)
+    with torch.cuda.device(x.device):
+        check(lib.quantize_qk_perblock_int8(_vp(x), B, N, S, D, _vp(x_q), _vp(scale), _stream(x.device)))
+    return x_q, scale
+
+
+def quantize_v_perchannel_fp8(v: torch.Tensor, v_q: Optional[torch.Tensor] = None,
+                              scale: Optional[torch.Tensor] = None):
+    """E4M3FN per (batch, head, channel); returns (codes uint8, scale fp32 [B, N, D])."""
+    lib = load()
+    _require(v, "v", torch.bfloat16)
+    B, N, S, D = v.shape
+    if v_q is None:
+        v_q = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    if scale is None:
+        scale = torch.empty((B, N, D), dtype=torch.float32, device=v.device)
+    _require(v_q, "v_q", torch.uint8, v.device)
+    _require(scale, "scale", torch.float32, v.device)
+    with torch.cuda.device(v.device):
+        check(lib.quantize_v_perchannel_fp8(_vp(v), B, N, S, D, _vp(v_q), _vp(scale), _stream(v.device)))
+    return v_q, scale
+
+
+def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scale: float,
+                  head_range=None, qblock_range=None, out=None, softmax_max=None, softmax_sum=None,
+                  return_softmax: bool = True):
+    """Quantised block-sparse attention (BNSD); returns (out, m, l) or (out, None, None)."""
+    lib = load()
+    dev = q_q.device
+    _require(q_q, "q_q", torch.int8, dev)
+    _require(k_q, "k_q", torch.int8, dev)
+    if v_q.dtype == torch.float8_e4m3fn:
+        v_q = v_q.view(torch.uint8)
+    _require(v_q, "v_q", torch.uint8, dev)
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _require(t, n, torch.float32, dev)
+    _require(counts, "counts", torch.int32, dev)
+    _require(idx, "idx", torch.int32, dev)
+    B, Nq, Sq, D = q_q.shape
+    Nkv, Skv = k_q.shape[1], k_q.shape[2]
+    QB, KB = (Sq + BLOCK - 1) // BLOCK, (Skv + BLOCK - 1) // BLOCK
+    if tuple(q_scale.shape) != (B, Nq, QB) or tuple(k_scale.shape) != (B, Nkv, KB) or \
+            tuple(v_scale.shape) != (B, Nkv, D):
+        raise ValueError("scale shapes must be q [B, Nq, QB], k [B, Nkv, KB], v [B, Nkv, D]")
+    if tuple(counts.shape) != (B, Nq, QB) or tuple(idx.shape) != (B, Nq, QB, KB):
+        raise ValueError("counts/idx must be [B, Nq, QB] and [B, Nq, QB, KB]")
+    if out is None:
+        out = torch.empty(q_q.shape, dtype=torch.bfloat16, device=dev)
+    if return_softmax:
+        if softmax_max is None:
+            softmax_max = torch.empty((B, Nq, Sq), dtype=torch.float32, device=dev)
+        if softmax_sum is None:
+            softmax_sum = torch.empty((B, Nq, Sq), dtype=torch.float32, device=dev)
+    desc = make_desc(layout=LAYOUT_BNSD, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
+                     head_range=head_range, qblock_range=qblock_range)
+    with torch.cuda.device(dev):
+        check(lib.attn_fwd_qbsa(ctypes.byref(desc), _vp(q_q), _vp(k_q), _vp(v_q), _vp(q_scale), _vp(k_scale),
+                                _vp(v_scale), _vp(counts), _vp(idx), _vp(out), _vp(softmax_max), _vp(softmax_sum),
+                                _stream(dev)))
+    return out, softmax_max, softmax_sum
+
+
+__all__ = ["attn_fwd", "attn_fwd_blocksparse", "attn_fwd_qbsa", "build_kv_block_list", "quantize_qk_perblock_int8",
+           "quantize_v_perchannel_fp8", "make_desc", "_lib"]

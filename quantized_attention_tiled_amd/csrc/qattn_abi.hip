@@ -1,0 +1,311 @@
+// C ABI of the qattn library: argument validation, subrange and grid set-up,
+// launches on the caller's stream. Nothing here allocates or keeps state
+// beyond a per-thread error message.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "qattn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared validation of the problem description; fills the geometry part of p.
+int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool allow_masks, int* total_qblocks) {
+  if (!d) return fail(QATTN_INVALID_ARGUMENT, "desc is NULL");
+  if (d->struct_size != sizeof(qattn_desc))
+    return fail(QATTN_INVALID_ARGUMENT, "desc->struct_size %u != %zu", d->struct_size, sizeof(qattn_desc));
+  if (d->layout != QATTN_LAYOUT_BNSD && d->layout != QATTN_LAYOUT_TND)
+    return fail(QATTN_INVALID_ARGUMENT, "layout %d is not BNSD (0) or TND (1)", d->layout);
+  if (d->layout == QATTN_LAYOUT_TND && !allow_tnd) return fail(QATTN_UNSUPPORTED, "this entry point needs BNSD");
+  if (d->B < 1 || d->Nq < 1 || d->Nkv < 1 || d->Sq < 0 || d->Skv < 0)
+    return fail(QATTN_INVALID_ARGUMENT, "bad sizes B=%d Nq=%d Nkv=%d Sq=%d Skv=%d", d->B, d->Nq, d->Nkv, d->Sq, d->Skv);
+  if (d->Nq % d->Nkv != 0) return fail(QATTN_INVALID_ARGUMENT, "Nq=%d is not a multiple of Nkv=%d", d->Nq, d->Nkv);
+  if (d->D != 64 && d->D != 128) return fail(QATTN_UNSUPPORTED, "head dimension D=%d (supported: 64, 128)", d->D);
+  if (!(std::isfinite(d->scale) && d->scale > 0.f)) return fail(QATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if (d->sparse_mode != 0 && d->sparse_mode != 2 && d->sparse_mode != 3)
+    return fail(QATTN_INVALID_ARGUMENT, "sparse_mode %d (supported: 0, 2, 3)", d->sparse_mode);
+  if (!allow_masks && (d->sparse_mode != 0 || d->atten_mask != nullptr))
+    return fail(QATTN_UNSUPPORTED, "block-sparse entry points take no causal mode and no atten_mask");
+  if (d->atten_mask != nullptr) {
+    if (d->layout != QATTN_LAYOUT_BNSD) return fail(QATTN_UNSUPPORTED, "atten_mask needs the BNSD layout");
+    if (d->mask_kind < QATTN_MASK_SS || d->mask_kind > QATTN_MASK_BNSS)
+      return fail(QATTN_INVALID_ARGUMENT, "mask_kind %d", d->mask_kind);
+  }
+  const int D = d->D;
+  p.B = d->B;
+  p.Nq = d->Nq;
+  p.Nkv = d->Nkv;
+  p.group = d->Nq / d->Nkv;
+  p.Sq = d->Sq;
+  p.Skv = d->Skv;
+  p.D = D;
+  p.scale = d->scale;
+  p.c = (float)((double)d->scale * 1.4426950408889634);
+  p.causal = d->sparse_mode;
+  int qblocks;
+  if (d->layout == QATTN_LAYOUT_BNSD) {
+    p.q_sb = (int64_t)d->Nq * d->Sq * D;
+    p.q_sh = (int64_t)d->Sq * D;
+    p.q_ss = D;
+    p.k_sb = (int64_t)d->Nkv * d->Skv * D;
+    p.k_sh = (int64_t)d->Skv * D;
+    p.k_ss = D;
+    p.ml_sb = (int64_t)d->Nq * d->Sq;
+    p.ml_sh = d->Sq;
+    p.ml_ss = 1;
+    p.QB = (d->Sq + qattn::kBlock - 1) / qattn::kBlock;
+    p.KB = (d->Skv + qattn::kBlock - 1) / qattn::kBlock;
+    p.nseq = 0;
+    qblocks = p.QB;
+    if (d->atten_mask) {
+      p.mask_ss = d->Skv;
+      const int64_t ss = (int64_t)d->Sq * d->Skv;
+      p.mask_sh = d->mask_kind == QATTN_MASK_BNSS ? ss : 0;
+      p.mask_sb = d->mask_kind == QATTN_MASK_SS ? 0 : (d->mask_kind == QATTN_MASK_B1SS ? ss : ss * d->Nq);
+    }
+  } else {
+    if (d->B > qattn::kMaxSeqs) return fail(QATTN_UNSUPPORTED, "TND with %d sequences (max %d)", d->B, qattn::kMaxSeqs);
+    if (!d->cu_seqlens_q || !d->cu_seqlens_kv) return fail(QATTN_INVALID_ARGUMENT, "TND needs cu_seqlens_q and cu_seqlens_kv");
+    if (d->cu_seqlens_q[0] != 0 || d->cu_seqlens_kv[0] != 0)
+      return fail(QATTN_INVALID_ARGUMENT, "cu_seqlens must start at 0");
+    qblocks = 0;
+    for (int i = 0; i < d->B; i++) {
+      const int lq = d->cu_seqlens_q[i + 1] - d->cu_seqlens_q[i];
+      const int lk = d->cu_seqlens_kv[i + 1] - d->cu_seqlens_kv[i];
+      if (lq < 0 || lk < 0) return fail(QATTN_INVALID_ARGUMENT, "cu_seqlens decrease at sequence %d", i);
+      qblocks += (lq + qattn::kBlock - 1) / qattn::kBlock;
+    }
+    if (d->cu_seqlens_q[d->B] != d->Sq || d->cu_seqlens_kv[d->B] != d->Skv)
+      return fail(QATTN_INVALID_ARGUMENT, "cu_seqlens end (%d, %d) != (Sq, Skv) = (%d, %d)", d->cu_seqlens_q[d->B],
+                  d->cu_seqlens_kv[d->B], d->Sq, d->Skv);
+    for (int i = 0; i <= d->B; i++) {
+      p.cu_q[i] = d->cu_seqlens_q[i];
+      p.cu_kv[i] = d->cu_seqlens_kv[i];
+    }
+    p.nseq = d->B;
+    p.q_sb = 0;
+    p.q_sh = D;
+    p.q_ss = (int64_t)d->Nq * D;
+    p.k_sb = 0;
+    p.k_sh = D;
+    p.k_ss = (int64_t)d->Nkv * D;
+    p.ml_sb = 0;
+    p.ml_sh = d->Sq;
+    p.ml_ss = 1;
+    p.QB = p.KB = 0;
+  }
+  // subrange
+  int h0 = d->head_begin, h1 = d->head_end, b0 = d->qblock_begin, b1 = d->qblock_end;
+  if (h0 == -1 && h1 == -1) {
+    h0 = 0;
+    h1 = d->Nq;
+  }
+  if (b0 == -1 && b1 == -1) {
+    b0 = 0;
+    b1 = qblocks;
+  }
+  if (h0 < 0 || h1 > d->Nq || h0 > h1) return fail(QATTN_INVALID_ARGUMENT, "head range [%d, %d) outside [0, %d)", h0, h1, d->Nq);
+  if (b0 < 0 || b1 > qblocks || b0 > b1)
+    return fail(QATTN_INVALID_ARGUMENT, "q-block range [%d, %d) outside [0, %d)", b0, b1, qblocks);
+  p.h0 = h0;
+  p.nh = h1 - h0;
+  p.qb0 = b0;
+  p.qb1 = b1;
+  *total_qblocks = qblocks;
+  return QATTN_OK;
+}
+
+int check_ptrs(const void* const* ptrs, const char* const* names, int n) {
+  for (int i = 0; i < n; i++) {
+    if (!ptrs[i]) return fail(QATTN_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(QATTN_MISALIGNED, "%s is not 16-byte aligned", names[i]);
+  }
+  return QATTN_OK;
+}
+
+int check_optional(const void* ptr, const char* name) {
+  if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 3u)) return fail(QATTN_MISALIGNED, "%s is not 4-byte aligned", name);
+  return QATTN_OK;
+}
+
+// Work items for the bf16 / quantised kernels: q-tiles of `per_tile` q-blocks.
+int finish_items(qattn::FwdParams& p, int per_tile) {
+  p.qblocks_per_tile = per_tile;
+  const int nqb = p.qb1 - p.qb0;
+  int64_t items;
+  if (p.nseq > 0) {
+    int qbpre = 0, tiles = 0;
+    for (int b = 0; b < p.nseq; b++) {
+      const int nqb_b = (p.cu_q[b + 1] - p.cu_q[b] + qattn::kBlock - 1) / qattn::kBlock;
+      const int lo = std::max(p.qb0, qbpre), hi = std::min(p.qb1, qbpre + nqb_b);
+      tiles += (std::max(0, hi - lo) + per_tile - 1) / per_tile;
+      qbpre += nqb_b;
+    }
+    p.total_tiles = tiles;
+    p.tiles_per_head = 0;
+    items = (int64_t)tiles * p.nh;
+  } else {
+    p.tiles_per_head = (nqb + per_tile - 1) / per_tile;
+    p.total_tiles = 0;
+    items = (int64_t)p.B * p.nh * p.tiles_per_head;
+  }
+  if (items > (int64_t)0x7fffff00) return fail(QATTN_UNSUPPORTED, "too many work items (%lld)", (long long)items);
+  p.total_items = (int)items;
+  return QATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QATTN_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+  return QATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qattn_last_error(void) { return g_err; }
+
+int qattn_version(void) { return 100; }
+
+int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v, qattn_bf16* o,
+             float* softmax_max, float* softmax_sum, void* stream) {
+  qattn::FwdParams p{};
+  int total_qb = 0;
+  int rc = setup_common(desc, p, true, true, &total_qb);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, o};
+  const char* names[] = {"q", "k", "v", "o"};
+  if ((rc = check_ptrs(ptrs, names, 4))) return rc;
+  if ((rc = check_optional(softmax_max, "softmax_max")) || (rc = check_optional(softmax_sum, "softmax_sum"))) return rc;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.m_out = softmax_max;
+  p.l_out = softmax_sum;
+  p.mask = desc->atten_mask;
+  int mode = 0;
+  if (desc->sparse_mode == 2 || desc->sparse_mode == 3) mode |= qattn::kCausal;
+  if (desc->atten_mask) mode |= qattn::kMask;
+  if (desc->layout == QATTN_LAYOUT_TND) mode |= qattn::kVarlen;
+  if ((rc = finish_items(p, 2))) return rc;
+  if (p.total_items == 0) return QATTN_OK;
+  return hip_status(qattn::launch_attn_bf16(p, mode, (hipStream_t)stream), "attn_fwd launch");
+}
+
+int build_kv_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32_t* counts, int32_t* idx,
+                        void* stream) {
+  if (B < 0 || N < 0 || QB < 0 || KB < 0) return fail(QATTN_INVALID_ARGUMENT, "negative size");
+  if ((int64_t)B * N * QB == 0) return QATTN_OK;
+  if (!keep || !counts || !idx) return fail(QATTN_INVALID_ARGUMENT, "keep, counts and idx must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(counts) & 3u) || (reinterpret_cast<uintptr_t>(idx) & 3u))
+    return fail(QATTN_MISALIGNED, "counts and idx must be 4-byte aligned");
+  return hip_status(qattn::launch_block_list(keep, B, N, QB, KB, counts, idx, (hipStream_t)stream),
+                    "build_kv_block_list launch");
+}
+
+int attn_fwd_blocksparse(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
+                         qattn_bf16* o, float* softmax_max, float* softmax_sum, const int32_t* counts,
+                         const int32_t* idx, void* stream) {
+  qattn::FwdParams p{};
+  int total_qb = 0;
+  int rc = setup_common(desc, p, false, false, &total_qb);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, o};
+  const char* names[] = {"q", "k", "v", "o"};
+  if ((rc = check_ptrs(ptrs, names, 4))) return rc;
+  if ((rc = check_optional(softmax_max, "softmax_max")) || (rc = check_optional(softmax_sum, "softmax_sum"))) return rc;
+  if (!counts || !idx) return fail(QATTN_INVALID_ARGUMENT, "counts and idx must be non-NULL");
+  if ((rc = check_optional(counts, "counts")) || (rc = check_optional(idx, "idx"))) return rc;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.m_out = softmax_max;
+  p.l_out = softmax_sum;
+  p.counts = counts;
+  p.idx = idx;
+  if ((rc = finish_items(p, 1))) return rc;
+  if (p.total_items == 0) return QATTN_OK;
+  return hip_status(qattn::launch_attn_bf16(p, qattn::kSparse, (hipStream_t)stream), "attn_fwd_blocksparse launch");
+}
+
+int quantize_qk_perblock_int8(const qattn_bf16* x, int B, int N, int S, int D, int8_t* x_q, float* scale,
+                              void* stream) {
+  if (B < 0 || N < 0 || S < 0) return fail(QATTN_INVALID_ARGUMENT, "negative size");
+  if (D != 64 && D != 128) return fail(QATTN_UNSUPPORTED, "head dimension D=%d (supported: 64, 128)", D);
+  if ((int64_t)B * N * S == 0) return QATTN_OK;
+  const void* ptrs[] = {x, x_q, scale};
+  const char* names[] = {"x", "x_q", "scale"};
+  int rc = check_ptrs(ptrs, names, 2);
+  if (rc) return rc;
+  if (!scale) return fail(QATTN_INVALID_ARGUMENT, "scale is NULL");
+  if ((rc = check_optional(scale, "scale"))) return rc;
+  return hip_status(qattn::launch_quant_qk(x, B, N, S, D, x_q, scale, (hipStream_t)stream),
+                    "quantize_qk_perblock_int8 launch");
+}
+
+int quantize_v_perchannel_fp8(const qattn_bf16* v, int B, int N, int S, int D, uint8_t* v_q, float* scale,
+                              void* stream) {
+  if (B < 0 || N < 0 || S < 0) return fail(QATTN_INVALID_ARGUMENT, "negative size");
+  if (D != 64 && D != 128) return fail(QATTN_UNSUPPORTED, "head dimension D=%d (supported: 64, 128)", D);
+  if ((int64_t)B * N == 0) return QATTN_OK;
+  if (!scale) return fail(QATTN_INVALID_ARGUMENT, "scale is NULL");
+  int rc = check_optional(scale, "scale");
+  if (rc) return rc;
+  if (S > 0) {
+    const void* ptrs[] = {v, v_q};
+    const char* names[] = {"v", "v_q"};
+    if ((rc = check_ptrs(ptrs, names, 2))) return rc;
+  }
+  return hip_status(qattn::launch_quant_v(v, B, N, S, D, v_q, scale, (hipStream_t)stream),
+                    "quantize_v_perchannel_fp8 launch");
+}
+
+int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, const uint8_t* v, const float* q_scale,
+                  const float* k_scale, const float* v_scale, const int32_t* counts, const int32_t* idx, qattn_bf16* o,
+                  float* softmax_max, float* softmax_sum, void* stream) {
+  qattn::FwdParams p{};
+  int total_qb = 0;
+  int rc = setup_common(desc, p, false, false, &total_qb);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, o};
+  const char* names[] = {"q", "k", "v", "o"};
+  if ((rc = check_ptrs(ptrs, names, 4))) return rc;
+  if (!q_scale || !k_scale || !v_scale || !counts || !idx)
+    return fail(QATTN_INVALID_ARGUMENT, "q_scale, k_scale, v_scale, counts and idx must be non-NULL");
+  const void* opt[] = {q_scale, k_scale, v_scale, counts, idx, softmax_max, softmax_sum};
+  const char* onames[] = {"q_scale", "k_scale", "v_scale", "counts", "idx", "softmax_max", "softmax_sum"};
+  for (int i = 0; i < 7; i++)
+    if ((rc = check_optional(opt[i], onames[i]))) return rc;
+  p.qi = q;
+  p.ki = k;
+  p.vf = v;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.counts = counts;
+  p.idx = idx;
+  p.o = o;
+  p.m_out = softmax_max;
+  p.l_out = softmax_sum;
+  if ((rc = finish_items(p, 1))) return rc;
+  if (p.total_items == 0) return QATTN_OK;
+  return hip_status(qattn::launch_attn_qbsa(p, (hipStream_t)stream), "attn_fwd_qbsa launch");
+}
+
+}  // extern "C"

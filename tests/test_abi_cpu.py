@@ -1,0 +1,169 @@
+"""C-ABI host checks that need no GPU.
+
+* the built library exports every function include/qattn.h declares;
+* the ctypes mirror of qattn_desc has the C layout (checked against gcc);
+* argument validation returns the documented status codes before any
+  launch (fake, never-dereferenced device pointers are enough for that).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qattn.h")
+LIB = os.path.join(ROOT, "quantized_attention_tiled_amd", "libqattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libqattn.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    from quantized_attention_tiled_amd import _lib
+    return _lib
+
+
+def test_exports_every_declared_symbol(q):
+    lib = q.load()
+    declared = _declared_functions()
+    assert set(declared) == set(q.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    for name in declared:
+        assert re.search(rf"\bT {name}$", nm, flags=re.M), name
+    assert lib.qattn_version() == 100
+
+
+def test_desc_layout_matches_c(q, tmp_path):
+    fields = [f for f, _ in q.QattnDesc._fields_]
+    src = tmp_path / "probe.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "qattn.h"', "int main(void) {",
+             '  printf("%zu\\n", sizeof(qattn_desc));']
+    lines += [f'  printf("%zu\\n", offsetof(qattn_desc, {f}));' for f in fields]
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(q.QattnDesc)
+    for f, off in zip(fields, out[1:]):
+        assert getattr(q.QattnDesc, f).offset == off, f
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _desc(q, **kw):
+    d = q.QattnDesc()
+    d.struct_size = ctypes.sizeof(q.QattnDesc)
+    base = dict(layout=0, B=1, Nq=4, Nkv=2, Sq=256, Skv=256, D=128, scale=0.1, sparse_mode=0, mask_kind=0,
+                head_begin=-1, head_end=-1, qblock_begin=-1, qblock_end=-1)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+def _fwd(q, d, qp=FAKE, kp=FAKE, vp=FAKE, op=FAKE, m=0, l=0):
+    lib = q.load()
+    return lib.attn_fwd(ctypes.byref(d) if d is not None else None, qp, kp, vp, op, m or None, l or None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), 2), (dict(D=0), 2), (dict(Nq=3, Nkv=2), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(sparse_mode=1), 1), (dict(layout=2), 1),
+    (dict(B=0), 1), (dict(Sq=-1), 1), (dict(Nkv=0), 1), (dict(head_begin=0, head_end=5), 1),
+    (dict(head_begin=3, head_end=2), 1), (dict(qblock_begin=0, qblock_end=3), 1), (dict(qblock_begin=-2, qblock_end=1), 1),
+])
+def test_invalid_descriptions(q, kw, status):
+    assert _fwd(q, _desc(q, **kw)) == status
+    assert q.load().qattn_last_error()
+
+
+def test_struct_size_and_null_desc(q):
+    d = _desc(q)
+    d.struct_size = 12
+    assert _fwd(q, d) == 1
+    assert _fwd(q, None) == 1
+
+
+def test_pointer_checks(q):
+    assert _fwd(q, _desc(q), qp=0) == 1
+    assert _fwd(q, _desc(q), vp=FAKE + 8) == 3
+    assert _fwd(q, _desc(q), m=FAKE + 2) == 3
+    assert b"not 16-byte aligned" in q.load().qattn_last_error() or b"4-byte" in q.load().qattn_last_error()
+
+
+def test_tnd_validation(q):
+    lib = q.load()
+
+    def tnd(cu_q, cu_kv, **kw):
+        aq = (ctypes.c_int32 * len(cu_q))(*cu_q)
+        ak = (ctypes.c_int32 * len(cu_kv))(*cu_kv)
+        d = _desc(q, layout=1, B=len(cu_q) - 1, Sq=cu_q[-1], Skv=cu_kv[-1], **kw)
+        d.cu_seqlens_q = ctypes.cast(aq, ctypes.POINTER(ctypes.c_int32))
+        d.cu_seqlens_kv = ctypes.cast(ak, ctypes.POINTER(ctypes.c_int32))
+        return lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None)
+
+    assert tnd([1, 5], [0, 5]) == 1                      # does not start at 0
+    assert tnd([0, 5, 3], [0, 5, 6]) == 1                # decreasing
+    d = _desc(q, layout=1, B=2, Sq=10, Skv=10)           # missing arrays
+    assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 1
+    big = list(range(0, 258))
+    assert tnd(big, big) == 2                            # 257 sequences > 256
+    aq = (ctypes.c_int32 * 3)(0, 4, 9)
+    d = _desc(q, layout=1, B=2, Sq=10, Skv=9)            # last entry != Sq
+    d.cu_seqlens_q = ctypes.cast(aq, ctypes.POINTER(ctypes.c_int32))
+    d.cu_seqlens_kv = ctypes.cast(aq, ctypes.POINTER(ctypes.c_int32))
+    assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 1
+    # a boolean mask needs BNSD
+    d2 = _desc(q, layout=1, B=1, Sq=5, Skv=5)
+    a5 = (ctypes.c_int32 * 2)(0, 5)
+    d2.cu_seqlens_q = ctypes.cast(a5, ctypes.POINTER(ctypes.c_int32))
+    d2.cu_seqlens_kv = ctypes.cast(a5, ctypes.POINTER(ctypes.c_int32))
+    d2.atten_mask = FAKE
+    assert lib.attn_fwd(ctypes.byref(d2), FAKE, FAKE, FAKE, FAKE, None, None, None) == 2
+
+
+def test_blocksparse_and_qbsa_validation(q):
+    lib = q.load()
+    d = _desc(q, sparse_mode=2)
+    assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 2
+    d = _desc(q)
+    d.atten_mask = FAKE
+    assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 2
+    d = _desc(q)
+    assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None) == 1
+    assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, layout=1)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             None, None, None) == 2
+    assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             None, None, None) == 1
+    assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, FAKE + 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             None, None, None) == 3
+
+
+def test_quantizer_and_list_validation(q):
+    lib = q.load()
+    assert lib.quantize_qk_perblock_int8(FAKE, 1, 1, 128, 96, FAKE, FAKE, None) == 2
+    assert lib.quantize_qk_perblock_int8(FAKE, 1, -1, 128, 128, FAKE, FAKE, None) == 1
+    assert lib.quantize_qk_perblock_int8(FAKE + 4, 1, 1, 128, 128, FAKE, FAKE, None) == 3
+    assert lib.quantize_qk_perblock_int8(FAKE, 1, 1, 128, 128, FAKE, None, None) == 1
+    assert lib.quantize_v_perchannel_fp8(FAKE, 1, 1, 128, 32, FAKE, FAKE, None) == 2
+    assert lib.quantize_v_perchannel_fp8(FAKE, 1, 1, 128, 128, FAKE, None, None) == 1
+    assert lib.build_kv_block_list(None, 1, 1, 4, 4, FAKE, FAKE, None) == 1
+    assert lib.build_kv_block_list(FAKE, 1, 1, 4, 4, FAKE + 2, FAKE, None) == 3
+    # empty problems are a successful no-op that launches nothing
+    assert lib.quantize_qk_perblock_int8(FAKE, 0, 1, 128, 128, FAKE, FAKE, None) == 0
+    assert lib.build_kv_block_list(FAKE, 1, 0, 4, 4, FAKE, FAKE, None) == 0
+    assert _fwd(q, _desc(q, Sq=0)) == 0
+    assert _fwd(q, _desc(q, head_begin=1, head_end=1)) == 0

@@ -1,0 +1,173 @@
+"""GPU parity of the bf16 attention forward (dense, causal, masks, TND, GQA,
+block-sparse) against the float64 oracle, element by element.
+
+Tolerances: O max-abs <= 1e-2; softmax max/sum relative <= 1e-3 (with
+|m| floored at 1); rows with no kept key must be exactly O = 0, m = -inf, l = 0.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import O_TOL_BF16, banner, check_ml, check_o, dev_bf16, f64, to_np
+from workloads import make_block_keep, make_workload, random_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qa():
+    import quantized_attention_tiled_amd as qa
+    qa.load()
+    return qa
+
+
+def _bnsd(seed, B, Nq, Nkv, Sq, Skv, D, recipe="normal"):
+    q = random_bf16(seed, (B, Nq, Sq, D), recipe)
+    k = random_bf16(seed + 1, (B, Nkv, Skv, D), recipe)
+    v = random_bf16(seed + 2, (B, Nkv, Skv, D), recipe)
+    return q, k, v
+
+
+def test_c1_dense_small(qa):
+    w = make_workload("c1_dense_small")
+    banner(f"c1 {w.q.shape}")
+    o, m, l = qa.attn_fwd(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), scale=w.scale)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(w.q), f64(w.k), f64(w.v), w.scale)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,Sq,Skv,D,mode", [
+    (1, 2, 2, 256, 256, 64, 0),
+    (2, 4, 2, 300, 300, 128, 0),      # ragged q and kv tails, GQA 2
+    (1, 4, 1, 200, 333, 64, 0),       # Sq != Skv, GQA 4
+    (1, 8, 1, 130, 130, 128, 0),      # GQA 8
+    (1, 2, 2, 384, 384, 128, 2),
+    (2, 4, 2, 300, 300, 64, 2),
+    (1, 2, 1, 200, 450, 128, 3),      # bottom-right with Skv > Sq
+    (1, 2, 2, 450, 200, 128, 3),      # bottom-right with Sq > Skv: leading rows see no key
+    (1, 2, 2, 450, 200, 64, 2),
+    (1, 1, 1, 1, 1, 128, 0),
+    (1, 1, 1, 5, 700, 64, 3),
+])
+def test_dense_and_causal(qa, B, Nq, Nkv, Sq, Skv, D, mode):
+    banner(f"dense B={B} Nq={Nq} Nkv={Nkv} Sq={Sq} Skv={Skv} D={D} mode={mode}")
+    q, k, v = _bnsd(100 + Sq + D + mode, B, Nq, Nkv, Sq, Skv, D)
+    scale = 1.0 / np.sqrt(D)
+    o, m, l = qa.attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=scale, sparse_mode=mode)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), scale, sparse_mode=mode)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+
+
+@pytest.mark.parametrize("kind,mode", [("SS", 0), ("B1SS", 0), ("BNSS", 0), ("SS", 2), ("BNSS", 3)])
+def test_boolean_masks(qa, kind, mode):
+    B, Nq, Nkv, Sq, Skv, D = 2, 4, 2, 200, 260, 128
+    banner(f"mask {kind} mode={mode}")
+    q, k, v = _bnsd(7 + mode, B, Nq, Nkv, Sq, Skv, D)
+    rng = np.random.default_rng(5)
+    shape = {"SS": (Sq, Skv), "B1SS": (B, 1, Sq, Skv), "BNSS": (B, Nq, Sq, Skv)}[kind]
+    mask = (rng.random(shape) < 0.3).astype(np.uint8)
+    mask[..., 17, :] = 1                                   # a fully masked row
+    scale = 0.09
+    o, m, l = qa.attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=scale, sparse_mode=mode,
+                          atten_mask=torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), scale, sparse_mode=mode, atten_mask=mask)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+    assert np.all(to_np(o)[:, :, 17] == 0)
+
+
+@pytest.mark.parametrize("lens_q,lens_kv,mode,Nq,Nkv,D", [
+    ([1, 5, 130, 257], None, 3, 4, 2, 128),
+    ([300, 0, 64, 129], None, 2, 2, 2, 64),
+    ([100, 260], [300, 120], 3, 4, 1, 128),                 # kv longer / shorter than q per sequence
+    ([128, 256, 384], None, 0, 2, 2, 128),
+    ([3, 0, 7], [5, 9, 0], 3, 2, 2, 64),                     # empty q and empty kv sequences
+])
+def test_tnd_varlen(qa, lens_q, lens_kv, mode, Nq, Nkv, D):
+    lens_kv = lens_q if lens_kv is None else lens_kv
+    banner(f"tnd lens_q={lens_q} lens_kv={lens_kv} mode={mode}")
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lens_kv)]).astype(np.int32)
+    q = random_bf16(31, (int(cq[-1]), Nq, D))
+    k = random_bf16(32, (int(ck[-1]), Nkv, D))
+    v = random_bf16(33, (int(ck[-1]), Nkv, D))
+    scale = 1.0 / np.sqrt(D)
+    o, m, l = qa.attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=scale, layout="TND", sparse_mode=mode,
+                          cu_seqlens_q=cq.tolist(), cu_seqlens_kv=ck.tolist())
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), scale, layout="TND", sparse_mode=mode,
+                                  cu_seqlens_q=cq, cu_seqlens_kv=ck)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+
+
+def test_varlen_config_scaled(qa):
+    """The causal GQA varlen recipe at reduced lengths (full size is in the full-size tests)."""
+    w = make_workload("c3_varlen_gqa_causal", lengths=[512, 700, 1029, 640])
+    banner(f"c3-shaped T={w.Sq}")
+    o, m, l = qa.attn_fwd(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), scale=w.scale, layout="TND",
+                          sparse_mode=w.sparse_mode, cu_seqlens_q=w.cu_seqlens_q.tolist(),
+                          cu_seqlens_kv=w.cu_seqlens_kv.tolist())
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(w.q), f64(w.k), f64(w.v), w.scale, layout="TND", sparse_mode=w.sparse_mode,
+                                  cu_seqlens_q=w.cu_seqlens_q, cu_seqlens_kv=w.cu_seqlens_kv)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+
+
+def test_block_list_bitexact(qa):
+    keep = make_block_keep(77, 2, 3, 37, 70, 0.3)
+    keep[0, 1, 5, :] = 0                                      # an empty row
+    keep[1, 2, 6, :] = 1                                      # a full row
+    counts, idx = qa.build_kv_block_list(torch.from_numpy(keep).cuda())
+    torch.cuda.synchronize()
+    rc, ri = oracle.kept_block_list(keep)
+    assert np.array_equal(to_np(counts), rc) and np.array_equal(to_np(idx), ri)
+
+
+@pytest.mark.parametrize("S,Nq,Nkv,D,p", [(640, 2, 2, 128, 0.3), (333, 4, 2, 64, 0.5), (1024, 2, 1, 128, 0.1)])
+def test_blocksparse(qa, S, Nq, Nkv, D, p):
+    banner(f"blocksparse S={S} Nq={Nq} Nkv={Nkv} D={D} p={p}")
+    q, k, v = _bnsd(900 + S, 1, Nq, Nkv, S, S, D, recipe="block_offset")
+    nb = (S + 127) // 128
+    keep = make_block_keep(901, 1, Nq, nb, nb, p)
+    keep[0, 0, 1, :] = 0                                      # q-block with no kept block
+    scale = 1.0 / np.sqrt(D)
+    counts, idx = qa.build_kv_block_list(torch.from_numpy(keep).cuda())
+    o, m, l = qa.attn_fwd_blocksparse(dev_bf16(q), dev_bf16(k), dev_bf16(v), counts, idx, scale=scale)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), scale, block_keep=keep)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+
+
+def test_blocksparse_all_kept_equals_dense(qa):
+    S, D = 512, 128
+    q, k, v = _bnsd(55, 1, 2, 2, S, S, D)
+    keep = np.ones((1, 2, 4, 4), np.uint8)
+    counts, idx = qa.build_kv_block_list(torch.from_numpy(keep).cuda())
+    a = qa.attn_fwd_blocksparse(dev_bf16(q), dev_bf16(k), dev_bf16(v), counts, idx, scale=0.1)
+    b = qa.attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=0.1)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), 0.1)
+    for out in (a, b):
+        check_o(to_np(out[0]), ro, O_TOL_BF16)
+        check_ml(to_np(out[1]), to_np(out[2]), rm, rl)
+
+
+def test_deterministic(qa):
+    q, k, v = _bnsd(66, 1, 4, 4, 1000, 1000, 128)
+    dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    a = qa.attn_fwd(dq, dk, dv, scale=0.1, sparse_mode=2)
+    b = qa.attn_fwd(dq, dk, dv, scale=0.1, sparse_mode=2)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y.view(torch.int32))

@@ -18,5 +18,6 @@ from .synth import (  # noqa: F401
     f32_to_bf16_bits,
     make_block_keep,
     make_workload,
+    random_bf16,
     varlen_lengths,
 )

@@ -70,6 +70,22 @@ def _draw_head(base: int, tid: int, b: int, n: int, S: int, D: int, recipe: str)
     return x
 
 
+def random_bf16(seed: int, shape, recipe: str = "normal") -> np.ndarray:
+    """bf16 bits of an arbitrary-shape tensor: N(0, 1) values (``normal``) or
+    N(0, 1) plus a per-(leading index, 128-row block) offset N(0, 0.5^2) along
+    the second-to-last axis (``block_offset``)."""
+    shape = tuple(int(s) for s in shape)
+    x = _rng(seed, 0).standard_normal(shape, dtype=np.float32)
+    if recipe == "block_offset":
+        S = shape[-2]
+        nblk = (S + BLOCK - 1) // BLOCK
+        off = _rng(seed, _T_OFF).standard_normal(shape[:-2] + (nblk, shape[-1]), dtype=np.float32) * np.float32(0.5)
+        x += np.repeat(off, BLOCK, axis=-2)[..., :S, :]
+    elif recipe != "normal":
+        raise ValueError(f"unknown recipe {recipe}")
+    return f32_to_bf16_bits(x)
+
+
 def make_block_keep(base: int, B: int, N: int, QB: int, KB: int, p_keep: float,
                     heads: Optional[list] = None) -> np.ndarray:
     """Block keep mask uint8 [B, N, QB, KB] (1 = keep); diagonal always kept."""
