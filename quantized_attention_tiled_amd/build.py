@@ -24,6 +24,9 @@ ARCH = "gfx950"
 # Packed fp32 instructions are switched off for all device code; the host
 # pass warns that it does not know the feature, which is harmless.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The bf16 attention kernel keeps its score accumulators in VGPRs (compiler MFMAs) and its output
+# accumulators in AGPRs (inline-asm MFMAs); see the comment on mfma_acc in attn_bf16.hip.
+SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def hipcc() -> str:
@@ -36,7 +39,7 @@ def hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c", f"-I{INCLUDE}", f"-I{CSRC}",
-           *DEVICE_FLAGS, os.path.join(CSRC, src), "-o", obj]
+           *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
