@@ -68,21 +68,41 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, co
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// O^T accumulation with the accumulator pinned to AGPRs. This file is built with the VGPR form
-// for compiler-generated MFMAs (the score accumulators, which the softmax reads on the VALU);
-// the O accumulators are only ever touched by these instructions, by their zero initialisation
-// and by the epilogue, so they live in the accumulation registers for the whole kernel.
-// The compiler's hazard recognizer does not look inside inline asm, so every transition between
-// these MFMAs and VALU work on their operands is padded by hand. Volatile asm statements keep
-// their relative order; the empty "pin" statements below tie register writes (before) and reads
-// (after) to that order, so the compiler cannot move them next to the MFMAs.
-__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// every write of x happens before this point, every later read after it
-__device__ __forceinline__ void pin_acc(f32x16& x) { asm volatile("" : "+a"(x)); }
-// every write of x happens before this point
-__device__ __forceinline__ void pin_operand(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+// O^T accumulation. kAgpr = true (64 query rows per wave, one wave per SIMD): the accumulator is
+// pinned to AGPRs. This file is built with the VGPR form for compiler-generated MFMAs (the score
+// accumulators, which the softmax reads on the VALU); the O accumulators are only ever touched by
+// these instructions, their zero initialisation and the epilogue, so they live in the
+// accumulation registers for the whole kernel. The compiler's hazard recognizer does not look
+// inside inline asm, so every transition between these MFMAs and VALU work on their operands is
+// padded by hand: volatile asm statements keep their relative order, and the empty "pin"
+// statements tie register writes (before) and reads (after) to that order, so the compiler
+// cannot move them next to the MFMAs.
+// kAgpr = false (32 rows per wave, two waves per SIMD): everything fits in the 256 VGPRs a wave
+// has at that occupancy, so the builtin is used and the compiler handles the hazards; no AGPR is
+// touched, which leaves the whole register budget to the VGPRs.
+template <bool kAgpr>
+struct AccO {
+  __device__ static __forceinline__ void mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    if constexpr (kAgpr) {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    } else {
+      acc = mfma_bf16(a, b, acc);
+    }
+  }
+  // every write of x happens before this point, every later read after it
+  __device__ static __forceinline__ void pin(f32x16& x) {
+    if constexpr (kAgpr) asm volatile("" : "+a"(x));
+  }
+  // every write of x happens before this point
+  __device__ static __forceinline__ void pin_operand(const bf16x8& x) {
+    if constexpr (kAgpr) asm volatile("" ::"v"(x));
+  }
+  // n + 1 wait states (n <= 7), only where the asm MFMAs need them
+  template <int n>
+  __device__ static __forceinline__ void nops() {
+    if constexpr (kAgpr) asm volatile("s_nop %0" ::"n"(n) : "memory");
+  }
+};
 
 // max / sum of x over lanes l and l ^ 32 (v_permlane32_swap returns both halves)
 __device__ __forceinline__ float pair_max(float x) {
@@ -108,15 +128,20 @@ struct Tile {
   __device__ static int vswz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
 };
 
+// NQ = 1: Q^T lives in registers and the LDS holds only the K and V rings (80 KiB at D = 128), so
+// two workgroups share a CU and each SIMD runs two waves whose MFMA and VALU phases interleave.
+// NQ = 2: 64 query rows per wave, Q^T staged in LDS, one workgroup per CU.
 template <int D, int NQ, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kThreads, NQ == 1 ? 2 : 1) void attn_bf16_kernel(const FwdParams p) {
   using T = Tile<D>;
   constexpr int DT = D / 16;   // k-steps of the score product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
+  constexpr bool kQInRegs = NQ == 1;
+  using Acc = AccO<!kQInRegs>;
   static_assert(T::kLoadsPerWave >= 1, "tile load split");
 
-  // Q tile of the workgroup (128 * NQ rows), then the K ring, then the V ring
-  constexpr int kQBytes = 128 * NQ * T::kRowBytes;
+  // Q tile of the workgroup (128 * NQ rows, NQ = 2 only), then the K ring, then the V ring
+  constexpr int kQBytes = kQInRegs ? 0 : 128 * NQ * T::kRowBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kQBytes + (kNBufK + kNBufV) * T::kBytes];
   uint8_t* const qbuf = smem;
   uint8_t* const kbuf = smem + kQBytes;
@@ -217,16 +242,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const FwdParams 
   auto issue_k = [&](int i) { issue_tile(kp, kbuf + (i % kNBufK) * T::kBytes, tile_key0(i), false); };
   auto issue_v = [&](int i) { issue_tile(vp, vbuf + (i % kNBufV) * T::kBytes, tile_key0(i), true); };
 
-  // ---- this wave's 32 * NQ query rows -> LDS (same swizzle as K); read back as the Q^T B operand ----
-  constexpr int kQLoads = 32 * NQ / T::kRowsPerLoad;
+  // ---- this wave's query rows as the Q^T B operand: lane (hl, l32) holds row l32, 16-byte chunk
+  // 2 t + hl for k-step t. NQ = 1: straight into registers; NQ = 2: through LDS (K's swizzle) ----
+  bf16x8 qreg[kQInRegs ? DT : 1];
   uint8_t* const qw = qbuf + wave * 32 * NQ * T::kRowBytes;
+  if constexpr (kQInRegs) {
+    const int r = max(min(wrow0 + l32, row_end - 1), 0);
+    const bf16x8* src = (const bf16x8*)(qp + (int64_t)r * p.q_ss);
 #pragma unroll
-  for (int n = 0; n < kQLoads; n++) {
-    const int row = n * T::kRowsPerLoad + lane / T::kChunks;
-    const int c = (lane % T::kChunks) ^ T::kswz(row);
-    const int r = max(min(wrow0 + row, row_end - 1), 0);
-    const uint16_t* src = qp + (int64_t)r * p.q_ss + c * 8;
-    __builtin_amdgcn_global_load_lds((gbl_cvoid*)src, (lds_void*)(qw + n * 1024), 16, 0, 0);
+    for (int t = 0; t < DT; t++) qreg[t] = src[2 * t + hl];
+  } else {
+    constexpr int kQLoads = 32 * NQ / T::kRowsPerLoad;
+#pragma unroll
+    for (int n = 0; n < kQLoads; n++) {
+      const int row = n * T::kRowsPerLoad + lane / T::kChunks;
+      const int c = (lane % T::kChunks) ^ T::kswz(row);
+      const int r = max(min(wrow0 + row, row_end - 1), 0);
+      const uint16_t* src = qp + (int64_t)r * p.q_ss + c * 8;
+      __builtin_amdgcn_global_load_lds((gbl_cvoid*)src, (lds_void*)(qw + n * 1024), 16, 0, 0);
+    }
   }
 
   // Softmax state per query column block j. The reference max mref of a row is fixed at the
@@ -254,10 +288,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const FwdParams 
   };
   // B operand (Q^T) for k-step t: this wave's query rows 32 j + l32, chunk 2t + hl
   auto read_q = [&](int t, bf16x8 (&qf)[NQ]) {
+    if constexpr (kQInRegs) {
+      qf[0] = qreg[t];
+    } else {
 #pragma unroll
-    for (int j = 0; j < NQ; j++) {
-      const int row = 32 * j + l32;
-      qf[j] = *(const bf16x8*)(qw + row * T::kRowBytes + (((2 * t + hl) ^ T::kswz(row)) << 4));
+      for (int j = 0; j < NQ; j++) {
+        const int row = 32 * j + l32;
+        qf[j] = *(const bf16x8*)(qw + row * T::kRowBytes + (((2 * t + hl) ^ T::kswz(row)) << 4));
+      }
     }
   };
   // A operand (V^T) of O^T += V^T P^T for 16-key chunk kc and 32-row block db:
@@ -332,7 +370,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const FwdParams 
     }
   };
 
-  __shared__ int wave_flags[kWaves];
+  // per-wave overflow flags, exchanged through the first K slot once the tile loop has drained
+  // (no load in flight, every read done: each tile ends with a full wait and a barrier)
+  int* const wave_flags = (int*)kbuf;
   for (int pass = 0; pass < 2; pass++) {
     // pass 0 for everyone; pass 1 only recomputes waves that flagged an outgrown reference
     const bool compute = pass == 0 || overflow;
@@ -349,8 +389,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const FwdParams 
 #pragma unroll
     for (int db = 0; db < DB; db++)
 #pragma unroll
-      for (int j = 0; j < NQ; j++) pin_acc(o[db][j]);
-    asm volatile("s_nop 4" ::: "memory");
+      for (int j = 0; j < NQ; j++) Acc::pin(o[db][j]);
+    Acc::template nops<4>();
     bool over = false;
 
     if (ntiles > 0) {
@@ -456,19 +496,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const FwdParams 
           // VALU writes of P -> MFMA operand reads
 #pragma unroll
           for (int j = 0; j < NQ; j++) {
-            pin_operand(pb[0][j]);
-            pin_operand(pb[1][j]);
+            Acc::pin_operand(pb[0][j]);
+            Acc::pin_operand(pb[1][j]);
           }
-          asm volatile("s_nop 4" ::: "memory");
+          Acc::template nops<4>();
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int db = 0; db < DB; db++)
 #pragma unroll
-            for (int j = 0; j < NQ; j++) mfma_acc(o[db][j], va0[db], pb[0][j]);
+            for (int j = 0; j < NQ; j++) Acc::mfma(o[db][j], va0[db], pb[0][j]);
 #pragma unroll
           for (int db = 0; db < DB; db++)
 #pragma unroll
-            for (int j = 0; j < NQ; j++) mfma_acc(o[db][j], va1[db], pb[1][j]);
+            for (int j = 0; j < NQ; j++) Acc::mfma(o[db][j], va1[db], pb[1][j]);
           __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -498,11 +538,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const FwdParams 
 
   // ---- epilogue: O = acc / l, softmax max and sum ----
   // last accumulating MFMA -> VALU reads of the accumulators
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  Acc::template nops<7>();
+  Acc::template nops<7>();
+  Acc::template nops<7>();
 #pragma unroll
   for (int db = 0; db < DB; db++)
 #pragma unroll
-    for (int j = 0; j < NQ; j++) pin_acc(o[db][j]);
+    for (int j = 0; j < NQ; j++) Acc::pin(o[db][j]);
 #pragma unroll
   for (int j = 0; j < NQ; j++) {
     const float lt = pair_sum(lsum[j]);
