@@ -50,6 +50,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKT = 64;  // keys per LDS tile
+constexpr int kPF = 2;   // MFMA operands are read from LDS this many slots ahead
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
@@ -61,6 +62,16 @@ template <int V>
 struct IC {
   static constexpr int value = V;
 };
+
+// Empty volatile asm statements keep their relative order. pin_def(x) makes x's value opaque at this
+// point, so nothing computed from x can be moved above it; pin_use(x) needs x, so nothing that
+// feeds x can be moved below it. Together they keep each pipeline step's VALU work inside the
+// step, between its MFMAs, where the compiler's code motion would otherwise hoist or sink it.
+__device__ __forceinline__ void pin_def(float& x) { asm volatile("" : "+v"(x)); }
+template <typename T>
+__device__ __forceinline__ void pin_use(const T& x) {
+  asm volatile("" ::"v"(x));
+}
 
 __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -292,82 +303,160 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   bool overflow = false;
   bool over = false;
   bool compute = true;
+  bool ref_all = false;  // every row of this wave has its reference max (wave-uniform)
 
-  // One pipeline step: the softmax of the current half (scores in sc, P into pc), interleaved one
-  // MFMA at a time with the scores of the next half (K slot KS, half KH, into sn) and with
-  // P(prev) V (pp, V slot VS, 16-key chunks 2 VH and 2 VH + 1). NEXT / CUR / PREV switch the
-  // three parts on; run says whether the current half reaches this wave at all (a half that does
-  // not run keeps its finite scores but is given row max -inf and exponent offset +inf, so every
-  // p is 0 and m, l and O stay unchanged). Operands are fetched two MFMAs ahead; hard scheduling
-  // barriers keep each MFMA with its slice of the softmax.
-  auto step = [&](auto KS, auto KH, auto VS, auto VH, auto NEXT, auto CUR, auto PREV, f32x16& sn, f32x16& sc,
-                  const bf16x8 (&pp)[2], bf16x8 (&pc)[2], bool run) {
+  // row max of a 32-key half over this lane's 16 scores and its partner lane l ^ 32 (max3 tree)
+  auto half_max = [&](const f32x16& s) -> float {
+    const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]), m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]), m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    const float m5 = fmaxf(fmaxf(m0, m1), m2), m6 = fmaxf(fmaxf(m3, m4), s[15]);
+    return pair_max(fmaxf(m5, m6));
+  };
+
+  // One pipeline step over MFMA slots 0 .. M - 1: slots 0 .. DT - 1 compute the scores of the next
+  // half (K slot KS, half KH, into sn); slots DT .. M - 1 compute P(prev) V (pp, V slot VS, 16-key
+  // chunks 2 VH and 2 VH + 1). Between the MFMAs the VALU runs the softmax of the current half (sc,
+  // exponent offset mu, P into pc) and its row max, which only feeds the true max and the overflow
+  // check (run: the half reaches this wave). NEXT / CUR / PREV switch the three parts on. Operands
+  // are read from LDS kPF slots ahead; PIN says the first two arrive in carry, POUT that the last
+  // slots read the first two of the following step (K slot KS2, half KH2) into carry. Hard
+  // scheduling barriers keep each MFMA with its slice of VALU work.
+  auto step = [&](auto KS, auto KH, auto VS, auto VH, auto NEXT, auto CUR, auto PREV, auto PIN, auto POUT,
+                  auto KS2, auto KH2, f32x16& sn, const f32x16& sc, const bf16x8 (&pp)[2], bf16x8 (&pc)[2],
+                  bf16x8 (&carry)[2], float mu, bool run) {
     constexpr int ks_ = decltype(KS)::value, kh_ = decltype(KH)::value;
     constexpr int vs_ = decltype(VS)::value, vh_ = decltype(VH)::value;
     constexpr bool next_ = decltype(NEXT)::value != 0, cur_ = decltype(CUR)::value != 0;
-    constexpr bool prev_ = decltype(PREV)::value != 0;
-    // MFMA k: even k = score k-step k / 2; odd k = P V MFMA k / 2 (chunk (k / 2) / DB, block
-    // (k / 2) % DB)
+    constexpr bool prev_ = decltype(PREV)::value != 0, pin_ = decltype(PIN)::value != 0;
+    constexpr bool pout_ = decltype(POUT)::value != 0;
+    constexpr int ks2_ = decltype(KS2)::value, kh2_ = decltype(KH2)::value;
+    constexpr int kPairSlots = M - 2;  // first-stage slots of the score pairs of the current half
     bf16x8 op[M];
     auto fetch = [&](int k) {
-      if (k % 2 == 0) {
-        if (next_) op[k] = read_k(ks_, kh_, k / 2);
+      if (k < DT) {
+        if (next_) op[k] = read_k(ks_, kh_, k);
       } else {
-        if (prev_) op[k] = read_v(vs_, 2 * vh_ + (k / 2) / DB, (k / 2) % DB);
+        if (prev_) op[k] = read_v(vs_, 2 * vh_ + (k - DT) / DB, (k - DT) % DB);
       }
     };
-    fetch(0);
-    fetch(1);
-    float mu = 0.f, ps = 0.f, mpart = kNegInf;
+    if (pin_) {
+      op[0] = carry[0];
+      op[1] = carry[1];
+#pragma unroll
+      for (int k = 2; k < kPF; k++) fetch(k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPF; k++) fetch(k);
+    }
+    float ps = 0.f, m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f, m4 = 0.f, m5 = 0.f;
+    float x[16], t[2];  // softmax pipeline registers
+    pin_def(mu);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < M; k++) {
-      if (k + 2 < M) fetch(k + 2);
-      if (k % 2 == 0) {
-        if (next_) sn = mfma_bf16(op[k], qreg[k / 2], k == 0 ? f32x16{} : sn);
+      if (k + kPF < M) {
+        fetch(k + kPF);
+      } else if (pout_ && k + kPF - M < 2) {
+        carry[k + kPF - M] = read_k(ks2_, kh2_, k + kPF - M);
+      }
+      if (k < DT) {
+        if (next_) sn = mfma_bf16(op[k], qreg[k], k == 0 ? f32x16{} : sn);
       } else {
-        if (prev_) o[(k / 2) % DB] = mfma_bf16(op[k], pp[(k / 2) / DB], o[(k / 2) % DB]);
+        if (prev_) o[(k - DT) % DB] = mfma_bf16(op[k], pp[(k - DT) / DB], o[(k - DT) % DB]);
       }
       if (cur_) {
-        if (k == 0) {
-#pragma unroll
-          for (int r = 0; r < 8; r++) mpart = fmaxf(mpart, sc[r]);
-        }
-        if (k == 1) {
-#pragma unroll
-          for (int r = 8; r < 16; r++) mpart = fmaxf(mpart, sc[r]);
-          const float mx = run ? pair_max(mpart) * p.c : kNegInf;
-          mtrue = fmaxf(mtrue, mx);
-          over = over || (mref != kNegInf && mx > mref + kRefSlack);
-          mref = (mref == kNegInf) ? mx : mref;
-          mu = !run ? kPosInf : (mref == kNegInf) ? 0.f : mref;
-        }
-        // score pairs 2 q, 2 q + 1 spread over MFMA slots 2 .. M - 1; register r goes to element
-        // r % 8 of P chunk r / 8
+        // The softmax of score pair q (registers 2 q, 2 q + 1) runs in three stages on consecutive
+        // slots a(q), a(q) + 1, a(q) + 2: the two FMAs, the two exponentials, then the bf16
+        // conversion and the row-sum additions, so no instruction waits on another of its own slot.
+        // Register r goes to element r % 8 of P chunk r / 8. The row sum adds the pair sums t(q) in
+        // order q = 0, 1, .. (one slot behind their own stage).
 #pragma unroll
         for (int q = 0; q < 8; q++) {
-          if (2 + (q * (M - 2)) / 8 == k) {
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * q], p.c, -mu));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * q + 1], p.c, -mu));
-            ps += e0 + e1;
-            pc[q >> 2][(2 * q) & 7] = (__bf16)e0;
-            pc[q >> 2][(2 * q + 1) & 7] = (__bf16)e1;
+          const int aq = (q * kPairSlots) / 8;
+          if (aq == k) {
+            x[2 * q] = __builtin_fmaf(sc[2 * q], p.c, -mu);
+            x[2 * q + 1] = __builtin_fmaf(sc[2 * q + 1], p.c, -mu);
+            pin_use(x[2 * q]);
+            pin_use(x[2 * q + 1]);
+          }
+          if (aq + 1 == k) {
+            x[2 * q] = __builtin_amdgcn_exp2f(x[2 * q]);
+            x[2 * q + 1] = __builtin_amdgcn_exp2f(x[2 * q + 1]);
+            pin_use(x[2 * q]);
+            pin_use(x[2 * q + 1]);
+          }
+          if (aq + 2 == k) {
+            pc[q >> 2][(2 * q) & 7] = (__bf16)x[2 * q];
+            pc[q >> 2][(2 * q + 1) & 7] = (__bf16)x[2 * q + 1];
+            t[q & 1] = x[2 * q] + x[2 * q + 1];
+            if (q > 0) ps = q == 1 ? t[0] : ps + t[(q - 1) & 1];
+            pin_use(t[q & 1]);
+            if (q > 0) pin_use(ps);
+            if ((q & 3) == 3) pin_use(pc[q >> 2]);
           }
         }
       }
+      if (cur_) {
+        // row max of the current half (max3 tree, then the partner lane), true max, overflow check
+        if (k == 0) {
+          m0 = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+          m1 = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
+          pin_use(m0);
+          pin_use(m1);
+        }
+        if (k == 1) {
+          m2 = fmaxf(fmaxf(sc[6], sc[7]), sc[8]);
+          m3 = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
+          pin_use(m2);
+          pin_use(m3);
+        }
+        if (k == 2) {
+          m4 = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
+          m5 = fmaxf(fmaxf(m0, m1), m2);
+          pin_use(m4);
+          pin_use(m5);
+        }
+        if (k == 3) {
+          m0 = fmaxf(m5, fmaxf(fmaxf(m3, m4), sc[15]));
+          pin_use(m0);
+        }
+        if (k == 4) {
+          m1 = pair_max(m0);
+          pin_use(m1);
+        }
+        if (k == 5) {
+          m2 = run ? m1 * p.c : kNegInf;
+          mtrue = fmaxf(mtrue, m2);
+          pin_use(mtrue);
+        }
+        if (k == 6) over = over | ((mref != kNegInf) & (m2 > mref + kRefSlack));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (cur_) lsum += ps;
+    if (cur_) lsum += ps + t[1];  // the last pair sum (q = 7)
   };
 
-  // the current half of a step: mask it if needed; does it reach this wave at all?
-  auto prepare = [&](int hidx, f32x16& sc) -> bool {
+  // Bookkeeping of half hidx once its scores s are known, before its step: mask it if needed and
+  // return the exponent offset for its softmax, the row's reference max (0 while a row has none).
+  // Only while some row of the wave still lacks a reference is this half's max taken here (it
+  // becomes the reference of those rows); otherwise the offset does not depend on the half at all.
+  // A half that does not reach this wave (run false) keeps its finite scores but gets offset
+  // +inf, so every p is 0, and its step leaves the true max alone.
+  auto finish = [&](int hidx, f32x16& s, bool& run) -> float {
     const int key0 = tile_key0(hidx >> 1);
     const bool valid = key0 >= 0;
     const int k0 = max(key0, 0) + 32 * (hidx & 1);
-    const bool run = compute && half_runs(k0);
-    if (run && half_needs_mask(k0, valid)) apply_mask(sc, k0, valid);
-    return run;
+    run = compute && half_runs(k0);
+    if (!run) return kPosInf;
+    if (half_needs_mask(k0, valid)) apply_mask(s, k0, valid);
+    if (!ref_all) {
+      const float mx = half_max(s) * p.c;
+      mref = (mref == kNegInf) ? mx : mref;
+      ref_all = __all(mref != kNegInf);
+      return (mref == kNegInf) ? 0.f : mref;
+    }
+    return mref;
   };
 
   for (int pass = 0; pass < 2; pass++) {
@@ -380,10 +469,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
     }
     if (pass == 1 && overflow) mref = mtrue;
     over = false;
+    ref_all = false;
 
     if (ntiles > 0) {
       f32x16 sx, sy;        // score buffers: the pipeline alternates between them
       bf16x8 pu[2], pv[2];  // P buffers, likewise
+      bf16x8 carry[2];      // operands handed from step to step
+      float mu;
+      bool run;
       // prologue: K(0), K(1) and V(0) land; scores of half 0
       issue_k(0, 0);
       if (ntiles > 1) issue_k(1, 1);
@@ -393,15 +486,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
       sy = f32x16{};
 #pragma unroll
       for (int t = 0; t < DT; t++) sy = mfma_bf16(read_k(0, 0, t), qreg[t], sy);
+      mu = finish(0, sy, run);
       // step 0: softmax of half 0, scores of half 1 (K(0), second half), no P V yet
-      {
-        const bool run = prepare(0, sy);
-        step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, sx, sy, pv, pu, run);
-      }
+      step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, sx, sy,
+           pv, pu, carry, mu, run);
       // barrier of tile 0: every wave is done with K(0); fill K(2) and V(1)
       __syncthreads();
       if (ntiles > 2) issue_k(2, 0);
       if (ntiles > 1) issue_v(1, 1);
+      mu = finish(1, sx, run);
 
       // Tile it (parity PAR = it % 2) runs steps 2 it + 1 and 2 it + 2:
       //   step 2 it + 1: softmax of half 2 it + 1 (sx -> pv), scores of half 2 it + 2 from K(it + 1)
@@ -415,18 +508,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
         constexpr int par = decltype(PAR)::value;
         constexpr bool last = decltype(LAST)::value != 0;
         if constexpr (!last) {
-          const bool run1 = prepare(2 * it + 1, sx);
-          step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<1>{}, sy, sx, pu, pv, run1);
-          const bool run2 = prepare(2 * it + 2, sy);
-          step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, sx, sy, pv, pu, run2);
+          step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<1>{}, IC<par ^ 1>{},
+               IC<1>{}, sy, sx, pu, pv, carry, mu, run);
+          mu = finish(2 * it + 2, sy, run);
+          step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{},
+               IC<0>{}, sx, sy, pv, pu, carry, mu, run);
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it + 2), V(it + 1)
           __syncthreads();
           if (it + 3 < ntiles) issue_k(it + 3, par ^ 1);
           if (it + 2 < ntiles) issue_v(it + 2, par);
+          mu = finish(2 * it + 3, sx, run);
         } else {
-          const bool run1 = prepare(2 * it + 1, sx);
-          step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, sy, sx, pu, pv, run1);
-          step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, sx, sy, pv, pu, false);
+          step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
+               IC<0>{}, sy, sx, pu, pv, carry, mu, run);
+          step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
+               IC<0>{}, sx, sy, pv, pu, carry, mu, false);
         }
       };
       int it = 0;
