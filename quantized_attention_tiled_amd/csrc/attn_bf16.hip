@@ -459,6 +459,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
     return mref;
   };
 
+  // Tile i is plain when both its halves reach every row of the workgroup with no key masked: no
+  // ragged sequence end, no causal diagonal, no boolean mask, a valid kept-list entry. In a plain
+  // tile, once every row of the wave has its reference max, the bookkeeping of a half is just that
+  // reference (one predicted scalar branch per half).
+  auto tile_plain = [&](int i) -> bool {
+    if constexpr ((MODE & kMask) != 0) return false;
+    const int key0 = tile_key0(i);
+    if (key0 < 0 || key0 + kKT > Lkv) return false;
+    if constexpr ((MODE & kCausal) != 0) return key0 + kKT - 1 <= row_begin + off;
+    return true;
+  };
+  auto bookkeep = [&](bool fast, int hidx, f32x16& s, bool& run) -> float {
+    if (__builtin_expect(fast, 1)) {
+      run = true;
+      return mref;
+    }
+    return finish(hidx, s, run);
+  };
+
   for (int pass = 0; pass < 2; pass++) {
     // pass 0 for everyone; pass 1 only recomputes waves that flagged an outgrown reference
     compute = pass == 0 || overflow;
@@ -508,16 +527,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
         constexpr int par = decltype(PAR)::value;
         constexpr bool last = decltype(LAST)::value != 0;
         if constexpr (!last) {
+          const bool fast = compute && ref_all && tile_plain(it + 1);
           step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<1>{}, IC<par ^ 1>{},
                IC<1>{}, sy, sx, pu, pv, carry, mu, run);
-          mu = finish(2 * it + 2, sy, run);
+          mu = bookkeep(fast, 2 * it + 2, sy, run);
           step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{},
                IC<0>{}, sx, sy, pv, pu, carry, mu, run);
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it + 2), V(it + 1)
           __syncthreads();
           if (it + 3 < ntiles) issue_k(it + 3, par ^ 1);
           if (it + 2 < ntiles) issue_v(it + 2, par);
-          mu = finish(2 * it + 3, sx, run);
+          mu = bookkeep(fast, 2 * it + 3, sx, run);
         } else {
           step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
                IC<0>{}, sy, sx, pu, pv, carry, mu, run);
