@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
     ntiles = kv_end > 0 ? (kv_end + kKT - 1) / kKT : 0;
   }
   // key0 of tile i, or -1 when a kept-list entry is out of range (the tile contributes nothing)
-  auto tile_key0 = [&](int i) -> int {
+  auto tile_key0 = [&](int i) __attribute__((always_inline)) -> int {
     if constexpr ((MODE & kSparse) != 0) {
       const int blk = list[i >> 1];
       return (blk >= 0 && blk < p.KB) ? blk * kBlock + (i & 1) * kKT : -1;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   const int kv_extent = Lkv > 0 ? (int)((Lkv - 1) * key_bytes) + T::kRowBytes : 0;
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, kv_extent, kBufferFlags);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, kv_extent, kBufferFlags);
-  auto issue_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int lds_off, int key0, uint32_t lane_off) {
+  auto issue_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int lds_off, int key0, uint32_t lane_off) __attribute__((always_inline)) {
     // an out-of-range kept-list entry loads the first keys (the tile is masked out entirely)
     const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(max(key0, 0)) * (uint32_t)key_bytes;
 #pragma unroll
@@ -213,8 +213,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(smem + lds_off + (n * kWaves + wave) * 1024), 16,
                                                lane_off, soff + (uint32_t)(n * kLoadRows * key_bytes), 0, 0);
   };
-  auto issue_k = [&](int i, int slot) { issue_tile(k_rsrc, kOffK + slot * T::kBytes, tile_key0(i), k_lane_off); };
-  auto issue_v = [&](int i, int slot) { issue_tile(v_rsrc, kOffV + slot * T::kBytes, tile_key0(i), v_lane_off); };
+  auto issue_k = [&](int i, int slot) __attribute__((always_inline)) { issue_tile(k_rsrc, kOffK + slot * T::kBytes, tile_key0(i), k_lane_off); };
+  auto issue_v = [&](int i, int slot) __attribute__((always_inline)) { issue_tile(v_rsrc, kOffV + slot * T::kBytes, tile_key0(i), v_lane_off); };
 
   // ---- this wave's query rows as the Q^T B operand: lane (hl, l32) holds row l32, 16-byte chunk
   // 2 t + hl for k-step t ----
@@ -249,10 +249,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
       vaddr[db] = vrow0 * T::kRowBytes + ((chunk ^ vs) << 4) + 8 * (sl & 1);
     }
   }
-  auto read_k = [&](int slot, int hf, int t) -> bf16x8 {
+  auto read_k = [&](int slot, int hf, int t) __attribute__((always_inline)) -> bf16x8 {
     return *(const bf16x8*)(smem + kOffK + slot * T::kBytes + hf * 32 * T::kRowBytes + kaddr[t]);
   };
-  auto read_v = [&](int slot, int kc, int db) -> bf16x8 {
+  auto read_v = [&](int slot, int kc, int db) __attribute__((always_inline)) -> bf16x8 {
     const uint8_t* base = smem + kOffV + slot * T::kBytes + kc * 16 * T::kRowBytes + vaddr[db];
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * T::kRowBytes));
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
 
   // mask one 32-key half tile in place (keys k0 .. k0 + 31): keys past the sequence, above the
   // causal diagonal, or set in atten_mask
-  auto apply_mask = [&](f32x16& s, int k0, bool valid) {
+  auto apply_mask = [&](f32x16& s, int k0, bool valid) __attribute__((always_inline)) {
     const int q = wrow0 + l32;
     // last allowed key of this row, relative to k0 and to this lane's 4 hl offset
     int lim = Lkv - 1;
@@ -283,14 +283,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
       }
     }
   };
-  auto half_needs_mask = [&](int k0, bool valid) {
+  auto half_needs_mask = [&](int k0, bool valid) __attribute__((always_inline)) {
     bool need = !valid || k0 + 32 > Lkv;
     if constexpr ((MODE & kCausal) != 0) need = need || (k0 + 31 > wrow0 + off);
     if constexpr ((MODE & kMask) != 0) need = true;
     return need;
   };
   // a causal half tile wholly above this wave's diagonal contributes nothing
-  auto half_runs = [&](int k0) {
+  auto half_runs = [&](int k0) __attribute__((always_inline)) {
     bool run = wave_active;
     if constexpr ((MODE & kCausal) != 0) run = run && k0 <= wrow_last + off;
     return run;
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   bool ref_all = false;  // every row of this wave has its reference max (wave-uniform)
 
   // row max of a 32-key half over this lane's 16 scores and its partner lane l ^ 32 (max3 tree)
-  auto half_max = [&](const f32x16& s) -> float {
+  auto half_max = [&](const f32x16& s) __attribute__((always_inline)) -> float {
     const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]), m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
     const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]), m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
     const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   // scheduling barriers keep each MFMA with its slice of VALU work.
   auto step = [&](auto KS, auto KH, auto VS, auto VH, auto NEXT, auto CUR, auto PREV, auto PIN, auto POUT,
                   auto KS2, auto KH2, f32x16& sn, const f32x16& sc, const bf16x8 (&pp)[2], bf16x8 (&pc)[2],
-                  bf16x8 (&carry)[2], float mu, bool run) {
+                  bf16x8 (&carry)[2], float mu, bool run) __attribute__((always_inline)) {
     constexpr int ks_ = decltype(KS)::value, kh_ = decltype(KH)::value;
     constexpr int vs_ = decltype(VS)::value, vh_ = decltype(VH)::value;
     constexpr bool next_ = decltype(NEXT)::value != 0, cur_ = decltype(CUR)::value != 0;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
     constexpr int ks2_ = decltype(KS2)::value, kh2_ = decltype(KH2)::value;
     constexpr int kPairSlots = M - 2;  // first-stage slots of the score pairs of the current half
     bf16x8 op[M];
-    auto fetch = [&](int k) {
+    auto fetch = [&](int k) __attribute__((always_inline)) {
       if (k < DT) {
         if (next_) op[k] = read_k(ks_, kh_, k);
       } else {
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   // becomes the reference of those rows); otherwise the offset does not depend on the half at all.
   // A half that does not reach this wave (run false) keeps its finite scores but gets offset
   // +inf, so every p is 0, and its step leaves the true max alone.
-  auto finish = [&](int hidx, f32x16& s, bool& run) -> float {
+  auto finish = [&](int hidx, f32x16& s, bool& run) __attribute__((always_inline)) -> float {
     const int key0 = tile_key0(hidx >> 1);
     const bool valid = key0 >= 0;
     const int k0 = max(key0, 0) + 32 * (hidx & 1);
@@ -463,14 +463,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   // ragged sequence end, no causal diagonal, no boolean mask, a valid kept-list entry. In a plain
   // tile, once every row of the wave has its reference max, the bookkeeping of a half is just that
   // reference (one predicted scalar branch per half).
-  auto tile_plain = [&](int i) -> bool {
+  auto tile_plain = [&](int i) __attribute__((always_inline)) -> bool {
     if constexpr ((MODE & kMask) != 0) return false;
     const int key0 = tile_key0(i);
     if (key0 < 0 || key0 + kKT > Lkv) return false;
     if constexpr ((MODE & kCausal) != 0) return key0 + kKT - 1 <= row_begin + off;
     return true;
   };
-  auto bookkeep = [&](bool fast, int hidx, f32x16& s, bool& run) -> float {
+  auto bookkeep = [&](bool fast, int hidx, f32x16& s, bool& run) __attribute__((always_inline)) -> float {
     if (__builtin_expect(fast, 1)) {
       run = true;
       return mref;
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
       // then the barrier of tile it + 1: K(it + 2) and V(it + 1) have landed everywhere and the
       // slots of K(it + 1) and V(it) are free, so K(it + 3) and V(it + 2) are issued into them.
       // The last tile has no next scores and no half 2 it + 2.
-      auto tile = [&](auto PAR, auto LAST, int it) {
+      auto tile = [&](auto PAR, auto LAST, int it) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
         constexpr bool last = decltype(LAST)::value != 0;
         if constexpr (!last) {
