@@ -1,0 +1,76 @@
+"""Build invariants of the gfx950 kernels, checked from the compiler's resource report (hipcc
+cross-compiles here; no GPU needed).
+
+* No kernel keeps data in private (scratch) memory, except the boolean-mask instantiations of the
+  bf16 kernel, whose per-element mask loads spill a few dozen registers. Scratch use elsewhere has
+  meant an outlined lambda that demoted the kernel arguments and register arrays to memory.
+* The bf16 kernel runs two waves per SIMD (at most 256 VGPRs) with at most 80 KiB of LDS per
+  workgroup, so that two workgroups share a CU.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from quantized_attention_tiled_amd import build as B
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                                reason="hipcc not available")
+
+MASK_MODES = {2, 3}  # kMask, kCausal | kMask
+
+
+def _resources(src):
+    cmd = [B.hipcc(), f"--offload-arch={B.ARCH}", "-O3", "-std=c++17", "-c", "--cuda-device-only",
+           f"-I{B.INCLUDE}", f"-I{B.CSRC}", *B.DEVICE_FLAGS, *B.SOURCE_FLAGS.get(src, []),
+           os.path.join(B.CSRC, src), "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    kernels = {}
+    cur = None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return kernels
+
+
+@pytest.fixture(scope="module")
+def bf16():
+    return _resources("attn_bf16.hip")
+
+
+def test_bf16_kernels_use_no_scratch(bf16):
+    assert bf16, "no kernels reported"
+    for name, res in bf16.items():
+        m = re.search(r"attn_bf16_kernelILi(\d+)ELi(\d+)EEE", name)
+        assert m, name
+        mode = int(m.group(2))
+        if mode in MASK_MODES:
+            continue
+        assert res.get("ScratchSize", 0) == 0, (name, res)
+        assert res.get("VGPRs Spill", 0) == 0, (name, res)
+
+
+def test_bf16_two_waves_per_simd_and_lds(bf16):
+    for name, res in bf16.items():
+        assert res.get("Occupancy", 0) >= 2, (name, res)
+        assert res.get("LDS Size", 0) <= 80 * 1024, (name, res)
+
+
+@pytest.mark.parametrize("src", [
+    pytest.param("attn_qbsa.hip", marks=pytest.mark.xfail(reason="the quantised kernel still spills 80 bytes per lane",
+                                                          strict=False)),
+    "quant.hip"])
+def test_other_kernels_use_no_scratch(src):
+    ks = _resources(src)
+    assert ks
+    for name, res in ks.items():
+        assert res.get("ScratchSize", 0) == 0, (name, res)
