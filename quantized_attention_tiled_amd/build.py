@@ -24,9 +24,10 @@ ARCH = "gfx950"
 # Packed fp32 instructions are switched off for all device code; the host
 # pass warns that it does not know the feature, which is harmless.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# The bf16 attention kernel keeps its score accumulators in VGPRs (compiler MFMAs) and its output
-# accumulators in AGPRs (inline-asm MFMAs); see the comment on mfma_acc in attn_bf16.hip.
-SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# The attention kernels run two waves per SIMD (256 registers per lane) and keep every MFMA
+# accumulator in ordinary VGPRs, so no accumulator is copied between register files.
+SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+                "attn_qbsa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def hipcc() -> str:
