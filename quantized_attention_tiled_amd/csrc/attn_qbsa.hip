@@ -77,6 +77,13 @@ __device__ __forceinline__ void pin_use(const T& x) {
 
 __device__ __forceinline__ int imax3(int a, int b, int c) { return max(max(a, b), c); }
 
+// a register whose contents do not matter (an empty asm output costs no instruction)
+__device__ __forceinline__ int any_reg() {
+  int r;
+  asm volatile("" : "=v"(r));
+  return r;
+}
+
 // max / sum of x over lanes l and l ^ 32 (v_permlane32_swap returns both halves)
 __device__ __forceinline__ int pair_max_i(int x) {
   const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
@@ -338,10 +345,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
               pin_use(x[2 * q + 1]);
             }
             if (aq + 2 == k) {
+              // word 1 of an even pair's dword is left as it was (pair q + 1 writes it)
               if (q & 1)
                 pc[q >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2 * q], x[2 * q + 1], pc[q >> 1], true);
               else
-                pc[q >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2 * q], x[2 * q + 1], 0, false);
+                pc[q >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2 * q], x[2 * q + 1], any_reg(), false);
               t[q & 1] = x[2 * q] + x[2 * q + 1];
               if (q > 0) ps = q == 1 ? t[0] : ps + t[(q - 1) & 1];
               pin_use(t[q & 1]);
