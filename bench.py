@@ -56,8 +56,9 @@ def flop_counts(w):
     """(executed, useful, dense_equivalent) flop counts: 2 D flops per (q, k)
     pair for Q.K^T and again for P.V. Executed counts the (row, key) pairs of
     the tiles the kernel processes: whole kept 128-key blocks for block-sparse;
-    for causal masks, each 64-row wave slice runs over the keys up to the end
-    of the 64-key tile that holds its last row's diagonal."""
+    for causal masks, the rows of each 128-row q-block (one workgroup) run over
+    the keys up to the end of the 64-key tile that holds the diagonal of the
+    q-block's last row."""
     D = w.D
     if w.layout == "TND":
         lens = np.diff(w.cu_seqlens_q)
@@ -67,8 +68,8 @@ def flop_counts(w):
             dense += L * L
             if w.sparse_mode in (2, 3):          # Lq == Lkv here, so both causal modes coincide
                 useful += L * (L + 1) // 2
-                for r0 in range(0, L, 64):
-                    r1 = min(L, r0 + 64)
+                for r0 in range(0, L, 128):
+                    r1 = min(L, r0 + 128)
                     executed += (r1 - r0) * min(L, ((r1 + 63) // 64) * 64)
             else:
                 useful += L * L
