@@ -14,9 +14,9 @@
 // whose matrix and vector work interleave.
 //   * Q^T, the B operand of S^T = K Q^T, stays in registers for the whole kernel;
 //   * K and V stream through LDS in 64-key tiles, each in a ring of two slots, straight from
-//     HBM with global_load_lds (16 bytes per lane, no staging registers) into XOR-swizzled
-//     row-major tiles. Right after the single barrier of tile j the loads of K(j + 2) and
-//     V(j + 1) are issued; they land by the barrier of tile j + 1;
+//     HBM with buffer_load ... lds (16 bytes per lane, no staging registers) into XOR-swizzled
+//     row-major tiles. The loads of K(j + 2) and V(j + 1) are spread over the MFMA slots of
+//     the first step after the single barrier of tile j; they land by the barrier of tile j + 1;
 //   * scores are formed transposed on v_mfma_f32_32x32x16_bf16, so one query sits in one lane
 //     column: the row max and the row sum are register chains plus one v_permlane32_swap;
 //   * P stays in registers: S^T converted to bf16 is directly the B operand of
@@ -45,7 +45,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(1))) const void gbl_cvoid;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -55,8 +54,6 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kRefSlack = 64.0f;  // base-2 exponent growth tolerated above a row's reference max
-// word 3 of a raw buffer resource on gfx9-family GPUs (dword data format; no swizzle, no stride)
-constexpr int kBufferFlags = 0x00020000;
 
 template <int V>
 struct IC {
@@ -203,15 +200,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   const uint32_t v_lane_off = (uint32_t)(lrow * key_bytes) + (uint32_t)((lphys ^ T::vswz(lrow)) << 4);
   constexpr int kLoadRows = kWaves * T::kRowsPerLoad;  // rows between two loads of one wave
   const int kv_extent = Lkv > 0 ? (int)((Lkv - 1) * key_bytes) + T::kRowBytes : 0;
-  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, kv_extent, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, kv_extent, kBufferFlags);
-  auto issue_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int lds_off, int key0, uint32_t lane_off) __attribute__((always_inline)) {
+  const rsrc4 k_rsrc = make_rsrc(kp, (uint32_t)kv_extent);
+  const rsrc4 v_rsrc = make_rsrc(vp, (uint32_t)kv_extent);
+  auto issue_tile = [&](const rsrc4& rsrc, int lds_off, int key0, uint32_t lane_off) __attribute__((always_inline)) {
     // an out-of-range kept-list entry loads the first keys (the tile is masked out entirely)
     const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(max(key0, 0)) * (uint32_t)key_bytes;
 #pragma unroll
     for (int n = 0; n < T::kLoadsPerWave; n++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(smem + lds_off + (n * kWaves + wave) * 1024), 16,
-                                               lane_off, soff + (uint32_t)(n * kLoadRows * key_bytes), 0, 0);
+      load_lds16(rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), lane_off, soff + (uint32_t)(n * kLoadRows * key_bytes));
+  };
+  // Load n of tile i into a ring slot, with soff = tile_soff(i): the ring loads after the first
+  // ones are spread over the MFMA slots of a pipeline step instead of being issued in a burst.
+  // A tile past the end loads the first keys into a slot that is not read again.
+  auto issue_one = [&](const rsrc4& rsrc, int lds_off, uint32_t soff, uint32_t lane_off, int n) __attribute__((always_inline)) {
+    load_lds16(rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), lane_off, soff + (uint32_t)(n * kLoadRows * key_bytes));
+  };
+  auto tile_soff = [&](int i) __attribute__((always_inline)) -> uint32_t {
+    const int key0 = i < ntiles ? tile_key0(i) : 0;
+    return (uint32_t)__builtin_amdgcn_readfirstlane(max(key0, 0)) * (uint32_t)key_bytes;
   };
   auto issue_k = [&](int i, int slot) __attribute__((always_inline)) { issue_tile(k_rsrc, kOffK + slot * T::kBytes, tile_key0(i), k_lane_off); };
   auto issue_v = [&](int i, int slot) __attribute__((always_inline)) { issue_tile(v_rsrc, kOffV + slot * T::kBytes, tile_key0(i), v_lane_off); };
@@ -320,11 +326,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   // exponent offset mu, P into pc) and its row max, which only feeds the true max and the overflow
   // check (run: the half reaches this wave). NEXT / CUR / PREV switch the three parts on. Operands
   // are read from LDS kPF slots ahead; PIN says the first two arrive in carry, POUT that the last
-  // slots read the first two of the following step (K slot KS2, half KH2) into carry. Hard
-  // scheduling barriers keep each MFMA with its slice of VALU work.
+  // slots read the first two of the following step (K slot KS2, half KH2) into carry. DMA = 1 +
+  // KD + 2 VD spreads the loads of the next K tile (into K slot KD, from byte offset dk) and V
+  // tile (V slot VD, from dv) over the step's slots; DMA = 0 issues none. Hard scheduling barriers
+  // keep each MFMA with its slice of VALU work.
   auto step = [&](auto KS, auto KH, auto VS, auto VH, auto NEXT, auto CUR, auto PREV, auto PIN, auto POUT,
-                  auto KS2, auto KH2, f32x16& sn, const f32x16& sc, const bf16x8 (&pp)[2], bf16x8 (&pc)[2],
-                  bf16x8 (&carry)[2], float mu, bool run) __attribute__((always_inline)) {
+                  auto KS2, auto KH2, auto DMA, f32x16& sn, const f32x16& sc, const bf16x8 (&pp)[2],
+                  bf16x8 (&pc)[2], bf16x8 (&carry)[2], float mu, bool run, uint32_t dk, uint32_t dv)
+                  __attribute__((always_inline)) {
+    constexpr int dma_ = decltype(DMA)::value;
     constexpr int ks_ = decltype(KS)::value, kh_ = decltype(KH)::value;
     constexpr int vs_ = decltype(VS)::value, vh_ = decltype(VH)::value;
     constexpr bool next_ = decltype(NEXT)::value != 0, cur_ = decltype(CUR)::value != 0;
@@ -359,6 +369,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
         fetch(k + kPF);
       } else if (pout_ && k + kPF - M < 2) {
         carry[k + kPF - M] = read_k(ks2_, kh2_, k + kPF - M);
+      }
+      if constexpr (dma_ != 0) {
+        constexpr int L = T::kLoadsPerWave;
+#pragma unroll
+        for (int j = 0; j < 2 * L; j++) {
+          if ((j * M) / (2 * L) != k) continue;
+          if (j < L)
+            issue_one(k_rsrc, kOffK + ((dma_ - 1) & 1) * T::kBytes, dk, k_lane_off, j);
+          else
+            issue_one(v_rsrc, kOffV + ((dma_ - 1) >> 1) * T::kBytes, dv, v_lane_off, j - L);
+        }
       }
       if (k < DT) {
         if (next_) sn = mfma_bf16(op[k], qreg[k], k == 0 ? f32x16{} : sn);
@@ -507,12 +528,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
       for (int t = 0; t < DT; t++) sy = mfma_bf16(read_k(0, 0, t), qreg[t], sy);
       mu = finish(0, sy, run);
       // step 0: softmax of half 0, scores of half 1 (K(0), second half), no P V yet
-      step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, sx, sy,
-           pv, pu, carry, mu, run);
-      // barrier of tile 0: every wave is done with K(0); fill K(2) and V(1)
+      step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{},
+           sx, sy, pv, pu, carry, mu, run, 0u, 0u);
+      // barrier of tile 0: every wave is done with K(0); K(2) and V(1) are loaded during step 1
       __syncthreads();
-      if (ntiles > 2) issue_k(2, 0);
-      if (ntiles > 1) issue_v(1, 1);
+      uint32_t dk = tile_soff(2), dv = tile_soff(1);
       mu = finish(1, sx, run);
 
       // Tile it (parity PAR = it % 2) runs steps 2 it + 1 and 2 it + 2:
@@ -521,28 +541,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
       //   step 2 it + 2: softmax of half 2 it + 2 (sy -> pu), scores of half 2 it + 3 from K(it + 1)
       //                  second half into sx, P(2 it + 1) V(it) on keys 32..63 (pv);
       // then the barrier of tile it + 1: K(it + 2) and V(it + 1) have landed everywhere and the
-      // slots of K(it + 1) and V(it) are free, so K(it + 3) and V(it + 2) are issued into them.
-      // The last tile has no next scores and no half 2 it + 2.
+      // slots of K(it + 1) and V(it) are free; K(it + 3) and V(it + 2) are loaded into them during
+      // the first step of tile it + 1. The last tile has no next scores and no half 2 it + 2.
       auto tile = [&](auto PAR, auto LAST, int it) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
         constexpr bool last = decltype(LAST)::value != 0;
         if constexpr (!last) {
           const bool fast = compute && ref_all && tile_plain(it + 1);
+          // loads of K(it + 2) into K slot PAR and V(it + 1) into V slot PAR ^ 1
           step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<1>{}, IC<par ^ 1>{},
-               IC<1>{}, sy, sx, pu, pv, carry, mu, run);
+               IC<1>{}, IC<1 + par + 2 * (par ^ 1)>{}, sy, sx, pu, pv, carry, mu, run, dk, dv);
           mu = bookkeep(fast, 2 * it + 2, sy, run);
           step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{},
-               IC<0>{}, sx, sy, pv, pu, carry, mu, run);
+               IC<0>{}, IC<0>{}, sx, sy, pv, pu, carry, mu, run, 0u, 0u);
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it + 2), V(it + 1)
           __syncthreads();
-          if (it + 3 < ntiles) issue_k(it + 3, par ^ 1);
-          if (it + 2 < ntiles) issue_v(it + 2, par);
+          dk = tile_soff(it + 3);
+          dv = tile_soff(it + 2);
           mu = bookkeep(fast, 2 * it + 3, sx, run);
         } else {
           step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
-               IC<0>{}, sy, sx, pu, pv, carry, mu, run);
+               IC<0>{}, IC<0>{}, sy, sx, pu, pv, carry, mu, run, 0u, 0u);
           step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
-               IC<0>{}, sx, sy, pv, pu, carry, mu, false);
+               IC<0>{}, IC<0>{}, sx, sy, pv, pu, carry, mu, false, 0u, 0u);
         }
       };
       int it = 0;
@@ -559,7 +580,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
     }
 
     // Does any wave of the workgroup need the second pass? The flags go through the first K slot:
-    // no load is in flight (the last tile issues none) and after this barrier no wave reads it.
+    // no load is in flight (each wave waits for its own) and after this barrier no wave reads it.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     int* const wave_flags = (int*)(smem + kOffK);
     if (pass == 0) overflow = __any(over);

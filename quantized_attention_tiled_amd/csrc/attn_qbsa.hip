@@ -14,7 +14,8 @@
 // so two workgroups share a CU and every SIMD runs two independent waves.
 //   * Q^T (INT8) stays in registers as the B operand of S^T = K Q^T on v_mfma_i32_32x32x32_i8;
 //   * K and V stream straight from HBM into XOR-swizzled row-major LDS tiles with
-//     buffer_load ... lds (16 bytes per lane), in rings of two slots, one barrier per kept block;
+//     buffer_load ... lds (16 bytes per lane), in rings of two slots, one barrier per kept block,
+//     the loads spread over the MFMA slots of the step after the barrier;
 //     the kept-list entry and the key scale of a block are fetched by vector loads two blocks
 //     ahead, so no scalar load is ever waited on between the LDS reads;
 //   * an INT8 score accumulator starts at the bit pattern of 1.5 * 2^23: read as a float it is
@@ -45,7 +46,6 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -182,16 +182,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
   const uint32_t v_lane_off = (uint32_t)(lrow * key_bytes) + (uint32_t)((lphys ^ T::vswz(lrow)) << 4);
   constexpr int kLoadRows = kWaves * T::kRowsPerLoad;
   const int kv_extent = Lkv > 0 ? (int)((Lkv - 1) * key_bytes) + T::kRowBytes : 0;
-  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, kv_extent, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, kv_extent, kBufferFlags);
-  auto issue_tile = [&](__amdgpu_buffer_rsrc_t rsrc, int lds_off, int blk, uint32_t lane_off) __attribute__((always_inline)) {
-    // an out-of-range kept-list entry loads the first keys (the block is then skipped)
+  const rsrc4 k_rsrc = make_rsrc(kp, (uint32_t)kv_extent);
+  const rsrc4 v_rsrc = make_rsrc(vp, (uint32_t)kv_extent);
+  // byte offset of kept block blk; an out-of-range entry (or a block past the end of the list)
+  // loads the first keys, into a slot that is then skipped or not read again
+  auto block_soff = [&](int blk) __attribute__((always_inline)) -> uint32_t {
     const int key0 = blk_valid(blk) ? blk * kTK : 0;
-    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(key0) * (uint32_t)key_bytes;
+    return (uint32_t)__builtin_amdgcn_readfirstlane(key0) * (uint32_t)key_bytes;
+  };
+  auto issue_one = [&](const rsrc4& rsrc, int lds_off, uint32_t soff, uint32_t lane_off, int n) __attribute__((always_inline)) {
+    load_lds16(rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), lane_off,
+               soff + (uint32_t)(n * kLoadRows * key_bytes));
+  };
+  auto issue_tile = [&](const rsrc4& rsrc, int lds_off, int blk, uint32_t lane_off) __attribute__((always_inline)) {
+    const uint32_t soff = block_soff(blk);
 #pragma unroll
-    for (int n = 0; n < T::kLoadsPerWave; n++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(smem + lds_off + (n * kWaves + wave) * 1024), 16,
-                                               lane_off, soff + (uint32_t)(n * kLoadRows * key_bytes), 0, 0);
+    for (int n = 0; n < T::kLoadsPerWave; n++) issue_one(rsrc, lds_off, soff, lane_off, n);
   };
   auto issue_k = [&](int blk, int slot) __attribute__((always_inline)) { issue_tile(k_rsrc, kOffK + slot * T::kBytes, blk, k_lane_off); };
   auto issue_v = [&](int blk, int slot) __attribute__((always_inline)) { issue_tile(v_rsrc, kOffV + slot * T::kBytes, blk, v_lane_off); };
@@ -276,10 +282,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     // the MFMAs the VALU runs the softmax of the current 64 keys (sc, factor ct, offset cc, P
     // into pc, row sum into lsum). NEXT / CUR / PREV switch the three parts on. Operands are read
     // from LDS kPF slots ahead; PIN says the first two arrive in carry, POUT that the last slots
-    // read the first two of the following step (K slot KS2, half KH2) into carry.
+    // read the first two of the following step (K slot KS2, half KH2) into carry. DMA = 1 + KD +
+    // 2 VD spreads the loads of the next K tile (into K slot KD, from byte offset dk) and V tile
+    // (V slot VD, from dv) over the step's slots; DMA = 0 issues none.
     auto step = [&](auto KS, auto KH, auto VS, auto VH, auto NEXT, auto CUR, auto PREV, auto PIN, auto POUT,
-                    auto KS2, auto KH2, i32x16 (&sn)[2], const i32x16 (&sc)[2], const i32x8& pp, i32x8& pc,
-                    i32x4 (&carry)[2], float ct, float cc, int& mm) __attribute__((always_inline)) {
+                    auto KS2, auto KH2, auto DMA, i32x16 (&sn)[2], const i32x16 (&sc)[2], const i32x8& pp,
+                    i32x8& pc, i32x4 (&carry)[2], float ct, float cc, int& mm, uint32_t dk, uint32_t dv)
+                    __attribute__((always_inline)) {
+      constexpr int dma_ = decltype(DMA)::value;
       constexpr int ks_ = decltype(KS)::value, kh_ = decltype(KH)::value;
       constexpr int vs_ = decltype(VS)::value, vh_ = decltype(VH)::value;
       constexpr bool next_ = decltype(NEXT)::value != 0, cur_ = decltype(CUR)::value != 0;
@@ -316,6 +326,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
           fetch(k + kPF);
         } else if (pout_ && k + kPF - M < 2) {
           carry[k + kPF - M] = read_k(ks2_, kh2_, 0, k + kPF - M);
+        }
+        if constexpr (dma_ != 0) {
+          constexpr int L = T::kLoadsPerWave;
+#pragma unroll
+          for (int j = 0; j < 2 * L; j++) {
+            if ((j * M) / (2 * L) != k) continue;
+            if (j < L)
+              issue_one(k_rsrc, kOffK + ((dma_ - 1) & 1) * T::kBytes, dk, k_lane_off, j);
+            else
+              issue_one(v_rsrc, kOffV + ((dma_ - 1) >> 1) * T::kBytes, dv, v_lane_off, j - L);
+          }
         }
         if (k < NS) {
           const int kb = k / DT, tt = k % DT;
@@ -483,12 +504,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     const bool fast0 = tile_plain(b0);
     cc = bookkeep(false, b0, 0, sy, 0, ct);
     // step 0: softmax of step 0, scores of step 1 (K(0), second half), no P V yet
-    step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, sx, sy,
-         pv, pu, carry, ct, cc, mm);
-    // barrier of block 0: every wave is done with K(0); fill K(2) and V(1)
+    step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{},
+         sx, sy, pv, pu, carry, ct, cc, mm, 0u, 0u);
+    // barrier of block 0: every wave is done with K(0); K(2) and V(1) are loaded during step 1
     __syncthreads();
-    if (ntiles > 2) issue_k(b2, 0);
-    if (ntiles > 1) issue_v(b1, 1);
+    uint32_t dk = block_soff(b2), dv = block_soff(b1);
     int k2v = load_ksc(b2);
     int b3v = load_blk(3);
     cc = bookkeep(fast0, b0, 1, sx, mm, ct);
@@ -499,24 +519,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     //   step 2 it + 2: softmax of step 2 it + 2 (sy -> pu), scores of step 2 it + 3 from K(it + 1)
     //                  second half into sx, P(2 it + 1) V(it) on keys 64..127 (pv);
     // then the barrier of block it + 1: K(it + 2) and V(it + 1) have landed everywhere and the
-    // slots of K(it + 1) and V(it) are free, so K(it + 3) and V(it + 2) are issued into them.
-    // The last block has no next scores and no step 2 it + 2.
+    // slots of K(it + 1) and V(it) are free; K(it + 3) and V(it + 2) are loaded into them during
+    // the first step of block it + 1. The last block has no next scores and no step 2 it + 2.
     auto tile = [&](auto PAR, auto LAST, int it) __attribute__((always_inline)) {
       constexpr int par = decltype(PAR)::value;
       constexpr bool last = decltype(LAST)::value != 0;
       if constexpr (!last) {
         const bool fast = tile_plain(b1);
+        // loads of K(it + 2) into K slot PAR and V(it + 1) into V slot PAR ^ 1
         step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<1>{}, IC<par ^ 1>{},
-             IC<1>{}, sy, sx, pu, pv, carry, ct, cc, mm);
+             IC<1>{}, IC<1 + par + 2 * (par ^ 1)>{}, sy, sx, pu, pv, carry, ct, cc, mm, dk, dv);
         ct = ct_of(k1v);
         cc = bookkeep(fast, b1, 0, sy, mm, ct);
         step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{},
-             IC<0>{}, sx, sy, pv, pu, carry, ct, cc, mm);
+             IC<0>{}, IC<0>{}, sx, sy, pv, pu, carry, ct, cc, mm, 0u, 0u);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it + 2), V(it + 1), list entry and scale
         __syncthreads();
         const int b3 = __builtin_amdgcn_readfirstlane(b3v);
-        if (it + 3 < ntiles) issue_k(b3, par ^ 1);
-        if (it + 2 < ntiles) issue_v(b2, par);
+        dk = block_soff(b3);
+        dv = block_soff(b2);
         const int k3v = load_ksc(b3);
         b3v = load_blk(it + 4);
         cc = bookkeep(fast, b1, 1, sx, mm, ct);
@@ -526,14 +547,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
         k2v = k3v;
       } else {
         step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
-             IC<0>{}, sy, sx, pu, pv, carry, ct, cc, mm);
+             IC<0>{}, IC<0>{}, sy, sx, pu, pv, carry, ct, cc, mm, 0u, 0u);
         if (pending) {
 #pragma unroll
           for (int db = 0; db < DB; db++) o[db] *= alpha_p;
           pending = false;
         }
         step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
-             IC<0>{}, sx, sy, pv, pu, carry, ct, cc, mm);
+             IC<0>{}, IC<0>{}, sx, sy, pv, pu, carry, ct, cc, mm, 0u, 0u);
       }
     };
     int it = 0;
@@ -547,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     } else {
       tile(IC<0>{}, IC<1>{}, it);
     }
-    // nothing may still be loading into registers when the workgroup ends
+    // nothing may still be loading into registers or LDS when the workgroup ends
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 

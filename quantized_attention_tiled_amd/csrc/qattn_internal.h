@@ -82,4 +82,38 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid, int total) {
 
 inline int grid_for_items(int total) { return ((total + 7) / 8) * 8; }
 
+// Raw buffer resource of the gfx9 family as four SGPRs: base address, no stride, `bytes` valid
+// bytes (reads past them return zeros), dword data format.
+typedef int rsrc4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  rsrc4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Byte address of a __shared__ location in the workgroup's LDS window.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Direct HBM -> LDS load (buffer_load_dwordx4 ... lds): lane l reads 16 bytes at buffer offset
+// voff + soff and writes them to LDS bytes lds + 16 l .. + 15; M0 holds lds. Written as inline
+// asm so that the compiler, which then does not see the LDS write, puts no wait for it in front
+// of later transposed LDS reads (it does so for the builtin form, which stalls a step on loads
+// meant to overlap it). Every reader of a loaded tile is ordered after the load by an explicit
+// vmcnt(0) wait and a workgroup barrier instead. M0 serves nothing else in these kernels; a build
+// test checks that every M0 write feeds one of these loads.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const rsrc4& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 }  // namespace qattn

@@ -88,3 +88,29 @@ def test_quant_kernels_use_no_scratch():
     assert ks
     for name, res in ks.items():
         assert res.get("ScratchSize", 0) == 0, (name, res)
+
+
+def _asm(src):
+    cmd = [B.hipcc(), f"--offload-arch={B.ARCH}", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+           f"-I{B.INCLUDE}", f"-I{B.CSRC}", *B.DEVICE_FLAGS, *B.SOURCE_FLAGS.get(src, []),
+           os.path.join(B.CSRC, src), "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return r.stdout
+
+
+@pytest.mark.parametrize("src", ["attn_bf16.hip", "attn_qbsa.hip"])
+def test_m0_only_feeds_direct_lds_loads(src):
+    """The direct HBM -> LDS loads set M0 in inline asm, where the compiler does not preserve it:
+    no other instruction of these kernels may read or write M0."""
+    lines = [ln.split(";")[0].strip() for ln in _asm(src).splitlines()]
+    lines = [ln for ln in lines if ln and not ln.startswith((".", "//"))]
+    uses = 0
+    for i, ln in enumerate(lines):
+        if not re.search(r"\bm0\b", ln):
+            continue
+        uses += 1
+        assert re.match(r"s_mov_b32 m0, s\d+$", ln), ln
+        nxt = [x for x in lines[i + 1:i + 4] if not x.startswith("s_nop")]
+        assert nxt and re.match(r"buffer_load_dwordx4 .* offen lds$", nxt[0]), (ln, lines[i + 1:i + 4])
+    assert uses > 0
