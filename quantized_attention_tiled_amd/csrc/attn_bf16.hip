@@ -8,10 +8,12 @@
 // layouts. The block-sparse variant is the BF16 BSA baseline of the EagleQBSA
 // article (128 x 128 blocks, masked blocks skipped).
 //
-// Work decomposition: one workgroup = 4 waves = one 128-row q-block of one (batch, head); each
-// wave owns 32 query rows. A workgroup needs 4 K/V tiles of LDS (64 KiB at D = 128) and at most
-// 256 VGPRs per lane, so two workgroups share a CU and every SIMD runs two independent waves
-// whose matrix and vector work interleave.
+// Work decomposition: 4 waves per 128-row q-block of one (batch, head); each wave owns 32 query
+// rows and needs at most 256 VGPRs per lane, so every SIMD runs two waves whose matrix and vector
+// work interleave. A workgroup holds 4 K/V tiles of LDS (64 KiB at D = 128). Causal and
+// block-sparse launches take one q-block per workgroup (two workgroups per CU); the other modes
+// take two consecutive q-blocks, eight waves sharing every K/V tile, which halves the tile loads
+// per query row.
 //   * Q^T, the B operand of S^T = K Q^T, stays in registers for the whole kernel;
 //   * K and V stream through LDS in 64-key tiles, each in a ring of two slots, straight from
 //     HBM with buffer_load ... lds (16 bytes per lane, no staging registers) into XOR-swizzled
@@ -46,8 +48,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(1))) const void gbl_cvoid;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWavesPerBlock = 4;  // waves per 128-row q-block (32 rows each)
 constexpr int kKT = 64;  // keys per LDS tile
 constexpr int kPF = 2;   // MFMA operands are read from LDS this many slots ahead
 constexpr float kNegInf = -__builtin_inff();
@@ -84,8 +85,9 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-// LDS tile geometry: 64 rows of D bf16 (D * 2 bytes), 16-byte chunks XOR-swizzled per row.
-template <int D>
+// LDS tile geometry: 64 rows of D bf16 (D * 2 bytes), 16-byte chunks XOR-swizzled per row, loaded
+// by kWaves waves.
+template <int D, int kWaves>
 struct Tile {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
@@ -98,9 +100,12 @@ struct Tile {
   __device__ static int vswz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
 };
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams p) {
-  using T = Tile<D>;
+// NQB q-blocks per workgroup share every K/V tile: 4 NQB waves, two waves per SIMD either way
+// (two workgroups per CU for NQB = 1, one for NQB = 2).
+template <int D, int MODE, int NQB>
+__global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_kernel(const FwdParams p) {
+  constexpr int kWaves = kWavesPerBlock * NQB;
+  using T = Tile<D, kWaves>;
   constexpr int DT = D / 16;    // score MFMAs per half tile (k-steps of 16)
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int NPV = 2 * DB;   // P V MFMAs per half tile (2 chunks of 16 keys x DB)
@@ -122,8 +127,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   const int item = xcd_remap(blockIdx.x, gridDim.x, p.total_items);
   if (item < 0) return;
 
-  // ---- which (batch, head, q-block) this workgroup owns ----
-  int b = 0, h, qblk = 0, Lq, Lkv;
+  // ---- which (batch, head) and q-blocks qblk .. qblk + nsub - 1 this workgroup owns ----
+  int b = 0, h, qblk = 0, nsub = NQB, Lq, Lkv;
   int64_t q_tok0 = 0, kv_tok0 = 0;
   if constexpr ((MODE & kVarlen) != 0) {
     h = p.h0 + item / p.total_tiles;
@@ -132,9 +137,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
     for (b = 0; b < p.nseq; b++) {
       const int nqb = (p.cu_q[b + 1] - p.cu_q[b] + kBlock - 1) / kBlock;
       const int lo = max(p.qb0, qbpre), hi = min(p.qb1, qbpre + nqb);
-      const int nt = max(0, hi - lo);
+      const int nt = (max(0, hi - lo) + NQB - 1) / NQB;
       if (t < tpre + nt) {
-        qblk = lo - qbpre + (t - tpre);
+        qblk = lo - qbpre + (t - tpre) * NQB;
+        nsub = min(NQB, hi - qbpre - qblk);
         break;
       }
       tpre += nt;
@@ -149,13 +155,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
     b = item / per_b;
     const int rem = item - b * per_b;
     h = p.h0 + rem / p.tiles_per_head;
-    qblk = p.qb0 + rem % p.tiles_per_head;
+    qblk = p.qb0 + (rem % p.tiles_per_head) * NQB;
+    nsub = min(NQB, p.qb1 - qblk);
     Lq = p.Sq;
     Lkv = p.Skv;
   }
   const int g = h / p.group;
   const int row_begin = qblk * kBlock;
-  const int row_end = min(row_begin + kBlock, Lq);
+  const int row_end = min(row_begin + nsub * kBlock, Lq);
 
   const uint16_t* qp = p.q + b * p.q_sb + h * p.q_sh + q_tok0 * p.q_ss;
   const uint16_t* kp = p.k + b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
@@ -587,7 +594,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
     if (pass == 0) overflow = __any(over);
     if (lane == 0) wave_flags[wave] = pass == 0 ? (int)overflow : 0;
     __syncthreads();
-    const bool again = pass == 0 && (wave_flags[0] | wave_flags[1] | wave_flags[2] | wave_flags[3]);
+    int any_flag = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) any_flag |= wave_flags[w];
+    const bool again = pass == 0 && any_flag != 0;
     __syncthreads();
     if (!again) break;
   }
@@ -617,32 +627,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const FwdParams 
   }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, int NQB>
 hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
+  if (p.qblocks_per_tile != NQB) return hipErrorInvalidValue;
   const int grid = grid_for_items(p.total_items);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, MODE>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, NQB>), dim3(grid), dim3(64 * kWavesPerBlock * NQB), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, int mode, hipStream_t stream) {
   switch (mode) {
-    case 0: return launch_t<D, 0>(p, stream);
-    case kCausal: return launch_t<D, kCausal>(p, stream);
-    case kMask: return launch_t<D, kMask>(p, stream);
-    case kCausal | kMask: return launch_t<D, kCausal | kMask>(p, stream);
-    case kSparse: return launch_t<D, kSparse>(p, stream);
-    case kVarlen: return launch_t<D, kVarlen>(p, stream);
-    case kVarlen | kCausal: return launch_t<D, kVarlen | kCausal>(p, stream);
+    case 0: return launch_t<D, 0, 2>(p, stream);
+    case kCausal: return launch_t<D, kCausal, 1>(p, stream);
+    case kMask: return launch_t<D, kMask, 2>(p, stream);
+    case kCausal | kMask: return launch_t<D, kCausal | kMask, 1>(p, stream);
+    case kSparse: return launch_t<D, kSparse, 1>(p, stream);
+    case kVarlen: return launch_t<D, kVarlen, 2>(p, stream);
+    case kVarlen | kCausal: return launch_t<D, kVarlen | kCausal, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-// one workgroup per 128-row q-block (the host sets qblocks_per_tile = 1)
+// q-blocks per workgroup by mode (the host sets qblocks_per_tile to match): two consecutive
+// q-blocks share the K/V tiles when both see the same keys (no causal mask, no kept list);
+// causal and block-sparse launches take one q-block each.
+int bf16_qblocks_per_tile(int mode) { return (mode & (kCausal | kSparse)) ? 1 : 2; }
+
+
 hipError_t launch_attn_bf16(const FwdParams& p, int mode, hipStream_t stream) {
-  if (p.qblocks_per_tile != 1) return hipErrorInvalidValue;
   if (p.D == 64) return launch_d<64>(p, mode, stream);
   if (p.D == 128) return launch_d<128>(p, mode, stream);
   return hipErrorInvalidValue;

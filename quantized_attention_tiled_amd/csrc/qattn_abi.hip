@@ -202,7 +202,7 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   if (desc->sparse_mode == 2 || desc->sparse_mode == 3) mode |= qattn::kCausal;
   if (desc->atten_mask) mode |= qattn::kMask;
   if (desc->layout == QATTN_LAYOUT_TND) mode |= qattn::kVarlen;
-  if ((rc = finish_items(p, 1))) return rc;
+  if ((rc = finish_items(p, qattn::bf16_qblocks_per_tile(mode)))) return rc;
   if (p.total_items == 0) return QATTN_OK;
   return hip_status(qattn::launch_attn_bf16(p, mode, (hipStream_t)stream), "attn_fwd launch");
 }

@@ -62,6 +62,7 @@ struct FwdParams {
 };
 
 hipError_t launch_attn_bf16(const FwdParams& p, int mode, hipStream_t stream);
+int bf16_qblocks_per_tile(int mode);  // q-blocks per workgroup the bf16 kernel takes in `mode`
 hipError_t launch_attn_qbsa(const FwdParams& p, hipStream_t stream);
 hipError_t launch_quant_qk(const uint16_t* x, int B, int N, int S, int D, int8_t* xq, float* scale,
                            hipStream_t stream);

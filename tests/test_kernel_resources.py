@@ -50,7 +50,7 @@ def bf16():
 def test_bf16_kernels_use_no_scratch(bf16):
     assert bf16, "no kernels reported"
     for name, res in bf16.items():
-        m = re.search(r"attn_bf16_kernelILi(\d+)ELi(\d+)EEE", name)
+        m = re.search(r"attn_bf16_kernelILi(\d+)ELi(\d+)ELi(\d+)EEE", name)
         assert m, name
         mode = int(m.group(2))
         if mode in MASK_MODES:
