@@ -200,6 +200,119 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def sustained_clock_power(step, step_ms, seconds=3.0, settle=1.0):
+    """GPU clock and socket power while the step runs back to back for about `seconds`, outside the
+    timed region: one thread keeps launching steps while this one reads `amd-smi metric -c -p`.
+    The tool's readings lag the load by up to a second, so samples before `settle` seconds are
+    dropped. Returns the kept samples (time, gfx clock averaged over the XCDs, socket power) and
+    their medians, or None when amd-smi is missing or prints something else."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    smi = shutil.which("amd-smi")
+    if smi is None:
+        return None
+    n = max(1, int(seconds * 1e3 / max(step_ms, 1e-3)))
+    busy = threading.Event()
+    busy.set()
+
+    def launcher():
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        busy.clear()
+
+    t = threading.Thread(target=launcher, daemon=True)
+    t0 = time.perf_counter()
+    t.start()
+    time.sleep(settle)
+    samples = []
+    while busy.is_set() and len(samples) < 12 and time.perf_counter() - t0 < 4 * seconds:
+        try:
+            r = subprocess.run([smi, "metric", "-c", "-p", "--json"], capture_output=True, text=True, timeout=15)
+            d = json.loads(r.stdout)
+            g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+            clks = [c["clk"]["value"] for key, c in g["clock"].items()
+                    if key.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)
+                    and isinstance(c["clk"].get("value"), (int, float))]
+            pw = g["power"]["socket_power"]["value"]
+        except Exception:  # noqa: BLE001 - a missing or changed tool only ends the sampling
+            break
+        if clks and isinstance(pw, (int, float)) and busy.is_set():
+            samples.append((round(time.perf_counter() - t0, 2), round(float(np.mean(clks))), float(pw)))
+    t.join(timeout=60)
+    if not samples:
+        return None
+    return {"sclk_mhz": round(float(np.median([c for _, c, _ in samples]))),
+            "socket_power_w": round(float(np.median([w for _, _, w in samples]))),
+            "samples_t_s_mhz_w": samples}
+
+
+def operator_sweep(seqs, sparsities=(0.0, 0.5, 0.9), reps=5):
+    """The single-operator sweep of the EagleQBSA article (section 4, Fig. 4.1) on this GPU: B=1,
+    N=40, D=128, for each S and block sparsity: bf16 dense attention, bf16 block-sparse attention
+    (BSA) and the quantised block-sparse kernel (QBSA; Q, K, V quantised beforehand, untimed).
+    QBSA with every block kept is the quantised dense case. Inputs are N(0,1) bf16 drawn on the GPU
+    from a fixed seed; a mask keeps the diagonal plus i.i.d. blocks with probability 1 - sparsity.
+    Prints one JSON line per case (median of `reps` launches), then the speed ratios."""
+    import torch
+    import quantized_attention_tiled_amd as qa
+    qa.load()
+    dev = torch.device("cuda:0")
+    B, N, D = 1, 40, 128
+    scale = 1.0 / float(np.sqrt(D))
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+    ratios = []
+    for S in seqs:
+        gen = torch.Generator(device=dev).manual_seed(7000 + S)
+        q, k, v = (torch.randn(B, N, S, D, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+        qq, qs = qa.quantize_qk_perblock_int8(q)
+        kq, ks = qa.quantize_qk_perblock_int8(k)
+        vq, vs = qa.quantize_v_perchannel_fp8(v)
+        o = torch.empty_like(q)
+        m = torch.empty((B, N, S), dtype=torch.float32, device=dev)
+        l = torch.empty_like(m)
+        QB = (S + 127) // 128
+        dense_flop = 4 * D * N * S * S
+        t_dense = timed(lambda: qa.attn_fwd(q, k, v, scale=scale, out=o, softmax_max=m, softmax_sum=l))
+        print(json.dumps({"sweep": "operator", "S": S, "sparsity": 0.0, "kernel": "bf16_dense", "ms": round(t_dense, 4),
+                          "executed_tflops": round(dense_flop / t_dense / 1e9, 1),
+                          "pct_peak": round(100 * dense_flop / t_dense / 1e9 / PEAK_BF16, 1)}), flush=True)
+        for sp in sparsities:
+            keep = (torch.rand(B, N, QB, QB, generator=gen, device=dev) >= sp).to(torch.uint8)
+            keep[:, :, torch.arange(QB), torch.arange(QB)] = 1
+            counts, idx = qa.build_kv_block_list(keep)
+            kept = float(keep.float().mean())
+            ex = 4 * D * 128 * 128 * int(keep.sum())
+            t_bsa = timed(lambda: qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=scale, out=o, softmax_max=m,
+                                                          softmax_sum=l))
+            t_q = timed(lambda: qa.attn_fwd_qbsa(qq, kq, vq, qs, ks, vs, counts, idx, scale=scale, out=o, softmax_max=m,
+                                                 softmax_sum=l))
+            for kern, t, peak in (("bf16_bsa", t_bsa, PEAK_BF16), ("qbsa", t_q, PEAK_FP8)):
+                print(json.dumps({"sweep": "operator", "S": S, "sparsity": sp, "kept_fraction": round(kept, 4),
+                                  "kernel": kern, "ms": round(t, 4), "executed_tflops": round(ex / t / 1e9, 1),
+                                  "dense_equiv_tflops": round(dense_flop / t / 1e9, 1),
+                                  "pct_peak": round(100 * ex / t / 1e9 / peak, 1)}), flush=True)
+            ratios.append({"S": S, "sparsity": sp, "dense_over_bsa": round(t_dense / t_bsa, 2),
+                           "dense_over_qbsa": round(t_dense / t_q, 2), "bsa_over_qbsa": round(t_bsa / t_q, 2)})
+        del q, k, v, qq, kq, vq, o
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "ratios", "rows": ratios}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +323,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=None)
+    ap.add_argument("--no-smi", action="store_true", help="skip the sustained clock / power sample")
+    ap.add_argument("--sweep", action="store_true", help="operator sweep (S x sparsity x kernel) instead of one line")
+    ap.add_argument("--sweep-seqs", default="8192,16384,32768,65536")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -222,6 +338,8 @@ def main(argv=None):
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)
         return 0
+    if a.sweep:
+        return operator_sweep([int(x) for x in a.sweep_seqs.split(",") if x])
 
     import quantized_attention_tiled_amd as qa
     from workloads import CONFIGS, make_workload
@@ -323,6 +441,7 @@ def main(argv=None):
     roof = {"bound": "mfma", "achieved": round(kvalue, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(kvalue / peak, 4), "traffic": traffic, "kernel": "attn_bf16_kernel" if kind != "qbsa"
             else "attn_qbsa_kernel", "flop_per_launch": ex, "launch_ms": round(kms, 4)}
+    sustained = None if a.no_smi else sustained_clock_power(step, ms)
     cpu = None
     if not a.no_cpu:
         log(f"cpu oracle baseline (~{a.cpu_seconds:.0f} s)")
@@ -346,7 +465,8 @@ def main(argv=None):
                    "pct_mfma_peak": round(100 * value / peak, 2), "median_ms": round(float(np.median(per)), 4),
                    "min_ms": round(float(per.min()), 4), "cv": round(float(per.std() / per.mean()), 4),
                    "algorithmic_bytes": alg_bytes, "algorithmic_gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
-                   "wall_s_timed": round(wall, 3), "kernel_source_sha": source_hash(kind)},
+                   "wall_s_timed": round(wall, 3), "kernel_source_sha": source_hash(kind),
+                   "sustained_clock_power": sustained},
     }
     print(json.dumps(line), flush=True)
     return 0

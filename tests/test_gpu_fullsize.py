@@ -45,6 +45,22 @@ def test_c2_dense_8k_full(qa):
         check_ml(to_np(m[0, h, rows]), to_np(l[0, h, rows]), rm, rl, what=f"c2 h{h}")
 
 
+def test_dense_64k_sampled(qa):
+    """Dense attention at the long end of the 8K-64K range the throughput target spans (S = 65536,
+    the C2 recipe with 8 heads: every work item is the one of the 40-head launch), sampled
+    q-blocks against the oracle."""
+    w = make_workload("c2_dense_8k", S=65536, N=8)
+    banner(f"dense 64k {w.q.shape}")
+    o, m, l = qa.attn_fwd(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    for h, qbs in ((0, [0, 511]), (5, [257])):
+        rows = _rows_of(qbs, w.Sq)
+        ro, rm, rl = oracle.attention_rows(f64(w.q[0, h]), f64(w.k[0, h]), f64(w.v[0, h]), w.scale, rows)
+        check_o(to_np(o[0, h, rows]), ro, O_TOL_BF16, f"dense64k h{h}")
+        check_ml(to_np(m[0, h, rows]), to_np(l[0, h, rows]), rm, rl, what=f"dense64k h{h}")
+
+
 def test_c3_varlen_full(qa):
     w = make_workload("c3_varlen_gqa_causal")
     banner(f"c3 full T={w.Sq} lens={np.diff(w.cu_seqlens_q).tolist()}")
