@@ -264,8 +264,12 @@ def operator_sweep(seqs, sparsities=(0.0, 0.5, 0.9), reps=5):
     scale = 1.0 / float(np.sqrt(D))
 
     def timed(fn):
-        for _ in range(2):
+        t0 = time.perf_counter()  # warm up for at least half a second (clocks ramp under load)
+        while True:
             fn()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 > 0.5:
+                break
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         ev[0].record()
         for i in range(reps):
