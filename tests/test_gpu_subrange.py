@@ -48,37 +48,42 @@ def _pieces(n_heads, n_qb):
     return splits
 
 
-@pytest.mark.parametrize("mode", [0, 2, 3])
-def test_dense_subranges(qa, mode):
+@pytest.mark.parametrize("mode,masked", [(0, False), (2, False), (3, False), (0, True), (3, True)])
+def test_dense_subranges(qa, mode, masked):
     B, Nq, Nkv, S, D = 1, 8, 4, 1100, 128
-    banner(f"subrange dense mode={mode}")
+    banner(f"subrange dense mode={mode} masked={masked}")
     q = dev_bf16(random_bf16(1, (B, Nq, S, D)))
     k = dev_bf16(random_bf16(2, (B, Nkv, S, D)))
     v = dev_bf16(random_bf16(3, (B, Nkv, S, D)))
-    full = qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode)
+    mask = None
+    if masked:  # B1SS boolean mask, about 20% of the keys masked
+        g = torch.Generator(device="cuda").manual_seed(5)
+        mask = (torch.rand((B, 1, S, S), generator=g, device="cuda") < 0.2).to(torch.uint8)
+    full = qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, atten_mask=mask)
     nqb = (S + 127) // 128
     for split in _pieces(Nq, nqb):
         out = (torch.zeros_like(full[0]), torch.zeros_like(full[1]), torch.zeros_like(full[2]))
         for hr, br in split:
-            qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, head_range=hr, qblock_range=br, out=out[0],
-                        softmax_max=out[1], softmax_sum=out[2])
+            qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, atten_mask=mask, head_range=hr, qblock_range=br,
+                        out=out[0], softmax_max=out[1], softmax_sum=out[2])
         torch.cuda.synchronize()
         _same(full, out)
 
 
-def test_tnd_subranges(qa):
+@pytest.mark.parametrize("mode", [0, 3])
+def test_tnd_subranges(qa, mode):
     lens = [300, 5, 700, 128]
     cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
     T, Nq, Nkv, D = cu[-1], 4, 2, 128
     q = dev_bf16(random_bf16(11, (T, Nq, D)))
     k = dev_bf16(random_bf16(12, (T, Nkv, D)))
     v = dev_bf16(random_bf16(13, (T, Nkv, D)))
-    full = qa.attn_fwd(q, k, v, scale=0.1, layout="TND", sparse_mode=3, cu_seqlens_q=cu)
+    full = qa.attn_fwd(q, k, v, scale=0.1, layout="TND", sparse_mode=mode, cu_seqlens_q=cu)
     nqb = sum((x + 127) // 128 for x in lens)
     for split in _pieces(Nq, nqb):
         out = (torch.zeros_like(full[0]), torch.zeros_like(full[1]), torch.zeros_like(full[2]))
         for hr, br in split:
-            qa.attn_fwd(q, k, v, scale=0.1, layout="TND", sparse_mode=3, cu_seqlens_q=cu, head_range=hr,
+            qa.attn_fwd(q, k, v, scale=0.1, layout="TND", sparse_mode=mode, cu_seqlens_q=cu, head_range=hr,
                         qblock_range=br, out=out[0], softmax_max=out[1], softmax_sum=out[2])
         torch.cuda.synchronize()
         _same(full, out)
@@ -111,16 +116,19 @@ def test_blocksparse_and_qbsa_subranges(qa):
         _same(fullq, outq)
 
 
-def test_subrange_leaves_rest_untouched(qa):
+@pytest.mark.parametrize("mode,qbr", [(0, (1, 3)), (0, (1, 2)), (0, (3, 4)), (3, (1, 2))])
+def test_subrange_leaves_rest_untouched(qa, mode, qbr):
+    """Only the slice's rows are written, also when a workgroup's second q-block lies outside it."""
     B, Nq, S, D = 1, 2, 512, 64
     q = dev_bf16(random_bf16(31, (B, Nq, S, D)))
     sentinel = torch.full((B, Nq, S, D), 7.0, dtype=torch.bfloat16, device="cuda")
     m = torch.full((B, Nq, S), 7.0, device="cuda")
     l = torch.full((B, Nq, S), 7.0, device="cuda")
-    qa.attn_fwd(q, q, q, scale=0.1, head_range=(1, 2), qblock_range=(1, 3), out=sentinel, softmax_max=m,
-                softmax_sum=l)
+    qa.attn_fwd(q, q, q, scale=0.1, sparse_mode=mode, head_range=(1, 2), qblock_range=qbr, out=sentinel,
+                softmax_max=m, softmax_sum=l)
     torch.cuda.synchronize()
     touched = torch.zeros((B, Nq, S), dtype=torch.bool, device="cuda")
-    touched[:, 1, 128:384] = True
+    touched[:, 1, 128 * qbr[0]:128 * qbr[1]] = True
     assert torch.all(sentinel[~touched] == 7.0) and torch.all(m[~touched] == 7.0) and torch.all(l[~touched] == 7.0)
+    assert not torch.any(sentinel[touched] == 7.0)
     assert not torch.any(sentinel[touched] == 7.0)
