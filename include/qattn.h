@@ -5,7 +5,7 @@
  *   "Ascend NPU fused attention operator" guide (npu_fusion_attention),
  *     section 2: O = Softmax(Mask(Q K^T * scale)) V, computed tile by tile with
  *     an online softmax so the S x S score matrix is never stored;
- *     section 3/4: head_num, input_layout (BNSD, TND), atten_mask with
+ *     section 3/4: head_num, input_layout (BNSD, BSND, BSH, SBH, TND), atten_mask with
  *     1 = masked and shapes SS / B1SS / BNSS, scale, sparse_mode 2/3 causal,
  *     cumulative sequence lengths for varlen;
  *     section 5: outputs are the attention result plus softmax_max and
@@ -43,6 +43,12 @@
  * Layouts
  *   BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D], o like q;
  *         softmax_max / softmax_sum fp32 [B, Nq, Sq].
+ *   BSND: q [B, Sq, Nq, D], k/v [B, Skv, Nkv, D], o like q. BSH, [B, S, N * D],
+ *         is the same memory.
+ *   SBH:  q [Sq, B, Nq * D], k/v [Skv, B, Nkv * D], o like q.
+ *         BSND and SBH take softmax_max / softmax_sum fp32 [B, Nq, Sq], as BNSD.
+ *         Their rows are strided: the key stride in bytes times Skv must stay
+ *         below 2^31 (a larger K or V returns QATTN_UNSUPPORTED).
  *   TND:  q [T, Nq, D], k/v [Tk, Nkv, D], o like q, with B sequences given
  *         by host cumulative lengths (B + 1 entries, leading 0, non-
  *         decreasing, last entry = T or Tk);
@@ -80,6 +86,8 @@ extern "C" {
 
 #define QATTN_LAYOUT_BNSD 0
 #define QATTN_LAYOUT_TND 1
+#define QATTN_LAYOUT_BSND 2 /* also BSH */
+#define QATTN_LAYOUT_SBH 3
 
 #define QATTN_MASK_SS 0   /* atten_mask [Sq, Skv] shared by all batches and heads */
 #define QATTN_MASK_B1SS 1 /* atten_mask [B, 1, Sq, Skv] shared by heads */
@@ -92,18 +100,18 @@ typedef uint16_t qattn_bf16; /* bfloat16 storage */
 /* Problem description shared by the three attention entry points. */
 typedef struct qattn_desc {
   uint32_t struct_size;  /* sizeof(qattn_desc); checked for versioning */
-  int32_t layout;        /* QATTN_LAYOUT_BNSD or QATTN_LAYOUT_TND */
-  int32_t B;             /* batch (BNSD) or number of sequences (TND) */
+  int32_t layout;        /* QATTN_LAYOUT_BNSD, _TND, _BSND (or BSH) or _SBH */
+  int32_t B;             /* batch, or number of sequences (TND) */
   int32_t Nq;            /* query heads (head_num) */
   int32_t Nkv;           /* key/value heads; Nq % Nkv == 0 */
-  int32_t Sq;            /* BNSD: query length; TND: total query tokens T */
-  int32_t Skv;           /* BNSD: key length; TND: total key tokens Tk */
+  int32_t Sq;            /* query length; TND: total query tokens T */
+  int32_t Skv;           /* key length; TND: total key tokens Tk */
   int32_t D;             /* head dimension: 64 or 128 */
   float scale;           /* softmax scale, finite and > 0 */
   int32_t sparse_mode;   /* 0: none / explicit mask; 2: causal top-left; 3: causal bottom-right */
   const int32_t* cu_seqlens_q;  /* TND: host [B + 1] cumulative query lengths; else NULL */
   const int32_t* cu_seqlens_kv; /* TND: host [B + 1] cumulative key lengths; else NULL */
-  const uint8_t* atten_mask;    /* BNSD only: device uint8, 1 = masked, 0 = kept; NULL = none */
+  const uint8_t* atten_mask;    /* not TND: device uint8, 1 = masked, 0 = kept; NULL = none */
   int32_t mask_kind;            /* QATTN_MASK_SS / _B1SS / _BNSS when atten_mask != NULL */
   int32_t head_begin;           /* subrange of q-heads [head_begin, head_end); -1, -1 = all */
   int32_t head_end;
@@ -117,7 +125,7 @@ typedef struct qattn_desc {
  *   q, k, v: bf16 in desc->layout; o: bf16, same shape as q.
  *   softmax_max, softmax_sum: fp32 outputs (layouts above), each nullable.
  *   Causal modes and an explicit atten_mask may be combined (a pair is kept
- *   only when both keep it). atten_mask requires the BNSD layout.
+ *   only when both keep it). atten_mask is not available with TND.
  *   Only rows of the requested head and q-block subrange are written.
  */
 int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
@@ -140,7 +148,8 @@ int build_kv_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32
  * BF16 BSA baseline; 128 x 128 blocks): each (batch, q-head, q-block) attends
  * only to the keys of its kept kv-blocks, visited in list order; masked
  * blocks are skipped, never computed.
- *   desc: BNSD, sparse_mode 0, atten_mask NULL (else QATTN_UNSUPPORTED).
+ *   desc: BNSD, BSND/BSH or SBH (not TND), sparse_mode 0, atten_mask NULL
+ *   (else QATTN_UNSUPPORTED).
  *   counts/idx: as produced by build_kv_block_list for [B, Nq, QB, KB].
  */
 int attn_fwd_blocksparse(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k,
@@ -177,7 +186,7 @@ int quantize_v_perchannel_fp8(const qattn_bf16* v, int B, int N, int S, int D, u
  * with INT8 MFMA; online softmax in fp32; p cast to FP8 E4M3 (unscaled,
  * round half even); acc += p8 . v_q with FP8 MFMA; O = acc * v_scale[d] / l,
  * where l sums the unrounded p. Output bf16.
- *   desc: BNSD, sparse_mode 0, atten_mask NULL.
+ *   desc: BNSD (other layouts: QATTN_UNSUPPORTED), sparse_mode 0, atten_mask NULL.
  *   q: int8 [B, Nq, Sq, D]; k: int8 [B, Nkv, Skv, D]; v: E4M3FN [B, Nkv, Skv, D];
  *   q_scale: fp32 [B, Nq, QB]; k_scale: fp32 [B, Nkv, KB]; v_scale: fp32 [B, Nkv, D].
  *   counts/idx: kept list [B, Nq, QB, KB]. softmax_max/sum nullable (the

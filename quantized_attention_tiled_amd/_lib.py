@@ -20,6 +20,8 @@ QATTN_HIP_ERROR = 4
 
 LAYOUT_BNSD = 0
 LAYOUT_TND = 1
+LAYOUT_BSND = 2  # also BSH
+LAYOUT_SBH = 3
 MASK_SS, MASK_B1SS, MASK_BNSS = 0, 1, 2
 MAX_SEQS = 256
 

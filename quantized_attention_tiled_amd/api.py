@@ -14,7 +14,8 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import LAYOUT_BNSD, LAYOUT_TND, MASK_B1SS, MASK_BNSS, MASK_SS, QattnDesc, check, load
+from ._lib import (LAYOUT_BNSD, LAYOUT_BSND, LAYOUT_SBH, LAYOUT_TND, MASK_B1SS, MASK_BNSS, MASK_SS, QattnDesc,
+                   check, load)
 
 BLOCK = 128
 
@@ -71,6 +72,36 @@ def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: i
     return d
 
 
+def _dims(layout: str, q: torch.Tensor, k: torch.Tensor, head_num: Optional[int]):
+    """(layout code, B, Nq, Sq, Nkv, Skv, D) of the batched layouts: BNSD and BSND are 4-D, BSH and
+    SBH 3-D with H = head_num * D (head_num counts the query heads; the kv heads follow from k)."""
+    if layout in ("BNSD", "BSND"):
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError(f"{layout} tensors must be 4-D")
+        if layout == "BNSD":
+            (B, Nq, Sq, D), (Bk, Nkv, Skv, Dk), code = q.shape, k.shape, LAYOUT_BNSD
+        else:
+            (B, Sq, Nq, D), (Bk, Skv, Nkv, Dk), code = q.shape, k.shape, LAYOUT_BSND
+    elif layout in ("BSH", "SBH"):
+        if q.dim() != 3 or k.dim() != 3:
+            raise ValueError(f"{layout} tensors must be 3-D")
+        if head_num is None or head_num < 1 or q.shape[2] % head_num:
+            raise ValueError(f"{layout} needs head_num dividing H = {q.shape[2]}")
+        Nq, D = int(head_num), q.shape[2] // int(head_num)
+        if k.shape[2] % D:
+            raise ValueError(f"k's H = {k.shape[2]} is not a multiple of D = {D}")
+        Nkv, Dk = k.shape[2] // D, D
+        if layout == "BSH":
+            (B, Sq), (Bk, Skv), code = q.shape[:2], k.shape[:2], LAYOUT_BSND
+        else:
+            (Sq, B), (Skv, Bk), code = q.shape[:2], k.shape[:2], LAYOUT_SBH
+    else:
+        raise ValueError("layout must be 'BNSD', 'BSND', 'BSH', 'SBH' or 'TND'")
+    if Bk != B or Dk != D:
+        raise ValueError(f"k/v do not match q in {layout}")
+    return code, B, Nq, Sq, Nkv, Skv, D
+
+
 def _mask_kind(mask: torch.Tensor, B: int, Nq: int, Sq: int, Skv: int) -> int:
     if mask.dim() == 2 and tuple(mask.shape) == (Sq, Skv):
         return MASK_SS
@@ -96,12 +127,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
              cu_seqlens_q: Optional[Sequence[int]] = None, cu_seqlens_kv: Optional[Sequence[int]] = None,
              head_range: Optional[Tuple[int, int]] = None, qblock_range: Optional[Tuple[int, int]] = None,
              out: Optional[torch.Tensor] = None, softmax_max: Optional[torch.Tensor] = None,
-             softmax_sum: Optional[torch.Tensor] = None):
+             softmax_sum: Optional[torch.Tensor] = None, head_num: Optional[int] = None):
     """Dense bf16 attention forward; returns (out, softmax_max, softmax_sum).
 
-    BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D]; m/l [B, Nq, Sq].
+    BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D]; BSND: q [B, Sq, Nq, D], k/v [B, Skv, Nkv, D];
+    BSH: q [B, Sq, Nq * D], SBH: q [Sq, B, Nq * D] (k/v alike, with head_num = Nq); m/l [B, Nq, Sq].
     TND:  q [T, Nq, D], k/v [Tk, Nkv, D] plus cumulative lengths; m/l [Nq, T].
-    ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (BNSD only).
+    ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (not with TND).
     With a head or q-block range only that slice of the outputs is written.
     """
     lib = load()
@@ -110,13 +142,10 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
         _require(t, n, torch.bfloat16, dev)
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
-    if layout == "BNSD":
-        B, Nq, Sq, D = q.shape
-        Nkv, Skv = k.shape[1], k.shape[2]
-        if k.shape[0] != B or k.shape[3] != D:
-            raise ValueError("k/v must be [B, Nkv, Skv, D] matching q")
-        lay, cu_q, cu_kv, ml_shape = LAYOUT_BNSD, None, None, (B, Nq, Sq)
-    elif layout == "TND":
+    if layout != "TND":
+        lay, B, Nq, Sq, Nkv, Skv, D = _dims(layout, q, k, head_num)
+        cu_q, cu_kv, ml_shape = None, None, (B, Nq, Sq)
+    else:
         Sq, Nq, D = q.shape
         Skv, Nkv = k.shape[0], k.shape[1]
         if k.shape[2] != D:
@@ -128,15 +157,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
             raise ValueError("cu_seqlens_q and cu_seqlens_kv differ in length")
         B = len(cu_q) - 1
         lay, ml_shape = LAYOUT_TND, (Nq, Sq)
-    else:
-        raise ValueError("layout must be 'BNSD' or 'TND'")
     kind = MASK_SS
     if atten_mask is not None:
         if atten_mask.dtype == torch.bool:
             atten_mask = atten_mask.view(torch.uint8)
         _require(atten_mask, "atten_mask", torch.uint8, dev)
-        if layout != "BNSD":
-            raise ValueError("atten_mask needs the BNSD layout")
+        if layout == "TND":
+            raise ValueError("atten_mask is not available with TND")
         kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)
     out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, ml_shape)
     for t, n, dt in ((out, "out", torch.bfloat16), (softmax_max, "softmax_max", torch.float32),
@@ -175,21 +202,22 @@ def build_kv_block_list(keep: torch.Tensor, counts: Optional[torch.Tensor] = Non
 
 
 def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range=None, qblock_range=None,
-                         out=None, softmax_max=None, softmax_sum=None):
-    """bf16 block-sparse attention over a kept-block list (BNSD); returns (out, m, l)."""
+                         out=None, softmax_max=None, softmax_sum=None, layout: str = "BNSD",
+                         head_num: Optional[int] = None):
+    """bf16 block-sparse attention over a kept-block list (BNSD, BSND, BSH or SBH, shapes as for
+    attn_fwd); returns (out, m [B, Nq, Sq], l)."""
     lib = load()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, torch.bfloat16, dev)
     _require(counts, "counts", torch.int32, dev)
     _require(idx, "idx", torch.int32, dev)
-    B, Nq, Sq, D = q.shape
-    Nkv, Skv = k.shape[1], k.shape[2]
+    lay, B, Nq, Sq, Nkv, Skv, D = _dims(layout, q, k, head_num)
     QB, KB = (Sq + BLOCK - 1) // BLOCK, (Skv + BLOCK - 1) // BLOCK
     if tuple(counts.shape) != (B, Nq, QB) or tuple(idx.shape) != (B, Nq, QB, KB):
         raise ValueError("counts/idx must be [B, Nq, QB] and [B, Nq, QB, KB]")
     out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, (B, Nq, Sq))
-    desc = make_desc(layout=LAYOUT_BNSD, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
+    desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
                      head_range=head_range, qblock_range=qblock_range)
     with torch.cuda.device(dev):
         check(lib.attn_fwd_blocksparse(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max),

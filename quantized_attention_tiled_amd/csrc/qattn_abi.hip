@@ -28,8 +28,8 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   if (!d) return fail(QATTN_INVALID_ARGUMENT, "desc is NULL");
   if (d->struct_size != sizeof(qattn_desc))
     return fail(QATTN_INVALID_ARGUMENT, "desc->struct_size %u != %zu", d->struct_size, sizeof(qattn_desc));
-  if (d->layout != QATTN_LAYOUT_BNSD && d->layout != QATTN_LAYOUT_TND)
-    return fail(QATTN_INVALID_ARGUMENT, "layout %d is not BNSD (0) or TND (1)", d->layout);
+  if (d->layout < QATTN_LAYOUT_BNSD || d->layout > QATTN_LAYOUT_SBH)
+    return fail(QATTN_INVALID_ARGUMENT, "layout %d is not BNSD (0), TND (1), BSND (2) or SBH (3)", d->layout);
   if (d->layout == QATTN_LAYOUT_TND && !allow_tnd) return fail(QATTN_UNSUPPORTED, "this entry point needs BNSD");
   if (d->B < 1 || d->Nq < 1 || d->Nkv < 1 || d->Sq < 0 || d->Skv < 0)
     return fail(QATTN_INVALID_ARGUMENT, "bad sizes B=%d Nq=%d Nkv=%d Sq=%d Skv=%d", d->B, d->Nq, d->Nkv, d->Sq, d->Skv);
@@ -41,7 +41,7 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   if (!allow_masks && (d->sparse_mode != 0 || d->atten_mask != nullptr))
     return fail(QATTN_UNSUPPORTED, "block-sparse entry points take no causal mode and no atten_mask");
   if (d->atten_mask != nullptr) {
-    if (d->layout != QATTN_LAYOUT_BNSD) return fail(QATTN_UNSUPPORTED, "atten_mask needs the BNSD layout");
+    if (d->layout == QATTN_LAYOUT_TND) return fail(QATTN_UNSUPPORTED, "atten_mask is not available with TND");
     if (d->mask_kind < QATTN_MASK_SS || d->mask_kind > QATTN_MASK_BNSS)
       return fail(QATTN_INVALID_ARGUMENT, "mask_kind %d", d->mask_kind);
   }
@@ -57,13 +57,30 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   p.c = (float)((double)d->scale * 1.4426950408889634);
   p.causal = d->sparse_mode;
   int qblocks;
-  if (d->layout == QATTN_LAYOUT_BNSD) {
-    p.q_sb = (int64_t)d->Nq * d->Sq * D;
-    p.q_sh = (int64_t)d->Sq * D;
-    p.q_ss = D;
-    p.k_sb = (int64_t)d->Nkv * d->Skv * D;
-    p.k_sh = (int64_t)d->Skv * D;
-    p.k_ss = D;
+  if (d->layout != QATTN_LAYOUT_TND) {
+    // element strides of batch, head and token (the head dimension is contiguous)
+    if (d->layout == QATTN_LAYOUT_BNSD) {
+      p.q_sb = (int64_t)d->Nq * d->Sq * D;
+      p.q_sh = (int64_t)d->Sq * D;
+      p.q_ss = D;
+      p.k_sb = (int64_t)d->Nkv * d->Skv * D;
+      p.k_sh = (int64_t)d->Skv * D;
+      p.k_ss = D;
+    } else if (d->layout == QATTN_LAYOUT_BSND) {
+      p.q_sb = (int64_t)d->Sq * d->Nq * D;
+      p.q_sh = D;
+      p.q_ss = (int64_t)d->Nq * D;
+      p.k_sb = (int64_t)d->Skv * d->Nkv * D;
+      p.k_sh = D;
+      p.k_ss = (int64_t)d->Nkv * D;
+    } else {  // SBH
+      p.q_sb = (int64_t)d->Nq * D;
+      p.q_sh = D;
+      p.q_ss = (int64_t)d->B * d->Nq * D;
+      p.k_sb = (int64_t)d->Nkv * D;
+      p.k_sh = D;
+      p.k_ss = (int64_t)d->B * d->Nkv * D;
+    }
     p.ml_sb = (int64_t)d->Nq * d->Sq;
     p.ml_sh = d->Sq;
     p.ml_ss = 1;
@@ -108,6 +125,10 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
     p.ml_ss = 1;
     p.QB = p.KB = 0;
   }
+  // The kernels address the K and V rows of one (batch, kv-head) through 32-bit byte offsets.
+  if (((int64_t)std::max(d->Skv, 1) - 1) * p.k_ss * 2 + 2 * D > (int64_t)INT32_MAX)
+    return fail(QATTN_UNSUPPORTED, "K/V rows of one head span more than 2^31 bytes (Skv=%d, key stride %lld)", d->Skv,
+                (long long)p.k_ss);
   // subrange
   int h0 = d->head_begin, h1 = d->head_end, b0 = d->qblock_begin, b1 = d->qblock_end;
   if (h0 == -1 && h1 == -1) {
@@ -283,6 +304,7 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
   int total_qb = 0;
   int rc = setup_common(desc, p, false, false, &total_qb);
   if (rc) return rc;
+  if (desc->layout != QATTN_LAYOUT_BNSD) return fail(QATTN_UNSUPPORTED, "attn_fwd_qbsa needs the BNSD layout");
   const void* ptrs[] = {q, k, v, o};
   const char* names[] = {"q", "k", "v", "o"};
   if ((rc = check_ptrs(ptrs, names, 4))) return rc;

@@ -81,7 +81,9 @@ def _fwd(q, d, qp=FAKE, kp=FAKE, vp=FAKE, op=FAKE, m=0, l=0):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(D=96), 2), (dict(D=0), 2), (dict(Nq=3, Nkv=2), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
-    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(sparse_mode=1), 1), (dict(layout=2), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(sparse_mode=1), 1), (dict(layout=4), 1),
+    (dict(layout=-1), 1), (dict(layout=3, B=64, Nq=64, Nkv=64, Skv=1 << 17, Sq=128), 2),
+    (dict(layout=2, Nq=64, Nkv=64, Skv=1 << 20, Sq=128), 2),
     (dict(B=0), 1), (dict(Sq=-1), 1), (dict(Nkv=0), 1), (dict(head_begin=0, head_end=5), 1),
     (dict(head_begin=3, head_end=2), 1), (dict(qblock_begin=0, qblock_end=3), 1), (dict(qblock_begin=-2, qblock_end=1), 1),
 ])
@@ -146,6 +148,9 @@ def test_blocksparse_and_qbsa_validation(q):
     assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None) == 1
     assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, layout=1)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                              None, None, None) == 2
+    for lay in (2, 3):  # BSND and SBH are bf16-only layouts
+        assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, layout=lay)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, None, None, None) == 2
     assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                              None, None, None) == 1
     assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, FAKE + 1, FAKE, FAKE, FAKE, FAKE, FAKE,

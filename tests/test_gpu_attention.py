@@ -171,3 +171,75 @@ def test_deterministic(qa):
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x.view(torch.int32),
                            y.view(torch.uint8) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+
+
+# ---- the other batched layouts of the fused attention guide (section 4.1): BSND, BSH, SBH ----
+
+def _to_layout(x, layout):
+    """BNSD [B, N, S, D] device tensor -> the same values in `layout`."""
+    B, N, S, D = x.shape
+    if layout == "BSND":
+        return x.permute(0, 2, 1, 3).contiguous()
+    if layout == "BSH":
+        return x.permute(0, 2, 1, 3).reshape(B, S, N * D).contiguous()
+    return x.permute(2, 0, 1, 3).reshape(S, B, N * D).contiguous()  # SBH
+
+
+def _from_layout(x, layout, B, N, S, D):
+    if layout == "BSND":
+        return x.permute(0, 2, 1, 3)
+    if layout == "BSH":
+        return x.reshape(B, S, N, D).permute(0, 2, 1, 3)
+    return x.reshape(S, B, N, D).permute(1, 2, 0, 3)
+
+
+def _bits(x):
+    return x.contiguous().view(torch.int16) if x.dtype == torch.bfloat16 else x.contiguous().view(torch.int32)
+
+
+@pytest.mark.parametrize("layout", ["BSND", "BSH", "SBH"])
+@pytest.mark.parametrize("mode,masked,D", [(0, False, 128), (3, False, 128), (0, True, 64), (2, False, 64)])
+def test_layouts_match_bnsd(qa, layout, mode, masked, D):
+    """A row's arithmetic does not depend on the strides, so every layout reproduces the BNSD call
+    bit for bit (O, softmax_max, softmax_sum)."""
+    B, Nq, Nkv, S = 2, 4, 2, 300
+    banner(f"layout {layout} mode={mode} masked={masked} D={D}")
+    q, k, v = (dev_bf16(x) for x in _bnsd(500 + D + mode, B, Nq, Nkv, S, S, D))
+    mask = None
+    if masked:
+        g = torch.Generator(device="cuda").manual_seed(9)
+        mask = (torch.rand((B, 1, S, S), generator=g, device="cuda") < 0.25).to(torch.uint8)
+    ref = qa.attn_fwd(q, k, v, scale=0.125, sparse_mode=mode, atten_mask=mask)
+    hn = Nq if layout in ("BSH", "SBH") else None
+    out = qa.attn_fwd(_to_layout(q, layout), _to_layout(k, layout), _to_layout(v, layout), scale=0.125,
+                      sparse_mode=mode, atten_mask=mask, layout=layout, head_num=hn)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(_from_layout(out[0], layout, B, Nq, S, D)), _bits(ref[0]))
+    assert torch.equal(_bits(out[1]), _bits(ref[1])) and torch.equal(_bits(out[2]), _bits(ref[2]))
+
+
+def test_bsnd_against_oracle(qa):
+    B, Nq, Nkv, S, D = 1, 4, 2, 400, 128
+    q, k, v = _bnsd(601, B, Nq, Nkv, S, S, D)
+    o, m, l = qa.attn_fwd(_to_layout(dev_bf16(q), "BSND"), _to_layout(dev_bf16(k), "BSND"),
+                          _to_layout(dev_bf16(v), "BSND"), scale=0.09, sparse_mode=3, layout="BSND")
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), 0.09, sparse_mode=3)
+    check_o(to_np(_from_layout(o, "BSND", B, Nq, S, D).contiguous()), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+
+
+@pytest.mark.parametrize("layout", ["BSND", "SBH"])
+def test_blocksparse_layouts_match_bnsd(qa, layout):
+    B, Nq, Nkv, S, D = 1, 4, 2, 640, 128
+    q, k, v = (dev_bf16(x) for x in _bnsd(700, B, Nq, Nkv, S, S, D))
+    nb = (S + 127) // 128
+    keep = torch.from_numpy(make_block_keep(701, B, Nq, nb, nb, 0.4)).cuda()
+    counts, idx = qa.build_kv_block_list(keep)
+    ref = qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=0.1)
+    hn = Nq if layout == "SBH" else None
+    out = qa.attn_fwd_blocksparse(_to_layout(q, layout), _to_layout(k, layout), _to_layout(v, layout), counts, idx,
+                                  scale=0.1, layout=layout, head_num=hn)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(_from_layout(out[0], layout, B, Nq, S, D)), _bits(ref[0]))
+    assert torch.equal(_bits(out[1]), _bits(ref[1])) and torch.equal(_bits(out[2]), _bits(ref[2]))
