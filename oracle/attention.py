@@ -7,14 +7,19 @@ Definition followed ("Ascend NPU fused attention operator" guide):
     mask, softmax over keys, multiply by V. This module is exactly those steps.
   * section 4.2: ``atten_mask`` uses 1 = masked, 0 = kept, shapes SS / B1SS / BNSS.
   * section 4.3: ``sparse_mode`` 2 and 3 are causal lower triangles anchored at
-    the top-left and bottom-right corners; varlen sequences are described by
-    cumulative lengths (TND layout, section 4.1).
+    the top-left and bottom-right corners; ``sparse_mode`` 0 takes its range from
+    ``pre_tokens`` and ``next_tokens`` (section 3's prototype defaults both to
+    2147483647, i.e. no limit); varlen sequences are described by cumulative
+    lengths (TND layout, section 4.1).
   * section 5: outputs are the attention result plus the softmax max and sum.
   * section 7: GQA requires Nq / Nkv to be an integer.
 
 Readings where the guide is silent (each stated once here):
   * causal top-left keeps j <= i, bottom-right keeps j <= i + Skv - Sq, with i
     and j counted inside one sequence;
+  * the sparse_mode 0 range keeps i - pre_tokens <= j <= i + next_tokens (a
+    band around the top-left diagonal; pre/next None means no limit), also
+    counted inside one sequence; the band is not combined with modes 2 and 3;
   * softmax_max m is the row maximum of the scaled, masked scores (natural-log
     domain) and softmax_sum l = sum_j exp(s_ij - m); a row with no unmasked key
     has O = 0, m = -inf, l = 0;
@@ -54,10 +59,11 @@ def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def _allowed(rows: np.ndarray, Sq: int, Skv: int, sparse_mode: int,
-             mask_rows: Optional[np.ndarray], keep: Optional[np.ndarray]) -> np.ndarray:
+             mask_rows: Optional[np.ndarray], keep: Optional[np.ndarray],
+             pre_tokens: Optional[int] = None, next_tokens: Optional[int] = None) -> np.ndarray:
     """Which (row, key) pairs survive the mask, for query rows ``rows`` of one sequence."""
-    j = np.arange(Skv)[None, :]
-    i = rows[:, None]
+    j = np.arange(Skv, dtype=np.int64)[None, :]
+    i = rows.astype(np.int64)[:, None]
     a = np.ones((len(rows), Skv), dtype=bool)
     if sparse_mode == 2:
         a &= j <= i
@@ -65,6 +71,13 @@ def _allowed(rows: np.ndarray, Sq: int, Skv: int, sparse_mode: int,
         a &= j <= i + (Skv - Sq)
     elif sparse_mode != 0:
         raise ValueError("sparse_mode must be 0, 2 or 3")
+    if pre_tokens is not None or next_tokens is not None:
+        if sparse_mode != 0:
+            raise ValueError("pre_tokens / next_tokens set the sparse_mode 0 range")
+        if pre_tokens is not None:
+            a &= j >= i - int(pre_tokens)
+        if next_tokens is not None:
+            a &= j <= i + int(next_tokens)
     if mask_rows is not None:
         a &= (mask_rows == 0)
     if keep is not None:
@@ -85,7 +98,8 @@ def _mask_for_head(atten_mask: Optional[np.ndarray], b: int, h: int) -> Optional
 
 def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, rows: Sequence[int],
                    *, sparse_mode: int = 0, mask: Optional[np.ndarray] = None,
-                   keep: Optional[np.ndarray] = None):
+                   keep: Optional[np.ndarray] = None, pre_tokens: Optional[int] = None,
+                   next_tokens: Optional[int] = None):
     """Attention for selected query rows of one head of one sequence.
 
     q [Sq, D], k [Skv, D], v [Skv, Dv]; ``mask`` [Sq, Skv] (1 = masked);
@@ -93,11 +107,11 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, ro
     """
     rows = np.asarray(rows, dtype=np.int64)
     Sq, Skv = q.shape[0], k.shape[0]
-    a = _allowed(rows, Sq, Skv, sparse_mode, None if mask is None else mask[rows], keep)
+    a = _allowed(rows, Sq, Skv, sparse_mode, None if mask is None else mask[rows], keep, pre_tokens, next_tokens)
     return softmax_attention(q[rows], k, v, scale, a)
 
 
-def _head(q, k, v, scale, sparse_mode, mask, keep):
+def _head(q, k, v, scale, sparse_mode, mask, keep, band=(None, None)):
     Sq = q.shape[0]
     o = np.zeros((Sq, v.shape[1]))
     m = np.zeros(Sq)
@@ -105,14 +119,16 @@ def _head(q, k, v, scale, sparse_mode, mask, keep):
     for r0 in range(0, Sq, BLOCK):
         rows = np.arange(r0, min(Sq, r0 + BLOCK))
         o[rows], m[rows], l[rows] = attention_rows(q, k, v, scale, rows, sparse_mode=sparse_mode,
-                                                   mask=mask, keep=keep)
+                                                   mask=mask, keep=keep, pre_tokens=band[0],
+                                                   next_tokens=band[1])
     return o, m, l
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, *, layout: str = "BNSD",
               sparse_mode: int = 0, atten_mask: Optional[np.ndarray] = None,
               cu_seqlens_q: Optional[np.ndarray] = None, cu_seqlens_kv: Optional[np.ndarray] = None,
-              block_keep: Optional[np.ndarray] = None):
+              block_keep: Optional[np.ndarray] = None, pre_tokens: Optional[int] = None,
+              next_tokens: Optional[int] = None):
     """Attention forward over a whole problem.
 
     BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D] -> o [B, Nq, Sq, D], m/l [B, Nq, Sq].
@@ -120,7 +136,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, *, layo
           leading 0) -> o [T, Nq, D], m/l [Nq, T].
     ``atten_mask``: uint8, 1 = masked, [Sq, Skv] / [B, 1, Sq, Skv] / [B, Nq, Sq, Skv] (BNSD).
     ``block_keep``: uint8 [B, Nq, QB, KB], 1 = keep (BNSD).
+    ``pre_tokens`` / ``next_tokens``: the sparse_mode 0 band (None = no limit).
     """
+    band = (pre_tokens, next_tokens)
     if layout == "BNSD":
         B, Nq, Sq, D = q.shape
         Nkv = k.shape[1]
@@ -134,7 +152,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, *, layo
             for h in range(Nq):
                 keep = None if block_keep is None else block_keep[b, h]
                 o[b, h], m[b, h], l[b, h] = _head(q[b, h], k[b, h // g], v[b, h // g], scale, sparse_mode,
-                                                  _mask_for_head(atten_mask, b, h), keep)
+                                                  _mask_for_head(atten_mask, b, h), keep, band)
         return o, m, l
     if layout == "TND":
         if atten_mask is not None or block_keep is not None:
@@ -152,7 +170,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, *, layo
             k0, k1 = int(cu_seqlens_kv[b]), int(cu_seqlens_kv[b + 1])
             for h in range(Nq):
                 oh, mh, lh = _head(q[q0:q1, h], k[k0:k1, h // g], v[k0:k1, h // g], scale, sparse_mode,
-                                   None, None)
+                                   None, None, band)
                 o[q0:q1, h], m[h, q0:q1], l[h, q0:q1] = oh, mh, lh
         return o, m, l
     raise ValueError("layout must be BNSD or TND")

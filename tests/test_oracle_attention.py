@@ -244,3 +244,44 @@ def test_matches_torch_sdpa(mode):
 def test_softmax_attention_empty_key_set():
     o, m, l = softmax_attention(np.ones((3, 2)), np.zeros((0, 2)), np.zeros((0, 2)), 1.0, np.zeros((3, 0), bool))
     assert np.all(o == 0) and np.all(np.isneginf(m)) and np.all(l == 0)
+
+
+# ---- the sparse_mode 0 range: pre_tokens / next_tokens (fused attention guide, section 4.3) ----
+
+@pytest.mark.parametrize("Sq,Skv", [(6, 6), (5, 9), (9, 4)])
+@pytest.mark.parametrize("pre,nxt", [(0, 0), (2, 1), (1, 3), (-1, 2), (3, -2), (2147483647, 0), (0, 2147483647),
+                                     (2147483647, 2147483647), (-3, 1)])
+def test_brute_force_band(Sq, Skv, pre, nxt):
+    D = 3
+    q, k, v = RNG.normal(size=(Sq, D)), RNG.normal(size=(Skv, D)), RNG.normal(size=(Skv, D))
+    ob, mb, lb = _brute(q, k, v, 0.6, lambda i, j: i - pre <= j <= i + nxt)
+    o, m, l = attention(q[None, None], k[None, None], v[None, None], 0.6, pre_tokens=pre, next_tokens=nxt)
+    np.testing.assert_allclose(o[0, 0], ob, atol=1e-12)
+    np.testing.assert_array_equal(np.isinf(m[0, 0]), np.isinf(mb))
+    fin = np.isfinite(mb)
+    np.testing.assert_allclose(m[0, 0][fin], mb[fin], atol=1e-12)
+    np.testing.assert_allclose(l[0, 0], lb, rtol=1e-12)
+
+
+@pytest.mark.parametrize("pre,nxt", [(100, 0), (0, 100), (37, 250), (300, -40), (-20, 90)])
+def test_zero_query_counts_band_keys(pre, nxt):
+    """Q = 0: every kept key has score 0, so l is the size of the row's range, which is
+    max(0, min(Skv - 1, i + next) - max(0, i - pre) + 1)."""
+    Sq, Skv, D = 260, 330, 4
+    q = np.zeros((Sq, D))
+    k, v = RNG.normal(size=(Skv, D)), RNG.normal(size=(Skv, 2))
+    o, m, l = attention(q[None, None], k[None, None], v[None, None], 1.0, pre_tokens=pre, next_tokens=nxt)
+    for i in range(Sq):
+        n = max(0, min(Skv - 1, i + nxt) - max(0, i - pre) + 1)
+        assert l[0, 0, i] == n
+        assert (m[0, 0, i] == 0.0) if n else np.isneginf(m[0, 0, i])
+
+
+def test_band_with_defaults_equals_unmasked_and_rejects_causal():
+    q, k, v = RNG.normal(size=(1, 1, 20, 3)), RNG.normal(size=(1, 1, 30, 3)), RNG.normal(size=(1, 1, 30, 3))
+    a = attention(q, k, v, 0.5)
+    b = attention(q, k, v, 0.5, pre_tokens=2147483647, next_tokens=2147483647)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    with pytest.raises(ValueError):
+        attention(q, k, v, 0.5, sparse_mode=2, pre_tokens=4)
