@@ -61,6 +61,11 @@
  * Definitions fixed by this library where the pages are silent
  *   - sparse_mode 2 keeps key j for query i when j <= i; sparse_mode 3 keeps it
  *     when j <= i + Skv - Sq (i, j counted inside one sequence).
+ *   - sparse_mode 0 keeps key j for query i when i - pre_tokens <= j <=
+ *     i + next_tokens (a band around the top-left diagonal, inside one
+ *     sequence); the defaults 2147483647 mean no limit. pre_tokens and
+ *     next_tokens must keep their defaults with sparse_mode 2 or 3 and on the
+ *     block-sparse and quantised entry points.
  *   - softmax_max m_i = max over kept j of s_ij (s = q.k * scale); softmax_sum
  *     l_i = sum over kept j of exp(s_ij - m_i). A row with no kept key gets
  *     O = 0, m = -inf, l = 0.
@@ -108,7 +113,7 @@ typedef struct qattn_desc {
   int32_t Skv;           /* key length; TND: total key tokens Tk */
   int32_t D;             /* head dimension: 64 or 128 */
   float scale;           /* softmax scale, finite and > 0 */
-  int32_t sparse_mode;   /* 0: none / explicit mask; 2: causal top-left; 3: causal bottom-right */
+  int32_t sparse_mode;   /* 0: none, explicit mask and/or band; 2: causal top-left; 3: causal bottom-right */
   const int32_t* cu_seqlens_q;  /* TND: host [B + 1] cumulative query lengths; else NULL */
   const int32_t* cu_seqlens_kv; /* TND: host [B + 1] cumulative key lengths; else NULL */
   const uint8_t* atten_mask;    /* not TND: device uint8, 1 = masked, 0 = kept; NULL = none */
@@ -117,6 +122,8 @@ typedef struct qattn_desc {
   int32_t head_end;
   int32_t qblock_begin;         /* subrange of q-blocks [qblock_begin, qblock_end); -1, -1 = all */
   int32_t qblock_end;
+  int32_t pre_tokens;           /* sparse_mode 0 band: keys up to this many before the diagonal */
+  int32_t next_tokens;          /* ... and this many after it; 2147483647 = no limit (both default) */
 } qattn_desc;
 
 /*

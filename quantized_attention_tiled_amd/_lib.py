@@ -60,7 +60,12 @@ class QattnDesc(ctypes.Structure):
         ("head_end", ctypes.c_int32),
         ("qblock_begin", ctypes.c_int32),
         ("qblock_end", ctypes.c_int32),
+        ("pre_tokens", ctypes.c_int32),
+        ("next_tokens", ctypes.c_int32),
     ]
+
+
+NO_LIMIT = 2147483647  # pre_tokens / next_tokens default: no band limit
 
 
 _lib = None

@@ -14,8 +14,8 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import (LAYOUT_BNSD, LAYOUT_BSND, LAYOUT_SBH, LAYOUT_TND, MASK_B1SS, MASK_BNSS, MASK_SS, QattnDesc,
-                   check, load)
+from ._lib import (LAYOUT_BNSD, LAYOUT_BSND, LAYOUT_SBH, LAYOUT_TND, MASK_B1SS, MASK_BNSS, MASK_SS, NO_LIMIT,
+                   QattnDesc, check, load)
 
 BLOCK = 128
 
@@ -58,7 +58,8 @@ def _ranges(head_range, qblock_range):
 
 def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: int, scale: float,
               sparse_mode: int = 0, cu_q=None, cu_kv=None, atten_mask: Optional[torch.Tensor] = None,
-              mask_kind: int = MASK_SS, head_range=None, qblock_range=None) -> QattnDesc:
+              mask_kind: int = MASK_SS, head_range=None, qblock_range=None, pre_tokens: int = NO_LIMIT,
+              next_tokens: int = NO_LIMIT) -> QattnDesc:
     d = QattnDesc()
     d.struct_size = ctypes.sizeof(QattnDesc)
     d.layout, d.B, d.Nq, d.Nkv, d.Sq, d.Skv, d.D = layout, B, Nq, Nkv, Sq, Skv, D
@@ -69,6 +70,7 @@ def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: i
     d.atten_mask = atten_mask.data_ptr() if atten_mask is not None else None
     d.mask_kind = int(mask_kind)
     (d.head_begin, d.head_end), (d.qblock_begin, d.qblock_end) = _ranges(head_range, qblock_range)
+    d.pre_tokens, d.next_tokens = int(pre_tokens), int(next_tokens)
     return d
 
 
@@ -127,13 +129,16 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
              cu_seqlens_q: Optional[Sequence[int]] = None, cu_seqlens_kv: Optional[Sequence[int]] = None,
              head_range: Optional[Tuple[int, int]] = None, qblock_range: Optional[Tuple[int, int]] = None,
              out: Optional[torch.Tensor] = None, softmax_max: Optional[torch.Tensor] = None,
-             softmax_sum: Optional[torch.Tensor] = None, head_num: Optional[int] = None):
+             softmax_sum: Optional[torch.Tensor] = None, head_num: Optional[int] = None,
+             pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT):
     """Dense bf16 attention forward; returns (out, softmax_max, softmax_sum).
 
     BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D]; BSND: q [B, Sq, Nq, D], k/v [B, Skv, Nkv, D];
     BSH: q [B, Sq, Nq * D], SBH: q [Sq, B, Nq * D] (k/v alike, with head_num = Nq); m/l [B, Nq, Sq].
     TND:  q [T, Nq, D], k/v [Tk, Nkv, D] plus cumulative lengths; m/l [Nq, T].
     ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (not with TND).
+    With sparse_mode 0, ``pre_tokens`` / ``next_tokens`` keep key j for query i when
+    i - pre_tokens <= j <= i + next_tokens (2147483647 = no limit).
     With a head or q-block range only that slice of the outputs is written.
     """
     lib = load()
@@ -173,7 +178,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
         raise ValueError("output shapes do not match")
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, atten_mask=atten_mask, mask_kind=kind, head_range=head_range,
-                     qblock_range=qblock_range)
+                     qblock_range=qblock_range, pre_tokens=pre_tokens, next_tokens=next_tokens)
     with torch.cuda.device(dev):
         check(lib.attn_fwd(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max), _vp(softmax_sum),
                            _stream(dev)))

@@ -172,10 +172,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
   const int wrow_last = min(wrow0 + 32, row_end) - 1;     // last valid row (< wrow0 if none)
   const bool wave_active = wrow0 < row_end;
 
-  // ---- key range ----
-  const int off = (MODE & kCausal) ? (p.causal == 3 ? Lkv - Lq : 0) : 0;
-  int kv_end = Lkv;
-  if constexpr ((MODE & kCausal) != 0) kv_end = min(Lkv, row_end - 1 + off + 1);
+  // ---- key range: the causal family keeps key j for row i when i - pre <= j <= i + off (top-left
+  // causal: off = 0; bottom-right: off = Lkv - Lq; the sparse_mode 0 band: off = next_tokens,
+  // pre = pre_tokens; the host clamps both into int range, pre = that bound when there is no lower
+  // limit). Tiles start at the one holding the workgroup's first row's lowest key. ----
+  const int off = (MODE & kCausal) ? (p.causal == 3 ? Lkv - Lq : p.band_next) : 0;
+  const int pre = (MODE & kCausal) ? p.band_pre : 0;
+  int kv_end = Lkv, t0 = 0;
+  if constexpr ((MODE & kCausal) != 0) {
+    kv_end = min(Lkv, row_end - 1 + off + 1);
+    t0 = max(row_begin - pre, 0) / kKT;
+  }
   int ntiles;
   const int32_t* list = nullptr;
   if constexpr ((MODE & kSparse) != 0) {
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
     list = p.idx + row * p.KB;
     ntiles = 2 * min(max(p.counts[row], 0), p.KB);
   } else {
-    ntiles = kv_end > 0 ? (kv_end + kKT - 1) / kKT : 0;
+    ntiles = kv_end > t0 * kKT ? (kv_end - t0 * kKT + kKT - 1) / kKT : 0;
   }
   // key0 of tile i, or -1 when a kept-list entry is out of range (the tile contributes nothing)
   auto tile_key0 = [&](int i) __attribute__((always_inline)) -> int {
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
       const int blk = list[i >> 1];
       return (blk >= 0 && blk < p.KB) ? blk * kBlock + (i & 1) * kKT : -1;
     } else {
-      return i * kKT;
+      return (t0 + i) * kKT;
     }
   };
 
@@ -279,13 +286,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
   // causal diagonal, or set in atten_mask
   auto apply_mask = [&](f32x16& s, int k0, bool valid) __attribute__((always_inline)) {
     const int q = wrow0 + l32;
-    // last allowed key of this row, relative to k0 and to this lane's 4 hl offset
-    int lim = Lkv - 1;
-    if constexpr ((MODE & kCausal) != 0) lim = min(lim, q + off);
+    // first and last allowed key of this row, relative to k0 and to this lane's 4 hl offset
+    int lim = Lkv - 1, lo = 0;
+    if constexpr ((MODE & kCausal) != 0) {
+      lim = min(lim, q + off);
+      lo = q - pre;
+    }
     lim = valid ? lim - k0 - 4 * hl : -1000000;
+    lo -= k0 + 4 * hl;
 #pragma unroll
     for (int r = 0; r < 16; r++)
-      if (key_off(r) > lim) s[r] = kNegInf;
+      if (key_off(r) > lim || ((MODE & kCausal) != 0 && key_off(r) < lo)) s[r] = kNegInf;
     if constexpr ((MODE & kMask) != 0) {
       const int qc = min(q, row_end - 1);
       const uint8_t* mrowp = p.mask + b * p.mask_sb + h * p.mask_sh + (int64_t)qc * p.mask_ss;
@@ -298,14 +309,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
   };
   auto half_needs_mask = [&](int k0, bool valid) __attribute__((always_inline)) {
     bool need = !valid || k0 + 32 > Lkv;
-    if constexpr ((MODE & kCausal) != 0) need = need || (k0 + 31 > wrow0 + off);
+    if constexpr ((MODE & kCausal) != 0) need = need || (k0 + 31 > wrow0 + off) || (k0 < wrow_last - pre);
     if constexpr ((MODE & kMask) != 0) need = true;
     return need;
   };
   // a causal half tile wholly above this wave's diagonal contributes nothing
   auto half_runs = [&](int k0) __attribute__((always_inline)) {
     bool run = wave_active;
-    if constexpr ((MODE & kCausal) != 0) run = run && k0 <= wrow_last + off;
+    if constexpr ((MODE & kCausal) != 0) run = run && k0 <= wrow_last + off && k0 + 31 >= wrow0 - pre;
     return run;
   };
 
@@ -495,7 +506,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
     if constexpr ((MODE & kMask) != 0) return false;
     const int key0 = tile_key0(i);
     if (key0 < 0 || key0 + kKT > Lkv) return false;
-    if constexpr ((MODE & kCausal) != 0) return key0 + kKT - 1 <= row_begin + off;
+    if constexpr ((MODE & kCausal) != 0) return key0 + kKT - 1 <= row_begin + off && key0 >= row_end - 1 - pre;
     return true;
   };
   auto bookkeep = [&](bool fast, int hidx, f32x16& s, bool& run) __attribute__((always_inline)) -> float {

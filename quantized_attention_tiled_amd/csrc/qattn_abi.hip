@@ -38,8 +38,11 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   if (!(std::isfinite(d->scale) && d->scale > 0.f)) return fail(QATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (d->sparse_mode != 0 && d->sparse_mode != 2 && d->sparse_mode != 3)
     return fail(QATTN_INVALID_ARGUMENT, "sparse_mode %d (supported: 0, 2, 3)", d->sparse_mode);
-  if (!allow_masks && (d->sparse_mode != 0 || d->atten_mask != nullptr))
-    return fail(QATTN_UNSUPPORTED, "block-sparse entry points take no causal mode and no atten_mask");
+  const bool band = d->pre_tokens != INT32_MAX || d->next_tokens != INT32_MAX;
+  if (band && d->sparse_mode != 0)
+    return fail(QATTN_INVALID_ARGUMENT, "pre_tokens / next_tokens set the sparse_mode 0 range only");
+  if (!allow_masks && (d->sparse_mode != 0 || d->atten_mask != nullptr || band))
+    return fail(QATTN_UNSUPPORTED, "block-sparse entry points take no causal mode, band or atten_mask");
   if (d->atten_mask != nullptr) {
     if (d->layout == QATTN_LAYOUT_TND) return fail(QATTN_UNSUPPORTED, "atten_mask is not available with TND");
     if (d->mask_kind < QATTN_MASK_SS || d->mask_kind > QATTN_MASK_BNSS)
@@ -56,6 +59,14 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   p.scale = d->scale;
   p.c = (float)((double)d->scale * 1.4426950408889634);
   p.causal = d->sparse_mode;
+  // causal-family key range i - band_pre <= j <= i + band_next, clamped to +-(Sq + Skv + 256) so
+  // that the kernels' int arithmetic cannot overflow (beyond that a limit removes nothing)
+  {
+    const int64_t lim = (int64_t)d->Sq + d->Skv + 256;
+    auto clampl = [lim](int64_t x) { return (int)std::max(-lim, std::min(lim, x)); };
+    p.band_pre = band ? clampl(d->pre_tokens) : (int)lim;
+    p.band_next = band ? clampl(d->next_tokens) : 0;
+  }
   int qblocks;
   if (d->layout != QATTN_LAYOUT_TND) {
     // element strides of batch, head and token (the head dimension is contiguous)
@@ -221,6 +232,7 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.mask = desc->atten_mask;
   int mode = 0;
   if (desc->sparse_mode == 2 || desc->sparse_mode == 3) mode |= qattn::kCausal;
+  if (desc->pre_tokens != INT32_MAX || desc->next_tokens != INT32_MAX) mode |= qattn::kCausal;  // the band
   if (desc->atten_mask) mode |= qattn::kMask;
   if (desc->layout == QATTN_LAYOUT_TND) mode |= qattn::kVarlen;
   if ((rc = finish_items(p, qattn::bf16_qblocks_per_tile(mode)))) return rc;

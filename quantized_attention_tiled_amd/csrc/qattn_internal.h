@@ -55,7 +55,8 @@ struct FwdParams {
   int total_items;
   float c;      // scale * log2(e): scores go to the base-2 exponent domain
   float scale;
-  int causal;   // 0 none, 2 top-left, 3 bottom-right
+  int causal;   // 0 none or the sparse_mode 0 band, 2 top-left, 3 bottom-right
+  int band_pre, band_next;  // causal-family key range i - band_pre <= j <= i + band_next (see the ABI)
   int nseq;
   int cu_q[kMaxSeqs + 1];
   int cu_kv[kMaxSeqs + 1];

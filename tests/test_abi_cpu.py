@@ -67,7 +67,8 @@ def _desc(q, **kw):
     d = q.QattnDesc()
     d.struct_size = ctypes.sizeof(q.QattnDesc)
     base = dict(layout=0, B=1, Nq=4, Nkv=2, Sq=256, Skv=256, D=128, scale=0.1, sparse_mode=0, mask_kind=0,
-                head_begin=-1, head_end=-1, qblock_begin=-1, qblock_end=-1)
+                head_begin=-1, head_end=-1, qblock_begin=-1, qblock_end=-1, pre_tokens=2147483647,
+                next_tokens=2147483647)
     base.update(kw)
     for k, v in base.items():
         setattr(d, k, v)
@@ -82,7 +83,7 @@ def _fwd(q, d, qp=FAKE, kp=FAKE, vp=FAKE, op=FAKE, m=0, l=0):
 @pytest.mark.parametrize("kw,status", [
     (dict(D=96), 2), (dict(D=0), 2), (dict(Nq=3, Nkv=2), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
     (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(sparse_mode=1), 1), (dict(layout=4), 1),
-    (dict(layout=-1), 1), (dict(layout=3, B=64, Nq=64, Nkv=64, Skv=1 << 17, Sq=128), 2),
+    (dict(layout=-1), 1), (dict(sparse_mode=2, pre_tokens=5), 1), (dict(sparse_mode=3, next_tokens=0), 1), (dict(layout=3, B=64, Nq=64, Nkv=64, Skv=1 << 17, Sq=128), 2),
     (dict(layout=2, Nq=64, Nkv=64, Skv=1 << 20, Sq=128), 2),
     (dict(B=0), 1), (dict(Sq=-1), 1), (dict(Nkv=0), 1), (dict(head_begin=0, head_end=5), 1),
     (dict(head_begin=3, head_end=2), 1), (dict(qblock_begin=0, qblock_end=3), 1), (dict(qblock_begin=-2, qblock_end=1), 1),
@@ -146,6 +147,10 @@ def test_blocksparse_and_qbsa_validation(q):
     assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 2
     d = _desc(q)
     assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None) == 1
+    d = _desc(q, pre_tokens=10)  # the band is a dense-entry-point option
+    assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 2
+    assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, next_tokens=0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, None, None, None) == 2
     assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, layout=1)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                              None, None, None) == 2
     for lay in (2, 3):  # BSND and SBH are bf16-only layouts

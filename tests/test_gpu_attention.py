@@ -243,3 +243,51 @@ def test_blocksparse_layouts_match_bnsd(qa, layout):
     torch.cuda.synchronize()
     assert torch.equal(_bits(_from_layout(out[0], layout, B, Nq, S, D)), _bits(ref[0]))
     assert torch.equal(_bits(out[1]), _bits(ref[1])) and torch.equal(_bits(out[2]), _bits(ref[2]))
+
+
+# ---- the sparse_mode 0 range: pre_tokens / next_tokens (fused attention guide, section 4.3) ----
+
+@pytest.mark.parametrize("B,Nq,Nkv,Sq,Skv,D,pre,nxt", [
+    (1, 2, 2, 512, 512, 128, 100, 0),       # sliding window ending at the diagonal
+    (2, 4, 2, 300, 300, 64, 64, 64),        # symmetric band, ragged tails, GQA 2
+    (1, 2, 1, 700, 450, 128, 130, 200),     # Sq > Skv
+    (1, 2, 2, 260, 900, 128, 0, 300),       # only keys at or after the diagonal
+    (1, 2, 2, 640, 640, 64, 2147483647, 31),
+    (1, 2, 2, 640, 640, 128, 300, -40),     # band strictly below the diagonal
+    (1, 1, 1, 400, 400, 128, -10, 5),       # narrow band strictly above it
+    (1, 1, 1, 300, 300, 128, -20, 10),      # empty band: every row fully masked
+])
+def test_band(qa, B, Nq, Nkv, Sq, Skv, D, pre, nxt):
+    banner(f"band B={B} Nq={Nq} Nkv={Nkv} Sq={Sq} Skv={Skv} D={D} pre={pre} next={nxt}")
+    q, k, v = _bnsd(800 + Sq + D, B, Nq, Nkv, Sq, Skv, D)
+    scale = 1.0 / np.sqrt(D)
+    o, m, l = qa.attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=scale, pre_tokens=pre, next_tokens=nxt)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), scale, pre_tokens=pre, next_tokens=nxt)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+
+
+def test_band_with_boolean_mask_and_tnd(qa):
+    B, Nq, Nkv, S, D = 2, 2, 2, 333, 128
+    q, k, v = _bnsd(901, B, Nq, Nkv, S, S, D)
+    mask = (np.random.default_rng(902).random((B, 1, S, S)) < 0.3).astype(np.uint8)
+    o, m, l = qa.attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=0.1, atten_mask=torch.from_numpy(mask).cuda(),
+                          pre_tokens=90, next_tokens=20)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), 0.1, atten_mask=mask, pre_tokens=90, next_tokens=20)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+    lens = [300, 5, 700, 130]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    qt = random_bf16(903, (T, 4, D))
+    kt = random_bf16(904, (T, 2, D))
+    vt = random_bf16(905, (T, 2, D))
+    o, m, l = qa.attn_fwd(dev_bf16(qt), dev_bf16(kt), dev_bf16(vt), scale=0.1, layout="TND", cu_seqlens_q=cu.tolist(),
+                          pre_tokens=150, next_tokens=0)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(f64(qt), f64(kt), f64(vt), 0.1, layout="TND", cu_seqlens_q=cu, cu_seqlens_kv=cu,
+                                  pre_tokens=150, next_tokens=0)
+    check_o(to_np(o), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)

@@ -48,8 +48,9 @@ def _pieces(n_heads, n_qb):
     return splits
 
 
-@pytest.mark.parametrize("mode,masked", [(0, False), (2, False), (3, False), (0, True), (3, True)])
-def test_dense_subranges(qa, mode, masked):
+@pytest.mark.parametrize("mode,masked,band", [(0, False, None), (2, False, None), (3, False, None), (0, True, None),
+                                             (3, True, None), (0, False, (200, 30)), (0, True, (64, 300))])
+def test_dense_subranges(qa, mode, masked, band):
     B, Nq, Nkv, S, D = 1, 8, 4, 1100, 128
     banner(f"subrange dense mode={mode} masked={masked}")
     q = dev_bf16(random_bf16(1, (B, Nq, S, D)))
@@ -59,13 +60,14 @@ def test_dense_subranges(qa, mode, masked):
     if masked:  # B1SS boolean mask, about 20% of the keys masked
         g = torch.Generator(device="cuda").manual_seed(5)
         mask = (torch.rand((B, 1, S, S), generator=g, device="cuda") < 0.2).to(torch.uint8)
-    full = qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, atten_mask=mask)
+    bk = {} if band is None else dict(pre_tokens=band[0], next_tokens=band[1])
+    full = qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, atten_mask=mask, **bk)
     nqb = (S + 127) // 128
     for split in _pieces(Nq, nqb):
         out = (torch.zeros_like(full[0]), torch.zeros_like(full[1]), torch.zeros_like(full[2]))
         for hr, br in split:
             qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, atten_mask=mask, head_range=hr, qblock_range=br,
-                        out=out[0], softmax_max=out[1], softmax_sum=out[2])
+                        out=out[0], softmax_max=out[1], softmax_sum=out[2], **bk)
         torch.cuda.synchronize()
         _same(full, out)
 
