@@ -320,8 +320,8 @@ def operator_sweep(seqs, sparsities=(0.0, 0.5, 0.9), reps=5):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c2_dense_8k")
     ap.add_argument("--seq", type=int, default=None, help="override S (dense BNSD configs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
