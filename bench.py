@@ -31,11 +31,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS (executed + dense-equiv), % MFMA peak, S=8K–64K"
-PEAK_BF16 = 2500.0   # TFLOP/s, MI355X published dense bf16 MFMA
+PEAK_BF16 = 2500.0   # TFLOP/s, MI355X published dense bf16 and fp16 MFMA
 PEAK_FP8 = 5000.0    # TFLOP/s (fp8) / TOP/s (int8), published dense
 HBM_PEAK = 8000.0    # GB/s
 KERNEL_SOURCES = {
-    "dense": ["attn_bf16.hip"], "blocksparse": ["attn_bf16.hip", "quant.hip"],
+    "dense": ["attn_fwd_kernel.h", "attn_fwd_bf16.hip"],
+    "blocksparse": ["attn_fwd_kernel.h", "attn_fwd_bf16.hip", "quant.hip"],
     "qbsa": ["attn_qbsa.hip", "quant.hip"],
 }
 
@@ -60,6 +61,7 @@ def flop_counts(w):
     the keys up to the end of the 64-key tile that holds the diagonal of the
     q-block's last row."""
     D = w.D
+    fpp = 2 * (D + w.v.shape[-1])  # flops per (q, k) pair: Q.K^T over D and P.V over Dv
     if w.layout == "TND":
         lens = np.diff(w.cu_seqlens_q)
         dense = useful = executed = 0
@@ -74,7 +76,7 @@ def flop_counts(w):
             else:
                 useful += L * L
                 executed += L * L
-        f = 4 * D * w.Nq
+        f = fpp * w.Nq
         return f * executed, f * useful, f * dense
     dense = w.B * w.Nq * w.Sq * w.Skv
     if w.keep is not None:
@@ -82,18 +84,19 @@ def flop_counts(w):
         rows = np.minimum(128, w.Sq - np.arange(w.keep.shape[2]) * 128)
         per_row = (w.keep.astype(np.int64) * blk[None, None, None, :]).sum(axis=3)
         pairs = int((per_row * rows[None, None, :]).sum())
-        return 4 * D * pairs, 4 * D * pairs, 4 * D * dense
-    return 4 * D * dense, 4 * D * dense, 4 * D * dense
+        return fpp * pairs, fpp * pairs, fpp * dense
+    return fpp * dense, fpp * dense, fpp * dense
 
 
 def algorithmic_bytes(w, kind):
     """Minimum HBM bytes of one step: read every input once, write every output once."""
     el = lambda a: int(np.prod(a.shape))  # noqa: E731
     ml = 2 * 4 * w.Nq * w.Sq * (w.B if w.layout == "BNSD" else 1)
+    eo = el(w.q) // w.D * w.v.shape[-1]  # output elements (head dimension Dv)
     if kind == "dense":
-        return 2 * (el(w.q) + el(w.k) + el(w.v)) + 2 * el(w.q) + ml
+        return 2 * (el(w.q) + el(w.k) + el(w.v)) + 2 * eo + ml
     if kind == "blocksparse":
-        return 2 * (el(w.q) + el(w.k) + el(w.v)) + 2 * el(w.q) + ml + el(w.keep) + 4 * el(w.keep)
+        return 2 * (el(w.q) + el(w.k) + el(w.v)) + 2 * eo + ml + el(w.keep) + 4 * el(w.keep)
     # quantised: bf16 in, int8/fp8 codes out and read back, bf16 O
     return (2 * (el(w.q) + el(w.k) + el(w.v)) + (el(w.q) + el(w.k) + el(w.v)) * 2 + 2 * el(w.q) + ml
             + 5 * el(w.keep))
@@ -330,6 +333,9 @@ def main(argv=None):
     ap.add_argument("--no-smi", action="store_true", help="skip the sustained clock / power sample")
     ap.add_argument("--sweep", action="store_true", help="operator sweep (S x sparsity x kernel) instead of one line")
     ap.add_argument("--sweep-seqs", default="8192,16384,32768,65536")
+    ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16",
+                    help="input / output type of the dense and block-sparse configs (fp16: the same values in float16)")
+    ap.add_argument("--dv", type=int, default=None, help="value head dimension below D (dense / block-sparse configs)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -354,13 +360,27 @@ def main(argv=None):
     log(f"generating {a.config} {'S=' + str(a.seq) if a.seq else ''}")
     w = make_workload(a.config, S=a.seq) if a.seq else make_workload(a.config)
     name = a.config if not a.seq else f"{a.config}_S{a.seq}"
+    if (a.dtype != "bf16" or a.dv) and kind == "qbsa":
+        log("--dtype / --dv apply to the dense and block-sparse configs only")
+        return 2
+    if a.dv:
+        if not 0 < a.dv < w.D:
+            log(f"--dv must lie below D = {w.D}")
+            return 2
+        w.v = np.ascontiguousarray(w.v[..., :a.dv])  # the first Dv channels of the same draw
+        name += f"_dv{a.dv}"
+    if a.dtype != "bf16":
+        name += f"_{a.dtype}"
     dev = torch.device("cuda:0")
 
     def up(bits):
+        if a.dtype == "fp16":  # the same values (bf16 -> fp16 is exact in this range) as float16
+            from workloads import bf16_bits_to_f32
+            return torch.from_numpy(bf16_bits_to_f32(bits).astype(np.float16)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v = up(w.q), up(w.k), up(w.v)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=dev)
     ml_shape = (w.B, w.Nq, w.Sq) if w.layout == "BNSD" else (w.Nq, w.Sq)
     m = torch.empty(ml_shape, dtype=torch.float32, device=dev)
     l = torch.empty(ml_shape, dtype=torch.float32, device=dev)
@@ -376,7 +396,7 @@ def main(argv=None):
                         cu_seqlens_kv=cu, out=o, softmax_max=m, softmax_sum=l)
             if kb is not None:
                 kb.record(stream)
-        dtype, peak = "bf16", PEAK_BF16
+        dtype, peak = a.dtype, PEAK_BF16
     elif kind == "blocksparse":
         keep = torch.from_numpy(w.keep).to(dev)
         counts = torch.empty(w.keep.shape[:3], dtype=torch.int32, device=dev)
@@ -389,7 +409,7 @@ def main(argv=None):
             qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=w.scale, out=o, softmax_max=m, softmax_sum=l)
             if kb is not None:
                 kb.record(stream)
-        dtype, peak = "bf16", PEAK_BF16
+        dtype, peak = a.dtype, PEAK_BF16
     else:
         keep = torch.from_numpy(w.keep).to(dev)
         counts = torch.empty(w.keep.shape[:3], dtype=torch.int32, device=dev)
@@ -443,7 +463,7 @@ def main(argv=None):
     # the dominant kernel: algorithmic flops of one launch / its mean launch duration (HIP events on the
     # launch stream, bracketing that launch alone)
     roof = {"bound": "mfma", "achieved": round(kvalue, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(kvalue / peak, 4), "traffic": traffic, "kernel": "attn_bf16_kernel" if kind != "qbsa"
+            "frac": round(kvalue / peak, 4), "traffic": traffic, "kernel": "attn_fwd_kernel" if kind != "qbsa"
             else "attn_qbsa_kernel", "flop_per_launch": ex, "launch_ms": round(kms, 4)}
     sustained = None if a.no_smi else sustained_clock_power(step, ms)
     cpu = None
@@ -457,6 +477,8 @@ def main(argv=None):
     else:
         wl = f"{name}: {w.description}" + (f" (S overridden to {w.Sq})" if a.seq else "")
         conf = {"workload": wl, "layout": "BNSD", "B": w.B, "N": w.Nq, "Nkv": w.Nkv, "S": w.Sq, "D": w.D}
+        if a.dv:
+            conf["Dv"] = a.dv
         if w.keep is not None:
             conf["kept_fraction"] = round(float(w.keep.mean()), 4)
     line = {

@@ -6,8 +6,9 @@
  *     section 2: O = Softmax(Mask(Q K^T * scale)) V, computed tile by tile with
  *     an online softmax so the S x S score matrix is never stored;
  *     section 3/4: head_num, input_layout (BNSD, BSND, BSH, SBH, TND), atten_mask with
- *     1 = masked and shapes SS / B1SS / BNSS, scale, sparse_mode 2/3 causal,
- *     cumulative sequence lengths for varlen;
+ *     1 = masked and shapes SS / B1SS / BNSS, scale, sparse_mode 2/3 causal and
+ *     the sparse_mode 0 range, cumulative sequence lengths for varlen; float16
+ *     or bfloat16 inputs of one type, and a value head dimension Dv <= D;
  *     section 5: outputs are the attention result plus softmax_max and
  *     softmax_sum per query row;
  *     section 7: GQA with Nq / Nkv an integer.
@@ -29,9 +30,10 @@
  *   - Every call is asynchronous on the caller's HIP stream (`stream` is a
  *     hipStream_t; NULL means the default stream). Buffers must stay alive
  *     until the stream has passed the call.
- *   - bf16 tensors are raw bfloat16 bits (uint16_t). Every pointer passed to a
- *     kernel must be 16-byte aligned, and every innermost dimension is
- *     contiguous.
+ *   - 16-bit tensors (qattn_bf16, i.e. uint16_t storage) hold raw bfloat16
+ *     bits, or IEEE binary16 bits where desc->dtype is QATTN_DTYPE_FP16. Every
+ *     pointer passed to a kernel must be 16-byte aligned, and every innermost
+ *     dimension is contiguous.
  *   - Validation happens on the host before any launch. On any error nothing
  *     is launched and no output byte is written. Device data (mask contents,
  *     NaN or Inf in inputs) is not inspected; kept-list entries outside
@@ -40,7 +42,7 @@
  *     for the calling thread's most recent failure. Nothing throws across
  *     the ABI.
  *
- * Layouts
+ * Layouts (v and o have head dimension Dv; q and k have D)
  *   BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D], o like q;
  *         softmax_max / softmax_sum fp32 [B, Nq, Sq].
  *   BSND: q [B, Sq, Nq, D], k/v [B, Skv, Nkv, D], o like q. BSH, [B, S, N * D],
@@ -94,13 +96,16 @@ extern "C" {
 #define QATTN_LAYOUT_BSND 2 /* also BSH */
 #define QATTN_LAYOUT_SBH 3
 
+#define QATTN_DTYPE_BF16 0 /* bfloat16 q, k, v and o */
+#define QATTN_DTYPE_FP16 1 /* IEEE float16 q, k, v and o */
+
 #define QATTN_MASK_SS 0   /* atten_mask [Sq, Skv] shared by all batches and heads */
 #define QATTN_MASK_B1SS 1 /* atten_mask [B, 1, Sq, Skv] shared by heads */
 #define QATTN_MASK_BNSS 2 /* atten_mask [B, Nq, Sq, Skv] */
 
 #define QATTN_MAX_SEQS 256 /* TND: at most this many sequences per call */
 
-typedef uint16_t qattn_bf16; /* bfloat16 storage */
+typedef uint16_t qattn_bf16; /* 16-bit element storage: bfloat16, or float16 per desc->dtype */
 
 /* Problem description shared by the three attention entry points. */
 typedef struct qattn_desc {
@@ -124,12 +129,17 @@ typedef struct qattn_desc {
   int32_t qblock_end;
   int32_t pre_tokens;           /* sparse_mode 0 band: keys up to this many before the diagonal */
   int32_t next_tokens;          /* ... and this many after it; 2147483647 = no limit (both default) */
+  int32_t dtype;                /* QATTN_DTYPE_BF16 (default) or _FP16: type of q, k, v and o; the
+                                   quantised entry point takes BF16 only */
+  int32_t Dv;                   /* value / output head dimension; 0 means D. Supported: Dv = D, or
+                                   D = 128 with Dv = 64; the quantised entry point needs Dv = D */
 } qattn_desc;
 
 /*
- * attn_fwd -- dense bf16 attention forward (fused attention guide, sections
+ * attn_fwd -- dense 16-bit attention forward (fused attention guide, sections
  * 2-5 and 7; power-cap page, InsertComm/BlockAttn splitting).
- *   q, k, v: bf16 in desc->layout; o: bf16, same shape as q.
+ *   q, k, v: bf16 or fp16 (desc->dtype) in desc->layout; o: same type, shape of
+ *   q with head dimension Dv. P is rounded to that type before P.V.
  *   softmax_max, softmax_sum: fp32 outputs (layouts above), each nullable.
  *   Causal modes and an explicit atten_mask may be combined (a pair is kept
  *   only when both keep it). atten_mask is not available with TND.
@@ -151,12 +161,12 @@ int build_kv_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32
                         void* stream);
 
 /*
- * attn_fwd_blocksparse -- bf16 block-sparse attention (EagleQBSA article,
+ * attn_fwd_blocksparse -- 16-bit block-sparse attention (EagleQBSA article,
  * BF16 BSA baseline; 128 x 128 blocks): each (batch, q-head, q-block) attends
  * only to the keys of its kept kv-blocks, visited in list order; masked
  * blocks are skipped, never computed.
  *   desc: BNSD, BSND/BSH or SBH (not TND), sparse_mode 0, atten_mask NULL
- *   (else QATTN_UNSUPPORTED).
+ *   (else QATTN_UNSUPPORTED); dtype and Dv as for attn_fwd.
  *   counts/idx: as produced by build_kv_block_list for [B, Nq, QB, KB].
  */
 int attn_fwd_blocksparse(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k,
@@ -193,7 +203,8 @@ int quantize_v_perchannel_fp8(const qattn_bf16* v, int B, int N, int S, int D, u
  * with INT8 MFMA; online softmax in fp32; p cast to FP8 E4M3 (unscaled,
  * round half even); acc += p8 . v_q with FP8 MFMA; O = acc * v_scale[d] / l,
  * where l sums the unrounded p. Output bf16.
- *   desc: BNSD (other layouts: QATTN_UNSUPPORTED), sparse_mode 0, atten_mask NULL.
+ *   desc: BNSD (other layouts: QATTN_UNSUPPORTED), sparse_mode 0, atten_mask NULL,
+ *   dtype BF16, Dv = D.
  *   q: int8 [B, Nq, Sq, D]; k: int8 [B, Nkv, Skv, D]; v: E4M3FN [B, Nkv, Skv, D];
  *   q_scale: fp32 [B, Nq, QB]; k_scale: fp32 [B, Nkv, KB]; v_scale: fp32 [B, Nkv, D].
  *   counts/idx: kept list [B, Nq, QB, KB]. softmax_max/sum nullable (the

@@ -23,6 +23,7 @@ LAYOUT_TND = 1
 LAYOUT_BSND = 2  # also BSH
 LAYOUT_SBH = 3
 MASK_SS, MASK_B1SS, MASK_BNSS = 0, 1, 2
+DTYPE_BF16, DTYPE_FP16 = 0, 1
 MAX_SEQS = 256
 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "MISALIGNED", 4: "HIP_ERROR"}
@@ -62,6 +63,8 @@ class QattnDesc(ctypes.Structure):
         ("qblock_end", ctypes.c_int32),
         ("pre_tokens", ctypes.c_int32),
         ("next_tokens", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("Dv", ctypes.c_int32),
     ]
 
 

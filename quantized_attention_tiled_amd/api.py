@@ -14,10 +14,11 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import (LAYOUT_BNSD, LAYOUT_BSND, LAYOUT_SBH, LAYOUT_TND, MASK_B1SS, MASK_BNSS, MASK_SS, NO_LIMIT,
-                   QattnDesc, check, load)
+from ._lib import (DTYPE_BF16, DTYPE_FP16, LAYOUT_BNSD, LAYOUT_BSND, LAYOUT_SBH, LAYOUT_TND, MASK_B1SS, MASK_BNSS,
+                   MASK_SS, NO_LIMIT, QattnDesc, check, load)
 
 BLOCK = 128
+_DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16}
 
 
 def _vp(t: Optional[torch.Tensor]):
@@ -59,7 +60,7 @@ def _ranges(head_range, qblock_range):
 def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: int, scale: float,
               sparse_mode: int = 0, cu_q=None, cu_kv=None, atten_mask: Optional[torch.Tensor] = None,
               mask_kind: int = MASK_SS, head_range=None, qblock_range=None, pre_tokens: int = NO_LIMIT,
-              next_tokens: int = NO_LIMIT) -> QattnDesc:
+              next_tokens: int = NO_LIMIT, dtype: int = DTYPE_BF16, Dv: int = 0) -> QattnDesc:
     d = QattnDesc()
     d.struct_size = ctypes.sizeof(QattnDesc)
     d.layout, d.B, d.Nq, d.Nkv, d.Sq, d.Skv, d.D = layout, B, Nq, Nkv, Sq, Skv, D
@@ -71,12 +72,14 @@ def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: i
     d.mask_kind = int(mask_kind)
     (d.head_begin, d.head_end), (d.qblock_begin, d.qblock_end) = _ranges(head_range, qblock_range)
     d.pre_tokens, d.next_tokens = int(pre_tokens), int(next_tokens)
+    d.dtype, d.Dv = int(dtype), int(Dv)
     return d
 
 
 def _dims(layout: str, q: torch.Tensor, k: torch.Tensor, head_num: Optional[int]):
     """(layout code, B, Nq, Sq, Nkv, Skv, D) of the batched layouts: BNSD and BSND are 4-D, BSH and
-    SBH 3-D with H = head_num * D (head_num counts the query heads; the kv heads follow from k)."""
+    SBH 3-D with H = head_num * D (head_num counts the query heads; the kv heads follow from k).
+    D is the query/key head dimension; v's follows from v (``_value_dim``)."""
     if layout in ("BNSD", "BSND"):
         if q.dim() != 4 or k.dim() != 4:
             raise ValueError(f"{layout} tensors must be 4-D")
@@ -104,6 +107,25 @@ def _dims(layout: str, q: torch.Tensor, k: torch.Tensor, head_num: Optional[int]
     return code, B, Nq, Sq, Nkv, Skv, D
 
 
+def _value_dim(layout: str, k: torch.Tensor, v: torch.Tensor, Nkv: int) -> int:
+    """Head dimension of v, whose other dimensions must match k's."""
+    if v.dim() != k.dim() or v.shape[:-1] != k.shape[:-1]:
+        raise ValueError(f"v {tuple(v.shape)} does not match k {tuple(k.shape)} outside the head dimension")
+    if layout in ("BSH", "SBH"):
+        if v.shape[-1] % Nkv:
+            raise ValueError(f"v's H = {v.shape[-1]} is not a multiple of Nkv = {Nkv}")
+        return v.shape[-1] // Nkv
+    return v.shape[-1]
+
+
+def _check_dtypes(q, k, v, dev) -> int:
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, q.dtype, dev)
+    return _DTYPES[q.dtype]
+
+
 def _mask_kind(mask: torch.Tensor, B: int, Nq: int, Sq: int, Skv: int) -> int:
     if mask.dim() == 2 and tuple(mask.shape) == (Sq, Skv):
         return MASK_SS
@@ -114,9 +136,9 @@ def _mask_kind(mask: torch.Tensor, B: int, Nq: int, Sq: int, Skv: int) -> int:
     raise ValueError(f"atten_mask shape {tuple(mask.shape)} is not SS, B1SS or BNSS for B={B} Nq={Nq} Sq={Sq} Skv={Skv}")
 
 
-def _outputs(q, out, softmax_max, softmax_sum, ml_shape):
+def _outputs(q, out, softmax_max, softmax_sum, ml_shape, o_shape=None):
     if out is None:
-        out = torch.empty_like(q, dtype=torch.bfloat16)
+        out = torch.empty(q.shape if o_shape is None else o_shape, dtype=q.dtype, device=q.device)
     if softmax_max is None:
         softmax_max = torch.empty(ml_shape, dtype=torch.float32, device=q.device)
     if softmax_sum is None:
@@ -131,11 +153,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
              out: Optional[torch.Tensor] = None, softmax_max: Optional[torch.Tensor] = None,
              softmax_sum: Optional[torch.Tensor] = None, head_num: Optional[int] = None,
              pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT):
-    """Dense bf16 attention forward; returns (out, softmax_max, softmax_sum).
+    """Dense attention forward on bfloat16 or float16 q, k, v (one type); returns (out,
+    softmax_max, softmax_sum), out in that type.
 
     BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D]; BSND: q [B, Sq, Nq, D], k/v [B, Skv, Nkv, D];
     BSH: q [B, Sq, Nq * D], SBH: q [Sq, B, Nq * D] (k/v alike, with head_num = Nq); m/l [B, Nq, Sq].
     TND:  q [T, Nq, D], k/v [Tk, Nkv, D] plus cumulative lengths; m/l [Nq, T].
+    v may have a smaller head dimension Dv (128 / 64); out then has Dv where q has D.
     ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (not with TND).
     With sparse_mode 0, ``pre_tokens`` / ``next_tokens`` keep key j for query i when
     i - pre_tokens <= j <= i + next_tokens (2147483647 = no limit).
@@ -143,17 +167,14 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     """
     lib = load()
     dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, n, torch.bfloat16, dev)
-    if k.shape != v.shape:
-        raise ValueError("k and v must have the same shape")
+    dtype = _check_dtypes(q, k, v, dev)
     if layout != "TND":
         lay, B, Nq, Sq, Nkv, Skv, D = _dims(layout, q, k, head_num)
         cu_q, cu_kv, ml_shape = None, None, (B, Nq, Sq)
     else:
         Sq, Nq, D = q.shape
         Skv, Nkv = k.shape[0], k.shape[1]
-        if k.shape[2] != D:
+        if k.dim() != 3 or k.shape[2] != D:
             raise ValueError("k/v must be [Tk, Nkv, D] matching q")
         cu_q, cu_kv = _cu(cu_seqlens_q), _cu(cu_seqlens_kv if cu_seqlens_kv is not None else cu_seqlens_q)
         if cu_q is None:
@@ -162,6 +183,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
             raise ValueError("cu_seqlens_q and cu_seqlens_kv differ in length")
         B = len(cu_q) - 1
         lay, ml_shape = LAYOUT_TND, (Nq, Sq)
+    Dv = _value_dim(layout, k, v, Nkv)
+    o_shape = q.shape[:-1] + (q.shape[-1] // D * Dv,)
     kind = MASK_SS
     if atten_mask is not None:
         if atten_mask.dtype == torch.bool:
@@ -170,15 +193,15 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
         if layout == "TND":
             raise ValueError("atten_mask is not available with TND")
         kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)
-    out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, ml_shape)
-    for t, n, dt in ((out, "out", torch.bfloat16), (softmax_max, "softmax_max", torch.float32),
+    out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, ml_shape, o_shape)
+    for t, n, dt in ((out, "out", q.dtype), (softmax_max, "softmax_max", torch.float32),
                      (softmax_sum, "softmax_sum", torch.float32)):
         _require(t, n, dt, dev)
-    if out.shape != q.shape or tuple(softmax_max.shape) != ml_shape or tuple(softmax_sum.shape) != ml_shape:
+    if out.shape != o_shape or tuple(softmax_max.shape) != ml_shape or tuple(softmax_sum.shape) != ml_shape:
         raise ValueError("output shapes do not match")
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, atten_mask=atten_mask, mask_kind=kind, head_range=head_range,
-                     qblock_range=qblock_range, pre_tokens=pre_tokens, next_tokens=next_tokens)
+                     qblock_range=qblock_range, pre_tokens=pre_tokens, next_tokens=next_tokens, dtype=dtype, Dv=Dv)
     with torch.cuda.device(dev):
         check(lib.attn_fwd(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max), _vp(softmax_sum),
                            _stream(dev)))
@@ -209,21 +232,27 @@ def build_kv_block_list(keep: torch.Tensor, counts: Optional[torch.Tensor] = Non
 def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range=None, qblock_range=None,
                          out=None, softmax_max=None, softmax_sum=None, layout: str = "BNSD",
                          head_num: Optional[int] = None):
-    """bf16 block-sparse attention over a kept-block list (BNSD, BSND, BSH or SBH, shapes as for
-    attn_fwd); returns (out, m [B, Nq, Sq], l)."""
+    """Block-sparse attention over a kept-block list on bfloat16 or float16 q, k, v (BNSD, BSND,
+    BSH or SBH, shapes and Dv as for attn_fwd); returns (out, m [B, Nq, Sq], l)."""
     lib = load()
     dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, n, torch.bfloat16, dev)
+    dtype = _check_dtypes(q, k, v, dev)
     _require(counts, "counts", torch.int32, dev)
     _require(idx, "idx", torch.int32, dev)
     lay, B, Nq, Sq, Nkv, Skv, D = _dims(layout, q, k, head_num)
+    Dv = _value_dim(layout, k, v, Nkv)
+    o_shape = q.shape[:-1] + (q.shape[-1] // D * Dv,)
     QB, KB = (Sq + BLOCK - 1) // BLOCK, (Skv + BLOCK - 1) // BLOCK
     if tuple(counts.shape) != (B, Nq, QB) or tuple(idx.shape) != (B, Nq, QB, KB):
         raise ValueError("counts/idx must be [B, Nq, QB] and [B, Nq, QB, KB]")
-    out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, (B, Nq, Sq))
+    out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, (B, Nq, Sq), o_shape)
+    for t, n, dt in ((out, "out", q.dtype), (softmax_max, "softmax_max", torch.float32),
+                     (softmax_sum, "softmax_sum", torch.float32)):
+        _require(t, n, dt, dev)
+    if out.shape != o_shape:
+        raise ValueError("output shape does not match")
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
-                     head_range=head_range, qblock_range=qblock_range)
+                     head_range=head_range, qblock_range=qblock_range, dtype=dtype, Dv=Dv)
     with torch.cuda.device(dev):
         check(lib.attn_fwd_blocksparse(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max),
                                        _vp(softmax_sum), _vp(counts), _vp(idx), _stream(dev)))

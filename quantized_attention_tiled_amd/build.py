@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
-SOURCES = ["qattn_abi.hip", "attn_bf16.hip", "attn_qbsa.hip", "quant.hip"]
+SOURCES = ["qattn_abi.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_qbsa.hip", "quant.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are switched off for all device code; the host
@@ -26,7 +26,8 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # The attention kernels run two waves per SIMD (256 registers per lane) and keep every MFMA
 # accumulator in ordinary VGPRs, so no accumulator is copied between register files.
-SOURCE_FLAGS = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+SOURCE_FLAGS = {"attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+                "attn_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
                 "attn_qbsa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
@@ -49,7 +50,7 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
+def build(jobs: int = 5, verbose: bool = False) -> str:
     """Compile every HIP source and link libqattn.so; returns the library path."""
     os.makedirs(OBJDIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
@@ -67,7 +68,7 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--jobs", type=int, default=5)
     ap.add_argument("--verbose", action="store_true")
     a = ap.parse_args(argv)
     print(build(a.jobs, a.verbose))

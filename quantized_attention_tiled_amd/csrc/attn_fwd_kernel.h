@@ -1,12 +1,14 @@
-// Fused, tiled bf16 attention forward for gfx950 (dense, causal, boolean mask,
-// varlen TND, GQA, 128 x 128 block-sparse).
+// Fused, tiled 16-bit attention forward for gfx950 (bf16 or fp16 inputs; dense, causal, band,
+// boolean mask, varlen TND, GQA, 128 x 128 block-sparse; value head dimension DV <= D).
+// The kernel template lives in this header; attn_fwd_bf16.hip and attn_fwd_f16.hip instantiate
+// it once per element type.
 //
 // What it computes: the fused attention guide ("Ascend NPU fused attention
 // operator", section 2) defines O = Softmax(Mask(Q K^T scale)) V evaluated with
 // tiling and an online softmax, never storing the score matrix; section 5
 // adds the per-row softmax max and sum; section 4 gives the masks and
-// layouts. The block-sparse variant is the BF16 BSA baseline of the EagleQBSA
-// article (128 x 128 blocks, masked blocks skipped).
+// layouts, the two input types (float16, bfloat16) and D_v <= D_k. The block-sparse variant is
+// the BF16 BSA baseline of the EagleQBSA article (128 x 128 blocks, masked blocks skipped).
 //
 // Work decomposition: 4 waves per 128-row q-block of one (batch, head); each wave owns 32 query
 // rows and needs at most 256 VGPRs per lane, so every SIMD runs two waves whose matrix and vector
@@ -19,9 +21,9 @@
 //     HBM with buffer_load ... lds (16 bytes per lane, no staging registers) into XOR-swizzled
 //     row-major tiles. The loads of K(j + 2) and V(j + 1) are spread over the MFMA slots of
 //     the first step after the single barrier of tile j; they land by the barrier of tile j + 1;
-//   * scores are formed transposed on v_mfma_f32_32x32x16_bf16, so one query sits in one lane
-//     column: the row max and the row sum are register chains plus one v_permlane32_swap;
-//   * P stays in registers: S^T converted to bf16 is directly the B operand of
+//   * scores are formed transposed on v_mfma_f32_32x32x16_{bf16,f16}, so one query sits in one
+//     lane column: the row max and the row sum are register chains plus one v_permlane32_swap;
+//   * P stays in registers: S^T converted to the input type (RNE) is directly the B operand of
 //     O^T += V^T P^T, whose V^T operand comes from the row-major V tile via ds_read_b64_tr_b16;
 //   * a three-stage software pipeline over 32-key half tiles h: while the VALU runs the
 //     softmax of h, the matrix cores compute the scores of h + 1 and P(h - 1) V(h - 1), one
@@ -30,19 +32,21 @@
 //     offset (the tile loop is unrolled by two so the ring slots are compile-time constants).
 // Softmax in the base-2 domain: p = exp2(s c - m_ref), c = scale log2(e), one FMA and one
 // v_exp_f32 per score. m_ref of a row is fixed at its first finite half-tile max and O is never
-// rescaled: p may exceed 1, up to 2^kRefSlack, which fp32 and bf16 carry with unchanged relative
-// precision. A wave whose true row max outgrows m_ref by more than kRefSlack flags itself, and
+// rescaled: p may exceed 1, up to 2^slack, which fp32 and the 16-bit type carry with unchanged
+// relative precision (slack 64 for bf16; 15 for fp16, whose largest finite value is 65504). A
+// wave whose true row max outgrows m_ref by more than the slack flags itself, and
 // the workgroup runs the key loop a second time in which only flagged waves recompute, from
 // their now-known true maxima. softmax_sum is rescaled to the true max at the end.
 // Every query row's arithmetic depends only on its own 32-row wave slice and the key order,
 // never on the launch shape, so any head / q-block subrange launch reproduces the full call bit
 // for bit.
+#pragma once
+
 #include "qattn_internal.h"
 
 namespace qattn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -54,7 +58,27 @@ constexpr int kPF = 2;   // MFMA operands are read from LDS this many slots ahea
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kRefSlack = 64.0f;  // base-2 exponent growth tolerated above a row's reference max
+
+// Element type of Q, K, V, P and O: 8-element MFMA operands, the MFMA and the largest base-2
+// exponent growth tolerated above a row's reference max (p <= 2^slack must stay finite in E).
+template <typename E>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  static constexpr float kSlack = 64.0f;
+  __device__ static f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Elem<_Float16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  static constexpr float kSlack = 15.0f;
+  __device__ static f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 template <int V>
 struct IC {
@@ -71,10 +95,6 @@ __device__ __forceinline__ void pin_use(const T& x) {
   asm volatile("" ::"v"(x));
 }
 
-__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 // max / sum of x over lanes l and l ^ 32 (v_permlane32_swap returns both halves)
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
@@ -85,8 +105,8 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-// LDS tile geometry: 64 rows of D bf16 (D * 2 bytes), 16-byte chunks XOR-swizzled per row, loaded
-// by kWaves waves.
+// LDS tile geometry: 64 rows of D 16-bit elements (D * 2 bytes), 16-byte chunks XOR-swizzled per
+// row, loaded by kWaves waves.
 template <int D, int kWaves>
 struct Tile {
   static constexpr int kRowBytes = D * 2;
@@ -101,20 +121,25 @@ struct Tile {
 };
 
 // NQB q-blocks per workgroup share every K/V tile: 4 NQB waves, two waves per SIMD either way
-// (two workgroups per CU for NQB = 1, one for NQB = 2).
-template <int D, int MODE, int NQB>
-__global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_kernel(const FwdParams p) {
+// (two workgroups per CU for NQB = 1, one for NQB = 2). D is the query/key head dimension, DV
+// the value head dimension (DV <= D).
+template <typename E, int D, int DV, int MODE, int NQB>
+__global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_kernel(const FwdParams p) {
+  typedef typename Elem<E>::v8 ev8;
+  constexpr float kRefSlack = Elem<E>::kSlack;
   constexpr int kWaves = kWavesPerBlock * NQB;
-  using T = Tile<D, kWaves>;
+  using T = Tile<D, kWaves>;    // K tiles
+  using TV = Tile<DV, kWaves>;  // V tiles
   constexpr int DT = D / 16;    // score MFMAs per half tile (k-steps of 16)
-  constexpr int DB = D / 32;    // 32-row blocks of O^T
+  constexpr int DB = DV / 32;   // 32-row blocks of O^T
   constexpr int NPV = 2 * DB;   // P V MFMAs per half tile (2 chunks of 16 keys x DB)
-  static_assert(DT == NPV, "score and P V MFMAs alternate one to one");
+  static_assert(DV <= D && NPV >= 4, "value head dimension");
   constexpr int M = DT + NPV;   // MFMAs per pipeline step
-  static_assert(T::kLoadsPerWave >= 1, "tile load split");
+  static_assert(M >= 8, "the row-max stages take slots 0 .. 6");
+  static_assert(T::kLoadsPerWave >= 1 && TV::kLoadsPerWave >= 1, "tile load split");
 
   // K slots 0, 1, then V slots 0, 1
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::kBytes + 2 * TV::kBytes];
   constexpr int kOffK = 0;
   constexpr int kOffV = 2 * T::kBytes;
 
@@ -166,7 +191,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
 
   const uint16_t* qp = p.q + b * p.q_sb + h * p.q_sh + q_tok0 * p.q_ss;
   const uint16_t* kp = p.k + b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
-  const uint16_t* vp = p.v + b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
+  const uint16_t* vp = p.v + b * p.v_sb + g * p.v_sh + kv_tok0 * p.v_ss;
 
   const int wrow0 = row_begin + wave * 32;                // first row of this wave
   const int wrow_last = min(wrow0 + 32, row_end) - 1;     // last valid row (< wrow0 if none)
@@ -207,41 +232,51 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
   // per lane. The swizzle of a lane's chunk does not depend on n, so one per-lane byte offset
   // serves every load; the tile's key offset goes in the scalar offset. The buffer extent is the
   // sequence's valid rows: rows past it (a ragged last tile) read as zeros and are masked. ----
-  const int64_t key_bytes = p.k_ss * 2;  // bytes between consecutive keys
+  const int64_t key_bytes = p.k_ss * 2;   // bytes between consecutive keys
+  const int64_t vkey_bytes = p.v_ss * 2;  // and between consecutive values
   const int lrow = wave * T::kRowsPerLoad + lane / T::kChunks;
-  const int lphys = lane % T::kChunks;
-  const uint32_t k_lane_off = (uint32_t)(lrow * key_bytes) + (uint32_t)((lphys ^ T::kswz(lrow)) << 4);
-  const uint32_t v_lane_off = (uint32_t)(lrow * key_bytes) + (uint32_t)((lphys ^ T::vswz(lrow)) << 4);
-  constexpr int kLoadRows = kWaves * T::kRowsPerLoad;  // rows between two loads of one wave
-  const int kv_extent = Lkv > 0 ? (int)((Lkv - 1) * key_bytes) + T::kRowBytes : 0;
-  const rsrc4 k_rsrc = make_rsrc(kp, (uint32_t)kv_extent);
-  const rsrc4 v_rsrc = make_rsrc(vp, (uint32_t)kv_extent);
-  auto issue_tile = [&](const rsrc4& rsrc, int lds_off, int key0, uint32_t lane_off) __attribute__((always_inline)) {
-    // an out-of-range kept-list entry loads the first keys (the tile is masked out entirely)
-    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(max(key0, 0)) * (uint32_t)key_bytes;
-#pragma unroll
-    for (int n = 0; n < T::kLoadsPerWave; n++)
-      load_lds16(rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), lane_off, soff + (uint32_t)(n * kLoadRows * key_bytes));
+  const int lrow_v = wave * TV::kRowsPerLoad + lane / TV::kChunks;
+  const uint32_t k_lane_off = (uint32_t)(lrow * key_bytes) + (uint32_t)(((lane % T::kChunks) ^ T::kswz(lrow)) << 4);
+  const uint32_t v_lane_off =
+      (uint32_t)(lrow_v * vkey_bytes) + (uint32_t)(((lane % TV::kChunks) ^ TV::vswz(lrow_v)) << 4);
+  const int k_extent = Lkv > 0 ? (int)((Lkv - 1) * key_bytes) + T::kRowBytes : 0;
+  const int v_extent = Lkv > 0 ? (int)((Lkv - 1) * vkey_bytes) + TV::kRowBytes : 0;
+  const rsrc4 k_rsrc = make_rsrc(kp, (uint32_t)k_extent);
+  const rsrc4 v_rsrc = make_rsrc(vp, (uint32_t)v_extent);
+  // Load n of a K (V) tile whose first key sits soff bytes into the sequence: rows between two
+  // loads of one wave are kWaves * kRowsPerLoad apart.
+  auto issue_one_k = [&](int lds_off, uint32_t soff, int n) __attribute__((always_inline)) {
+    load_lds16(k_rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), k_lane_off,
+               soff + (uint32_t)(n * kWaves * T::kRowsPerLoad * key_bytes));
   };
-  // Load n of tile i into a ring slot, with soff = tile_soff(i): the ring loads after the first
-  // ones are spread over the MFMA slots of a pipeline step instead of being issued in a burst.
-  // A tile past the end loads the first keys into a slot that is not read again.
-  auto issue_one = [&](const rsrc4& rsrc, int lds_off, uint32_t soff, uint32_t lane_off, int n) __attribute__((always_inline)) {
-    load_lds16(rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), lane_off, soff + (uint32_t)(n * kLoadRows * key_bytes));
+  auto issue_one_v = [&](int lds_off, uint32_t soff, int n) __attribute__((always_inline)) {
+    load_lds16(v_rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), v_lane_off,
+               soff + (uint32_t)(n * kWaves * TV::kRowsPerLoad * vkey_bytes));
   };
-  auto tile_soff = [&](int i) __attribute__((always_inline)) -> uint32_t {
+  // Byte offsets of tile i's first key in K and in V. The ring loads after the first ones are
+  // spread over the MFMA slots of a pipeline step instead of being issued in a burst; a tile past
+  // the end (or an out-of-range kept-list entry, masked out entirely) loads the first keys.
+  auto tile_soff = [&](int i, int64_t bytes) __attribute__((always_inline)) -> uint32_t {
     const int key0 = i < ntiles ? tile_key0(i) : 0;
-    return (uint32_t)__builtin_amdgcn_readfirstlane(max(key0, 0)) * (uint32_t)key_bytes;
+    return (uint32_t)__builtin_amdgcn_readfirstlane(max(key0, 0)) * (uint32_t)bytes;
   };
-  auto issue_k = [&](int i, int slot) __attribute__((always_inline)) { issue_tile(k_rsrc, kOffK + slot * T::kBytes, tile_key0(i), k_lane_off); };
-  auto issue_v = [&](int i, int slot) __attribute__((always_inline)) { issue_tile(v_rsrc, kOffV + slot * T::kBytes, tile_key0(i), v_lane_off); };
+  auto issue_k = [&](int i, int slot) __attribute__((always_inline)) {
+    const uint32_t soff = tile_soff(i, key_bytes);
+#pragma unroll
+    for (int n = 0; n < T::kLoadsPerWave; n++) issue_one_k(kOffK + slot * T::kBytes, soff, n);
+  };
+  auto issue_v = [&](int i, int slot) __attribute__((always_inline)) {
+    const uint32_t soff = tile_soff(i, vkey_bytes);
+#pragma unroll
+    for (int n = 0; n < TV::kLoadsPerWave; n++) issue_one_v(kOffV + slot * TV::kBytes, soff, n);
+  };
 
   // ---- this wave's query rows as the Q^T B operand: lane (hl, l32) holds row l32, 16-byte chunk
   // 2 t + hl for k-step t ----
-  bf16x8 qreg[DT];
+  ev8 qreg[DT];
   {
     const int r = max(min(wrow0 + l32, row_end - 1), 0);
-    const bf16x8* src = (const bf16x8*)(qp + (int64_t)r * p.q_ss);
+    const ev8* src = (const ev8*)(qp + (int64_t)r * p.q_ss);
 #pragma unroll
     for (int t = 0; t < DT; t++) qreg[t] = src[2 * t + hl];
   }
@@ -262,21 +297,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
   {
     const int grp = lane >> 4, sl = lane & 15;
     const int vrow0 = 4 * (grp >> 1) + (sl >> 2);
-    const int vs = T::vswz(vrow0);
+    const int vs = TV::vswz(vrow0);
 #pragma unroll
     for (int db = 0; db < DB; db++) {
       const int chunk = 4 * db + 2 * (grp & 1) + ((sl & 3) >> 1);
-      vaddr[db] = vrow0 * T::kRowBytes + ((chunk ^ vs) << 4) + 8 * (sl & 1);
+      vaddr[db] = vrow0 * TV::kRowBytes + ((chunk ^ vs) << 4) + 8 * (sl & 1);
     }
   }
-  auto read_k = [&](int slot, int hf, int t) __attribute__((always_inline)) -> bf16x8 {
-    return *(const bf16x8*)(smem + kOffK + slot * T::kBytes + hf * 32 * T::kRowBytes + kaddr[t]);
+  auto read_k = [&](int slot, int hf, int t) __attribute__((always_inline)) -> ev8 {
+    return *(const ev8*)(smem + kOffK + slot * T::kBytes + hf * 32 * T::kRowBytes + kaddr[t]);
   };
-  auto read_v = [&](int slot, int kc, int db) __attribute__((always_inline)) -> bf16x8 {
-    const uint8_t* base = smem + kOffV + slot * T::kBytes + kc * 16 * T::kRowBytes + vaddr[db];
+  auto read_v = [&](int slot, int kc, int db) __attribute__((always_inline)) -> ev8 {
+    const uint8_t* base = smem + kOffV + slot * TV::kBytes + kc * 16 * TV::kRowBytes + vaddr[db];
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * T::kRowBytes));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * TV::kRowBytes));
+    return __builtin_bit_cast(ev8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
   // register r of a 32-key accumulator block holds key 8 (r / 4) + 4 hl + r % 4 of that block
@@ -349,8 +384,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
   // tile (V slot VD, from dv) over the step's slots; DMA = 0 issues none. Hard scheduling barriers
   // keep each MFMA with its slice of VALU work.
   auto step = [&](auto KS, auto KH, auto VS, auto VH, auto NEXT, auto CUR, auto PREV, auto PIN, auto POUT,
-                  auto KS2, auto KH2, auto DMA, f32x16& sn, const f32x16& sc, const bf16x8 (&pp)[2],
-                  bf16x8 (&pc)[2], bf16x8 (&carry)[2], float mu, bool run, uint32_t dk, uint32_t dv)
+                  auto KS2, auto KH2, auto DMA, f32x16& sn, const f32x16& sc, const ev8 (&pp)[2],
+                  ev8 (&pc)[2], ev8 (&carry)[2], float mu, bool run, uint32_t dk, uint32_t dv)
                   __attribute__((always_inline)) {
     constexpr int dma_ = decltype(DMA)::value;
     constexpr int ks_ = decltype(KS)::value, kh_ = decltype(KH)::value;
@@ -360,7 +395,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
     constexpr bool pout_ = decltype(POUT)::value != 0;
     constexpr int ks2_ = decltype(KS2)::value, kh2_ = decltype(KH2)::value;
     constexpr int kPairSlots = M - 2;  // first-stage slots of the score pairs of the current half
-    bf16x8 op[M];
+    ev8 op[M];
     auto fetch = [&](int k) __attribute__((always_inline)) {
       if (k < DT) {
         if (next_) op[k] = read_k(ks_, kh_, k);
@@ -389,25 +424,25 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
         carry[k + kPF - M] = read_k(ks2_, kh2_, k + kPF - M);
       }
       if constexpr (dma_ != 0) {
-        constexpr int L = T::kLoadsPerWave;
+        constexpr int LK = T::kLoadsPerWave, LV = TV::kLoadsPerWave;
 #pragma unroll
-        for (int j = 0; j < 2 * L; j++) {
-          if ((j * M) / (2 * L) != k) continue;
-          if (j < L)
-            issue_one(k_rsrc, kOffK + ((dma_ - 1) & 1) * T::kBytes, dk, k_lane_off, j);
+        for (int j = 0; j < LK + LV; j++) {
+          if ((j * M) / (LK + LV) != k) continue;
+          if (j < LK)
+            issue_one_k(kOffK + ((dma_ - 1) & 1) * T::kBytes, dk, j);
           else
-            issue_one(v_rsrc, kOffV + ((dma_ - 1) >> 1) * T::kBytes, dv, v_lane_off, j - L);
+            issue_one_v(kOffV + ((dma_ - 1) >> 1) * TV::kBytes, dv, j - LK);
         }
       }
       if (k < DT) {
-        if (next_) sn = mfma_bf16(op[k], qreg[k], k == 0 ? f32x16{} : sn);
+        if (next_) sn = Elem<E>::mfma(op[k], qreg[k], k == 0 ? f32x16{} : sn);
       } else {
-        if (prev_) o[(k - DT) % DB] = mfma_bf16(op[k], pp[(k - DT) / DB], o[(k - DT) % DB]);
+        if (prev_) o[(k - DT) % DB] = Elem<E>::mfma(op[k], pp[(k - DT) / DB], o[(k - DT) % DB]);
       }
       if (cur_) {
         // The softmax of score pair q (registers 2 q, 2 q + 1) runs in three stages on consecutive
-        // slots a(q), a(q) + 1, a(q) + 2: the two FMAs, the two exponentials, then the bf16
-        // conversion and the row-sum additions, so no instruction waits on another of its own slot.
+        // slots a(q), a(q) + 1, a(q) + 2: the two FMAs, the two exponentials, then the conversion
+        // to E and the row-sum additions, so no instruction waits on another of its own slot.
         // Register r goes to element r % 8 of P chunk r / 8. The row sum adds the pair sums t(q) in
         // order q = 0, 1, .. (one slot behind their own stage).
 #pragma unroll
@@ -426,8 +461,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
             pin_use(x[2 * q + 1]);
           }
           if (aq + 2 == k) {
-            pc[q >> 2][(2 * q) & 7] = (__bf16)x[2 * q];
-            pc[q >> 2][(2 * q + 1) & 7] = (__bf16)x[2 * q + 1];
+            pc[q >> 2][(2 * q) & 7] = (E)x[2 * q];
+            pc[q >> 2][(2 * q + 1) & 7] = (E)x[2 * q + 1];
             t[q & 1] = x[2 * q] + x[2 * q + 1];
             if (q > 0) ps = q == 1 ? t[0] : ps + t[(q - 1) & 1];
             pin_use(t[q & 1]);
@@ -531,8 +566,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
 
     if (ntiles > 0) {
       f32x16 sx, sy;        // score buffers: the pipeline alternates between them
-      bf16x8 pu[2], pv[2];  // P buffers, likewise
-      bf16x8 carry[2];      // operands handed from step to step
+      ev8 pu[2], pv[2];  // P buffers, likewise
+      ev8 carry[2];      // operands handed from step to step
       float mu;
       bool run;
       // prologue: K(0), K(1) and V(0) land; scores of half 0
@@ -543,14 +578,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
       __syncthreads();
       sy = f32x16{};
 #pragma unroll
-      for (int t = 0; t < DT; t++) sy = mfma_bf16(read_k(0, 0, t), qreg[t], sy);
+      for (int t = 0; t < DT; t++) sy = Elem<E>::mfma(read_k(0, 0, t), qreg[t], sy);
       mu = finish(0, sy, run);
       // step 0: softmax of half 0, scores of half 1 (K(0), second half), no P V yet
       step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{},
            sx, sy, pv, pu, carry, mu, run, 0u, 0u);
       // barrier of tile 0: every wave is done with K(0); K(2) and V(1) are loaded during step 1
       __syncthreads();
-      uint32_t dk = tile_soff(2), dv = tile_soff(1);
+      uint32_t dk = tile_soff(2, key_bytes), dv = tile_soff(1, vkey_bytes);
       mu = finish(1, sx, run);
 
       // Tile it (parity PAR = it % 2) runs steps 2 it + 1 and 2 it + 2:
@@ -574,8 +609,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
                IC<0>{}, IC<0>{}, sx, sy, pv, pu, carry, mu, run, 0u, 0u);
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it + 2), V(it + 1)
           __syncthreads();
-          dk = tile_soff(it + 3);
-          dv = tile_soff(it + 2);
+          dk = tile_soff(it + 3, key_bytes);
+          dv = tile_soff(it + 2, vkey_bytes);
           mu = bookkeep(fast, 2 * it + 3, sx, run);
         } else {
           step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
@@ -620,14 +655,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
   const float lout = (mtrue == kNegInf) ? 0.f : lt * __builtin_amdgcn_exp2f(mref - mtrue);
   const int q = wrow0 + l32;
   if (q < row_end) {
-    uint16_t* op = p.o + b * p.q_sb + h * p.q_sh + (q_tok0 + q) * p.q_ss;
+    uint16_t* op = p.o + b * p.o_sb + h * p.o_sh + (q_tok0 + q) * p.o_ss;
 #pragma unroll
     for (int db = 0; db < DB; db++)
 #pragma unroll
       for (int g4 = 0; g4 < 4; g4++) {
-        __bf16 v4[4];
+        E v4[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) v4[e] = (__bf16)(o[db][4 * g4 + e] * inv);
+        for (int e = 0; e < 4; e++) v4[e] = (E)(o[db][4 * g4 + e] * inv);
         *(uint2*)(op + db * 32 + 8 * g4 + 4 * hl) = __builtin_bit_cast(uint2, v4);
       }
     if (hl == 0) {
@@ -638,40 +673,37 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_bf16_
   }
 }
 
-template <int D, int MODE, int NQB>
+template <typename E, int D, int DV, int MODE, int NQB>
 hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   if (p.qblocks_per_tile != NQB) return hipErrorInvalidValue;
   const int grid = grid_for_items(p.total_items);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, NQB>), dim3(grid), dim3(64 * kWavesPerBlock * NQB), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<E, D, DV, MODE, NQB>), dim3(grid), dim3(64 * kWavesPerBlock * NQB), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
-template <int D>
+template <typename E, int D, int DV>
 hipError_t launch_d(const FwdParams& p, int mode, hipStream_t stream) {
   switch (mode) {
-    case 0: return launch_t<D, 0, 2>(p, stream);
-    case kCausal: return launch_t<D, kCausal, 1>(p, stream);
-    case kMask: return launch_t<D, kMask, 2>(p, stream);
-    case kCausal | kMask: return launch_t<D, kCausal | kMask, 1>(p, stream);
-    case kSparse: return launch_t<D, kSparse, 1>(p, stream);
-    case kVarlen: return launch_t<D, kVarlen, 2>(p, stream);
-    case kVarlen | kCausal: return launch_t<D, kVarlen | kCausal, 1>(p, stream);
+    case 0: return launch_t<E, D, DV, 0, 2>(p, stream);
+    case kCausal: return launch_t<E, D, DV, kCausal, 1>(p, stream);
+    case kMask: return launch_t<E, D, DV, kMask, 2>(p, stream);
+    case kCausal | kMask: return launch_t<E, D, DV, kCausal | kMask, 1>(p, stream);
+    case kSparse: return launch_t<E, D, DV, kSparse, 1>(p, stream);
+    case kVarlen: return launch_t<E, D, DV, kVarlen, 2>(p, stream);
+    case kVarlen | kCausal: return launch_t<E, D, DV, kVarlen | kCausal, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-}  // namespace
-
-// q-blocks per workgroup by mode (the host sets qblocks_per_tile to match): two consecutive
-// q-blocks share the K/V tiles when both see the same keys (no causal mask, no kept list);
-// causal and block-sparse launches take one q-block each.
-int bf16_qblocks_per_tile(int mode) { return (mode & (kCausal | kSparse)) ? 1 : 2; }
-
-
-hipError_t launch_attn_bf16(const FwdParams& p, int mode, hipStream_t stream) {
-  if (p.D == 64) return launch_d<64>(p, mode, stream);
-  if (p.D == 128) return launch_d<128>(p, mode, stream);
+// Every (D, DV) pair the library supports, for element type E.
+template <typename E>
+hipError_t launch_attn_fwd(const FwdParams& p, int mode, hipStream_t stream) {
+  if (p.D == 64 && p.Dv == 64) return launch_d<E, 64, 64>(p, mode, stream);
+  if (p.D == 128 && p.Dv == 128) return launch_d<E, 128, 128>(p, mode, stream);
+  if (p.D == 128 && p.Dv == 64) return launch_d<E, 128, 64>(p, mode, stream);
   return hipErrorInvalidValue;
 }
 
+}  // namespace
 }  // namespace qattn

@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int q = wrow0 + l32;
   if (q < row_end) {
-    uint16_t* op = p.o + b * p.q_sb + h * p.q_sh + (int64_t)q * p.q_ss;
+    uint16_t* op = p.o + b * p.o_sb + h * p.o_sh + (int64_t)q * p.o_ss;
     const float* vsc = p.v_scale + ((int64_t)b * p.Nkv + g) * D;
 #pragma unroll
     for (int db = 0; db < DB; db++)

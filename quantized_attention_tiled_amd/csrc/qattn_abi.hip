@@ -35,6 +35,12 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
     return fail(QATTN_INVALID_ARGUMENT, "bad sizes B=%d Nq=%d Nkv=%d Sq=%d Skv=%d", d->B, d->Nq, d->Nkv, d->Sq, d->Skv);
   if (d->Nq % d->Nkv != 0) return fail(QATTN_INVALID_ARGUMENT, "Nq=%d is not a multiple of Nkv=%d", d->Nq, d->Nkv);
   if (d->D != 64 && d->D != 128) return fail(QATTN_UNSUPPORTED, "head dimension D=%d (supported: 64, 128)", d->D);
+  if (d->dtype != QATTN_DTYPE_BF16 && d->dtype != QATTN_DTYPE_FP16)
+    return fail(QATTN_INVALID_ARGUMENT, "dtype %d is not BF16 (0) or FP16 (1)", d->dtype);
+  const int Dv = d->Dv == 0 ? d->D : d->Dv;
+  if (Dv < 0 || Dv > d->D) return fail(QATTN_INVALID_ARGUMENT, "Dv=%d must lie in [1, D=%d] (0 means D)", d->Dv, d->D);
+  if (Dv != d->D && !(d->D == 128 && Dv == 64))
+    return fail(QATTN_UNSUPPORTED, "Dv=%d with D=%d (supported: Dv = D, or D = 128 with Dv = 64)", Dv, d->D);
   if (!(std::isfinite(d->scale) && d->scale > 0.f)) return fail(QATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (d->sparse_mode != 0 && d->sparse_mode != 2 && d->sparse_mode != 3)
     return fail(QATTN_INVALID_ARGUMENT, "sparse_mode %d (supported: 0, 2, 3)", d->sparse_mode);
@@ -56,6 +62,7 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   p.Sq = d->Sq;
   p.Skv = d->Skv;
   p.D = D;
+  p.Dv = Dv;
   p.scale = d->scale;
   p.c = (float)((double)d->scale * 1.4426950408889634);
   p.causal = d->sparse_mode;
@@ -70,28 +77,26 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   int qblocks;
   if (d->layout != QATTN_LAYOUT_TND) {
     // element strides of batch, head and token (the head dimension is contiguous)
-    if (d->layout == QATTN_LAYOUT_BNSD) {
-      p.q_sb = (int64_t)d->Nq * d->Sq * D;
-      p.q_sh = (int64_t)d->Sq * D;
-      p.q_ss = D;
-      p.k_sb = (int64_t)d->Nkv * d->Skv * D;
-      p.k_sh = (int64_t)d->Skv * D;
-      p.k_ss = D;
-    } else if (d->layout == QATTN_LAYOUT_BSND) {
-      p.q_sb = (int64_t)d->Sq * d->Nq * D;
-      p.q_sh = D;
-      p.q_ss = (int64_t)d->Nq * D;
-      p.k_sb = (int64_t)d->Skv * d->Nkv * D;
-      p.k_sh = D;
-      p.k_ss = (int64_t)d->Nkv * D;
-    } else {  // SBH
-      p.q_sb = (int64_t)d->Nq * D;
-      p.q_sh = D;
-      p.q_ss = (int64_t)d->B * d->Nq * D;
-      p.k_sb = (int64_t)d->Nkv * D;
-      p.k_sh = D;
-      p.k_ss = (int64_t)d->B * d->Nkv * D;
-    }
+    // of a [B | S, N, S | B, width] tensor in the layout, for N heads, length S and head width w
+    auto strides = [&](int N, int S, int w, int64_t& sb, int64_t& sh, int64_t& ss) {
+      if (d->layout == QATTN_LAYOUT_BNSD) {
+        sb = (int64_t)N * S * w;
+        sh = (int64_t)S * w;
+        ss = w;
+      } else if (d->layout == QATTN_LAYOUT_BSND) {
+        sb = (int64_t)S * N * w;
+        sh = w;
+        ss = (int64_t)N * w;
+      } else {  // SBH
+        sb = (int64_t)N * w;
+        sh = w;
+        ss = (int64_t)d->B * N * w;
+      }
+    };
+    strides(d->Nq, d->Sq, D, p.q_sb, p.q_sh, p.q_ss);
+    strides(d->Nkv, d->Skv, D, p.k_sb, p.k_sh, p.k_ss);
+    strides(d->Nkv, d->Skv, Dv, p.v_sb, p.v_sh, p.v_ss);
+    strides(d->Nq, d->Sq, Dv, p.o_sb, p.o_sh, p.o_ss);
     p.ml_sb = (int64_t)d->Nq * d->Sq;
     p.ml_sh = d->Sq;
     p.ml_ss = 1;
@@ -131,13 +136,19 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
     p.k_sb = 0;
     p.k_sh = D;
     p.k_ss = (int64_t)d->Nkv * D;
+    p.v_sb = 0;
+    p.v_sh = Dv;
+    p.v_ss = (int64_t)d->Nkv * Dv;
+    p.o_sb = 0;
+    p.o_sh = Dv;
+    p.o_ss = (int64_t)d->Nq * Dv;
     p.ml_sb = 0;
     p.ml_sh = d->Sq;
     p.ml_ss = 1;
     p.QB = p.KB = 0;
   }
   // The kernels address the K and V rows of one (batch, kv-head) through 32-bit byte offsets.
-  if (((int64_t)std::max(d->Skv, 1) - 1) * p.k_ss * 2 + 2 * D > (int64_t)INT32_MAX)
+  if (((int64_t)std::max(d->Skv, 1) - 1) * std::max(p.k_ss, p.v_ss) * 2 + 2 * D > (int64_t)INT32_MAX)
     return fail(QATTN_UNSUPPORTED, "K/V rows of one head span more than 2^31 bytes (Skv=%d, key stride %lld)", d->Skv,
                 (long long)p.k_ss);
   // subrange
@@ -235,9 +246,11 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   if (desc->pre_tokens != INT32_MAX || desc->next_tokens != INT32_MAX) mode |= qattn::kCausal;  // the band
   if (desc->atten_mask) mode |= qattn::kMask;
   if (desc->layout == QATTN_LAYOUT_TND) mode |= qattn::kVarlen;
-  if ((rc = finish_items(p, qattn::bf16_qblocks_per_tile(mode)))) return rc;
+  if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(mode)))) return rc;
   if (p.total_items == 0) return QATTN_OK;
-  return hip_status(qattn::launch_attn_bf16(p, mode, (hipStream_t)stream), "attn_fwd launch");
+  const hipError_t e = desc->dtype == QATTN_DTYPE_FP16 ? qattn::launch_attn_fwd_f16(p, mode, (hipStream_t)stream)
+                                                       : qattn::launch_attn_fwd_bf16(p, mode, (hipStream_t)stream);
+  return hip_status(e, "attn_fwd launch");
 }
 
 int build_kv_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32_t* counts, int32_t* idx,
@@ -272,9 +285,12 @@ int attn_fwd_blocksparse(const qattn_desc* desc, const qattn_bf16* q, const qatt
   p.l_out = softmax_sum;
   p.counts = counts;
   p.idx = idx;
-  if ((rc = finish_items(p, 1))) return rc;
+  if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(qattn::kSparse)))) return rc;
   if (p.total_items == 0) return QATTN_OK;
-  return hip_status(qattn::launch_attn_bf16(p, qattn::kSparse, (hipStream_t)stream), "attn_fwd_blocksparse launch");
+  const hipError_t e = desc->dtype == QATTN_DTYPE_FP16
+                           ? qattn::launch_attn_fwd_f16(p, qattn::kSparse, (hipStream_t)stream)
+                           : qattn::launch_attn_fwd_bf16(p, qattn::kSparse, (hipStream_t)stream);
+  return hip_status(e, "attn_fwd_blocksparse launch");
 }
 
 int quantize_qk_perblock_int8(const qattn_bf16* x, int B, int N, int S, int D, int8_t* x_q, float* scale,
@@ -317,6 +333,8 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
   int rc = setup_common(desc, p, false, false, &total_qb);
   if (rc) return rc;
   if (desc->layout != QATTN_LAYOUT_BNSD) return fail(QATTN_UNSUPPORTED, "attn_fwd_qbsa needs the BNSD layout");
+  if (desc->dtype != QATTN_DTYPE_BF16) return fail(QATTN_UNSUPPORTED, "attn_fwd_qbsa writes bf16 (dtype must be BF16)");
+  if (p.Dv != p.D) return fail(QATTN_UNSUPPORTED, "attn_fwd_qbsa needs Dv == D");
   const void* ptrs[] = {q, k, v, o};
   const char* names[] = {"q", "k", "v", "o"};
   if ((rc = check_ptrs(ptrs, names, 4))) return rc;

@@ -22,7 +22,7 @@ enum ModeBits : int {
 
 // Everything an attention launch needs, passed by value as the kernel argument.
 struct FwdParams {
-  // bf16 path
+  // 16-bit path (bf16 or fp16 bits)
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
@@ -44,9 +44,11 @@ struct FwdParams {
   // element strides: batch, head, token (the head dimension is contiguous)
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
   int64_t ml_sb, ml_sh, ml_ss;
   int64_t mask_sb, mask_sh, mask_ss;
-  int B, Nq, Nkv, group, Sq, Skv, D;
+  int B, Nq, Nkv, group, Sq, Skv, D, Dv;
   int h0, nh, qb0, qb1;  // head and q-block subrange
   int QB, KB;            // q-blocks and kv-blocks per sequence (BNSD)
   int qblocks_per_tile;  // q-blocks one workgroup covers
@@ -62,8 +64,12 @@ struct FwdParams {
   int cu_kv[kMaxSeqs + 1];
 };
 
-hipError_t launch_attn_bf16(const FwdParams& p, int mode, hipStream_t stream);
-int bf16_qblocks_per_tile(int mode);  // q-blocks per workgroup the bf16 kernel takes in `mode`
+hipError_t launch_attn_fwd_bf16(const FwdParams& p, int mode, hipStream_t stream);
+hipError_t launch_attn_fwd_f16(const FwdParams& p, int mode, hipStream_t stream);
+// q-blocks per workgroup of the 16-bit kernels in `mode` (the host sets qblocks_per_tile to
+// match): two consecutive q-blocks share the K/V tiles when both see the same keys (no causal
+// mask or band, no kept list); causal, band and block-sparse launches take one q-block each.
+inline int fwd_qblocks_per_tile(int mode) { return (mode & (kCausal | kSparse)) ? 1 : 2; }
 hipError_t launch_attn_qbsa(const FwdParams& p, hipStream_t stream);
 hipError_t launch_quant_qk(const uint16_t* x, int B, int N, int S, int D, int8_t* xq, float* scale,
                            hipStream_t stream);

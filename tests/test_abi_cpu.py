@@ -68,7 +68,7 @@ def _desc(q, **kw):
     d.struct_size = ctypes.sizeof(q.QattnDesc)
     base = dict(layout=0, B=1, Nq=4, Nkv=2, Sq=256, Skv=256, D=128, scale=0.1, sparse_mode=0, mask_kind=0,
                 head_begin=-1, head_end=-1, qblock_begin=-1, qblock_end=-1, pre_tokens=2147483647,
-                next_tokens=2147483647)
+                next_tokens=2147483647, dtype=0, Dv=0)
     base.update(kw)
     for k, v in base.items():
         setattr(d, k, v)
@@ -87,6 +87,8 @@ def _fwd(q, d, qp=FAKE, kp=FAKE, vp=FAKE, op=FAKE, m=0, l=0):
     (dict(layout=2, Nq=64, Nkv=64, Skv=1 << 20, Sq=128), 2),
     (dict(B=0), 1), (dict(Sq=-1), 1), (dict(Nkv=0), 1), (dict(head_begin=0, head_end=5), 1),
     (dict(head_begin=3, head_end=2), 1), (dict(qblock_begin=0, qblock_end=3), 1), (dict(qblock_begin=-2, qblock_end=1), 1),
+    (dict(dtype=2), 1), (dict(dtype=-1), 1), (dict(Dv=-64), 1), (dict(Dv=256), 1), (dict(D=64, Dv=128), 1),
+    (dict(Dv=32), 2), (dict(Dv=96), 2), (dict(D=64, Dv=32), 2),
 ])
 def test_invalid_descriptions(q, kw, status):
     assert _fwd(q, _desc(q, **kw)) == status
@@ -155,6 +157,9 @@ def test_blocksparse_and_qbsa_validation(q):
                              None, None, None) == 2
     for lay in (2, 3):  # BSND and SBH are bf16-only layouts
         assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, layout=lay)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, None, None, None) == 2
+    for kw in (dict(dtype=1), dict(Dv=64)):  # the quantised path writes bf16 and needs Dv = D
+        assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, **kw)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  FAKE, None, None, None) == 2
     assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                              None, None, None) == 1

@@ -1,0 +1,166 @@
+"""GPU parity of the 16-bit attention forward with float16 inputs and with a value head dimension
+smaller than the query/key one (fused attention guide, section 4.1: float16 or bfloat16 inputs of
+one type, D_q = D_k >= D_v), against the float64 oracle, element by element.
+
+Tolerances: O max-abs <= 1e-2 for both input types (the bound stated for the 16-bit path), and the
+float16 cases must in addition stay within 4e-3. That tighter bound: the output is rounded to
+float16 (half an ulp is 2^-11 |O|, below 2e-3 for |O| < 4, the range of these N(0, 1) inputs) and
+P is rounded to float16 before P.V (relative 2^-11 per term, which averages out over the keys);
+a kernel rounding anything to bfloat16 (2^-8) would exceed it. softmax max/sum relative <= 1e-3.
+Subrange launches of both variants are compared with the full call bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import O_TOL_BF16, banner, check_ml, check_o, dev_bf16, f64, to_np
+from workloads import make_block_keep, random_bf16, random_f16
+
+pytestmark = pytest.mark.gpu
+
+O_TOL_F16 = 4e-3
+
+
+@pytest.fixture(scope="module")
+def qa():
+    import quantized_attention_tiled_amd as qa
+    qa.load()
+    return qa
+
+
+def _inputs(dtype, seed, q_shape, k_shape, v_shape):
+    """Device tensors of the given type and their float64 values for the oracle."""
+    out = []
+    for i, shape in enumerate((q_shape, k_shape, v_shape)):
+        if dtype == "fp16":
+            x = random_f16(seed + i, shape)
+            out.append((torch.from_numpy(x).cuda(), x.astype(np.float64)))
+        else:
+            bits = random_bf16(seed + i, shape)
+            out.append((dev_bf16(bits), f64(bits)))
+    return out
+
+
+def _check(dtype, o, m, l, ro, rm, rl, what=""):
+    assert o.dtype == (torch.float16 if dtype == "fp16" else torch.bfloat16)
+    og = o.float().cpu().numpy().astype(np.float64)
+    err = check_o(og, ro, O_TOL_F16 if dtype == "fp16" else O_TOL_BF16, what)
+    banner(f"{what}: O max-abs err {err:.3e}")
+    check_ml(to_np(m), to_np(l), rm, rl, what=what)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("B,Nq,Nkv,Sq,Skv,D,Dv,mode", [
+    (1, 2, 2, 256, 256, 64, 64, 0),
+    (2, 4, 2, 300, 300, 128, 128, 0),   # ragged tails, GQA 2
+    (1, 4, 1, 200, 333, 128, 64, 0),    # Dv < D, Sq != Skv, GQA 4
+    (2, 4, 2, 300, 300, 128, 64, 2),
+    (1, 2, 1, 200, 450, 128, 64, 3),
+    (1, 2, 2, 450, 200, 128, 128, 3),   # leading rows see no key
+    (1, 1, 1, 1, 1, 128, 64, 0),
+])
+def test_dense_and_causal(qa, dtype, B, Nq, Nkv, Sq, Skv, D, Dv, mode):
+    if dtype == "bf16" and Dv == D:
+        pytest.skip("bf16 with Dv = D is covered by test_gpu_attention")
+    what = f"{dtype} B={B} Nq={Nq} Nkv={Nkv} Sq={Sq} Skv={Skv} D={D} Dv={Dv} mode={mode}"
+    banner(what)
+    (q, qr), (k, kr), (v, vr) = _inputs(dtype, 300 + Sq + D + Dv + mode, (B, Nq, Sq, D), (B, Nkv, Skv, D),
+                                        (B, Nkv, Skv, Dv))
+    scale = 1.0 / np.sqrt(D)
+    o, m, l = qa.attn_fwd(q, k, v, scale=scale, sparse_mode=mode)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (B, Nq, Sq, Dv)
+    ro, rm, rl = oracle.attention(qr, kr, vr, scale, sparse_mode=mode)
+    _check(dtype, o, m, l, ro, rm, rl, what)
+
+
+@pytest.mark.parametrize("dtype,Dv", [("fp16", 128), ("fp16", 64), ("bf16", 64)])
+def test_mask_and_band(qa, dtype, Dv):
+    B, Nq, Nkv, Sq, Skv, D = 2, 4, 2, 200, 260, 128
+    what = f"{dtype} mask+band Dv={Dv}"
+    banner(what)
+    (q, qr), (k, kr), (v, vr) = _inputs(dtype, 31, (B, Nq, Sq, D), (B, Nkv, Skv, D), (B, Nkv, Skv, Dv))
+    mask = (np.random.default_rng(8).random((B, 1, Sq, Skv)) < 0.3).astype(np.uint8)
+    mask[..., 9, :] = 1
+    o, m, l = qa.attn_fwd(q, k, v, scale=0.09, atten_mask=torch.from_numpy(mask).cuda(), pre_tokens=70,
+                          next_tokens=20)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(qr, kr, vr, 0.09, atten_mask=mask, pre_tokens=70, next_tokens=20)
+    _check(dtype, o, m, l, ro, rm, rl, what)
+
+
+@pytest.mark.parametrize("dtype,Dv,mode", [("fp16", 128, 0), ("fp16", 64, 3), ("bf16", 64, 2)])
+def test_tnd(qa, dtype, Dv, mode):
+    lens_q, lens_kv = [300, 1, 129, 64], [280, 40, 129, 500]
+    cq = np.concatenate([[0], np.cumsum(lens_q)])
+    ck = np.concatenate([[0], np.cumsum(lens_kv)])
+    Nq, Nkv, D = 4, 2, 128
+    what = f"{dtype} TND Dv={Dv} mode={mode}"
+    banner(what)
+    (q, qr), (k, kr), (v, vr) = _inputs(dtype, 41, (cq[-1], Nq, D), (ck[-1], Nkv, D), (ck[-1], Nkv, Dv))
+    o, m, l = qa.attn_fwd(q, k, v, scale=0.088, layout="TND", sparse_mode=mode, cu_seqlens_q=cq.tolist(),
+                          cu_seqlens_kv=ck.tolist())
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (cq[-1], Nq, Dv)
+    ro, rm, rl = oracle.attention(qr, kr, vr, 0.088, layout="TND", sparse_mode=mode, cu_seqlens_q=cq,
+                                  cu_seqlens_kv=ck)
+    _check(dtype, o, m, l, ro, rm, rl, what)
+
+
+@pytest.mark.parametrize("dtype,Dv,layout", [("fp16", 128, "BNSD"), ("fp16", 64, "BSND"), ("bf16", 64, "BNSD")])
+def test_blocksparse(qa, dtype, Dv, layout):
+    B, Nq, Nkv, S, D = 1, 4, 2, 640, 128
+    QB = KB = (S + 127) // 128
+    what = f"{dtype} block-sparse Dv={Dv} {layout}"
+    banner(what)
+    (q, qr), (k, kr), (v, vr) = _inputs(dtype, 51, (B, Nq, S, D), (B, Nkv, S, D), (B, Nkv, S, Dv))
+    keep = make_block_keep(61, B, Nq, QB, KB, 0.4)
+    counts, idx = qa.build_kv_block_list(torch.from_numpy(keep).cuda())
+    if layout == "BSND":
+        o, m, l = qa.attn_fwd_blocksparse(q.transpose(1, 2).contiguous(), k.transpose(1, 2).contiguous(),
+                                          v.transpose(1, 2).contiguous(), counts, idx, scale=0.088, layout="BSND")
+        o = o.transpose(1, 2)
+    else:
+        o, m, l = qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=0.088)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(qr, kr, vr, 0.088, block_keep=keep)
+    _check(dtype, o, m, l, ro, rm, rl, what)
+
+
+@pytest.mark.parametrize("layout", ["BSH", "SBH"])
+def test_3d_layouts_with_dv(qa, layout):
+    """BSH / SBH carry Dv in v's hidden size: H_v = Nkv * Dv."""
+    B, Nq, Nkv, S, D, Dv = 2, 4, 2, 260, 128, 64
+    banner(f"fp16 {layout} Dv={Dv}")
+    (q, qr), (k, kr), (v, vr) = _inputs("fp16", 71, (B, Nq, S, D), (B, Nkv, S, D), (B, Nkv, S, Dv))
+    ref = qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=2)
+
+    def to3(x):  # BNSD -> BSH or SBH
+        x = x.permute(0, 2, 1, 3) if layout == "BSH" else x.permute(2, 0, 1, 3)
+        return x.reshape(x.shape[0], x.shape[1], -1).contiguous()
+
+    o, m, l = qa.attn_fwd(to3(q), to3(k), to3(v), scale=0.1, sparse_mode=2, layout=layout, head_num=Nq)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), to3(ref[0]).view(torch.int16))
+    assert torch.equal(m, ref[1]) and torch.equal(l, ref[2])
+
+
+@pytest.mark.parametrize("dtype,Dv,mode", [("fp16", 128, 0), ("fp16", 64, 3), ("bf16", 64, 0)])
+def test_subranges_bitexact(qa, dtype, Dv, mode):
+    B, Nq, Nkv, S, D = 1, 4, 2, 700, 128
+    banner(f"subranges {dtype} Dv={Dv} mode={mode}")
+    (q, _), (k, _), (v, _) = _inputs(dtype, 81, (B, Nq, S, D), (B, Nkv, S, D), (B, Nkv, S, Dv))
+    full = qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode)
+    nqb = (S + 127) // 128
+    for split in ([((h, h + 1), (0, nqb)) for h in range(Nq)], [((0, Nq), (i, i + 1)) for i in range(nqb)],
+                  [((0, 2), (0, 3)), ((0, 2), (3, nqb)), ((2, Nq), (0, 1)), ((2, Nq), (1, nqb))]):
+        out = tuple(torch.zeros_like(x) for x in full)
+        for hr, br in split:
+            qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, head_range=hr, qblock_range=br, out=out[0],
+                        softmax_max=out[1], softmax_sum=out[2])
+        torch.cuda.synchronize()
+        assert torch.equal(full[0].view(torch.int16), out[0].view(torch.int16))
+        assert torch.equal(full[1].view(torch.int32), out[1].view(torch.int32))
+        assert torch.equal(full[2].view(torch.int32), out[2].view(torch.int32))

@@ -2,12 +2,13 @@
 cross-compiles here; no GPU needed).
 
 * No kernel keeps data in private (scratch) memory, except the boolean-mask instantiations of the
-  bf16 kernel, whose per-element mask loads spill a few dozen registers. Scratch use elsewhere has
+  16-bit kernel, whose per-element mask loads spill a few dozen registers. Scratch use elsewhere has
   meant an outlined lambda that demoted the kernel arguments and register arrays to memory.
 * Both attention kernels run two waves per SIMD (at most 256 VGPRs) with at most 80 KiB of LDS
   per workgroup, so that two workgroups share a CU.
 """
 
+import functools
 import os
 import re
 import shutil
@@ -23,10 +24,12 @@ pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.ex
 MASK_MODES = {2, 3}  # kMask, kCausal | kMask
 
 
-def _resources(src):
-    cmd = [B.hipcc(), f"--offload-arch={B.ARCH}", "-O3", "-std=c++17", "-c", "--cuda-device-only",
+@functools.lru_cache(maxsize=None)
+def _compile(src):
+    """Device assembly and per-kernel resource report of one source (one hipcc run)."""
+    cmd = [B.hipcc(), f"--offload-arch={B.ARCH}", "-O3", "-std=c++17", "-S", "--cuda-device-only",
            f"-I{B.INCLUDE}", f"-I{B.CSRC}", *B.DEVICE_FLAGS, *B.SOURCE_FLAGS.get(src, []),
-           os.path.join(B.CSRC, src), "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+           os.path.join(B.CSRC, src), "-o", "-", "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     kernels = {}
@@ -39,28 +42,46 @@ def _resources(src):
         m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
         if m and cur is not None:
             cur[m.group(1).strip()] = int(m.group(2))
-    return kernels
+    return kernels, r.stdout
 
 
-@pytest.fixture(scope="module")
-def bf16():
-    return _resources("attn_bf16.hip")
+def _resources(src):
+    return _compile(src)[0]
 
 
-def test_bf16_kernels_use_no_scratch(bf16):
-    assert bf16, "no kernels reported"
-    for name, res in bf16.items():
-        m = re.search(r"attn_bf16_kernelILi(\d+)ELi(\d+)ELi(\d+)EEE", name)
+FWD_SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f16.hip"]
+# element type, D, Dv, mode, q-blocks per workgroup
+FWD_NAME = re.compile(r"attn_fwd_kernelI(DF16b|DF16_)Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEE")
+
+
+@pytest.fixture(scope="module", params=FWD_SOURCES)
+def fwd(request):
+    return _resources(request.param)
+
+
+def test_fwd_instantiations(fwd):
+    """Each element type gets every (D, Dv) pair in all seven modes."""
+    shapes = set()
+    for name in fwd:
+        m = FWD_NAME.search(name)
         assert m, name
-        mode = int(m.group(2))
+        shapes.add((int(m.group(2)), int(m.group(3)), int(m.group(4))))
+    assert shapes == {(d, dv, mode) for d, dv in [(64, 64), (128, 128), (128, 64)] for mode in [0, 1, 2, 3, 4, 8, 9]}
+    assert len({FWD_NAME.search(n).group(1) for n in fwd}) == 1
+
+
+def test_fwd_kernels_use_no_scratch(fwd):
+    assert fwd, "no kernels reported"
+    for name, res in fwd.items():
+        mode = int(FWD_NAME.search(name).group(4))
         if mode in MASK_MODES:
             continue
         assert res.get("ScratchSize", 0) == 0, (name, res)
         assert res.get("VGPRs Spill", 0) == 0, (name, res)
 
 
-def test_bf16_two_waves_per_simd_and_lds(bf16):
-    for name, res in bf16.items():
+def test_fwd_two_waves_per_simd_and_lds(fwd):
+    for name, res in fwd.items():
         assert res.get("Occupancy", 0) >= 2, (name, res)
         assert res.get("LDS Size", 0) <= 80 * 1024, (name, res)
 
@@ -91,15 +112,10 @@ def test_quant_kernels_use_no_scratch():
 
 
 def _asm(src):
-    cmd = [B.hipcc(), f"--offload-arch={B.ARCH}", "-O3", "-std=c++17", "-S", "--cuda-device-only",
-           f"-I{B.INCLUDE}", f"-I{B.CSRC}", *B.DEVICE_FLAGS, *B.SOURCE_FLAGS.get(src, []),
-           os.path.join(B.CSRC, src), "-o", "-"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    return r.stdout
+    return _compile(src)[1]
 
 
-@pytest.mark.parametrize("src", ["attn_bf16.hip", "attn_qbsa.hip"])
+@pytest.mark.parametrize("src", FWD_SOURCES + ["attn_qbsa.hip"])
 def test_m0_only_feeds_direct_lds_loads(src):
     """The direct HBM -> LDS loads set M0 in inline asm, where the compiler does not preserve it:
     no other instruction of these kernels may read or write M0."""

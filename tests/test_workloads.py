@@ -3,7 +3,7 @@
 import numpy as np
 import torch
 
-from workloads import CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, make_block_keep, make_workload
+from workloads import CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, make_block_keep, make_workload, random_f16
 
 
 def test_bf16_rounding_matches_torch():
@@ -15,6 +15,18 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(f32_to_bf16_bits(x), ref)
     np.testing.assert_array_equal(bf16_bits_to_f32(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16)
                                   .float().numpy())
+
+
+def test_f16_inputs_round_like_torch():
+    x = random_f16(5, (3, 200, 64), "block_offset")
+    assert x.dtype == np.float16
+    rng = np.random.default_rng(np.random.SeedSequence([5, 0]))
+    raw = rng.standard_normal((3, 200, 64), dtype=np.float32)
+    # the offsets move values, the rounding must still be torch's float -> half
+    np.testing.assert_array_equal(random_f16(5, (3, 200, 64), "normal"),
+                                  torch.from_numpy(raw).half().numpy())
+    assert 0.9 < float(np.std(x.astype(np.float64))) < 1.3
+    np.testing.assert_array_equal(x, random_f16(5, (3, 200, 64), "block_offset"))
 
 
 def test_deterministic_and_head_subsets():

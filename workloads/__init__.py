@@ -2,7 +2,7 @@
 
 This module is shared by the tests, the benchmark and the smoke check. It holds
 no attention or quantisation arithmetic: it only draws random numbers, rounds
-them once to bfloat16 (that rounding *is* the input definition) and builds the
+them once to bfloat16 or float16 (that rounding *is* the input definition) and builds the
 block masks and sequence lengths. Both the HIP path and the oracle consume the
 same bytes produced here.
 
@@ -19,5 +19,6 @@ from .synth import (  # noqa: F401
     make_block_keep,
     make_workload,
     random_bf16,
+    random_f16,
     varlen_lengths,
 )

@@ -1,7 +1,7 @@
 """Synthetic workloads shaped like the pages' attention benchmarks.
 
 Recipes (all values drawn in float32 and rounded once, to nearest-even, to
-bfloat16):
+bfloat16, or to float16 for the float16 inputs):
 
 * ``normal``        x ~ N(0, 1)
 * ``block_offset``  x ~ N(0, 1) + o[blk, d], o ~ N(0, 0.5^2), one offset vector
@@ -84,6 +84,21 @@ def random_bf16(seed: int, shape, recipe: str = "normal") -> np.ndarray:
     elif recipe != "normal":
         raise ValueError(f"unknown recipe {recipe}")
     return f32_to_bf16_bits(x)
+
+
+def random_f16(seed: int, shape, recipe: str = "normal") -> np.ndarray:
+    """float16 values of an arbitrary-shape tensor (the recipes of ``random_bf16``, drawn in
+    float32 from the same seed and rounded once, to nearest-even, to IEEE binary16)."""
+    shape = tuple(int(s) for s in shape)
+    x = _rng(seed, 0).standard_normal(shape, dtype=np.float32)
+    if recipe == "block_offset":
+        S = shape[-2]
+        nblk = (S + BLOCK - 1) // BLOCK
+        off = _rng(seed, _T_OFF).standard_normal(shape[:-2] + (nblk, shape[-1]), dtype=np.float32) * np.float32(0.5)
+        x += np.repeat(off, BLOCK, axis=-2)[..., :S, :]
+    elif recipe != "normal":
+        raise ValueError(f"unknown recipe {recipe}")
+    return x.astype(np.float16)
 
 
 def make_block_keep(base: int, B: int, N: int, QB: int, KB: int, p_keep: float,
