@@ -13,6 +13,8 @@ Definition followed ("Ascend NPU fused attention operator" guide):
     lengths (TND layout, section 4.1).
   * section 5: outputs are the attention result plus the softmax max and sum.
   * section 7: GQA requires Nq / Nkv to be an integer.
+  * EagleQBSA article, API call: per-batch ``actual_seq_lengths`` /
+    ``actual_seq_lengths_kv`` beside a padded BNSD tensor.
 
 Readings where the guide is silent (each stated once here):
   * causal top-left keeps j <= i, bottom-right keeps j <= i + Skv - Sq, with i
@@ -25,7 +27,11 @@ Readings where the guide is silent (each stated once here):
     has O = 0, m = -inf, l = 0;
   * q-head h reads kv-head h // (Nq / Nkv) (contiguous groups);
   * block keep masks use 1 = keep on 128 x 128 blocks;
-  * m and l are laid out [B, Nq, Sq] for BNSD and [Nq, T] for TND.
+  * m and l are laid out [B, Nq, Sq] for BNSD and [Nq, T] for TND;
+  * with actual lengths (aq_b, akv_b), batch b is the sequence of its first
+    aq_b queries and akv_b keys (masks, causal anchors and the band counted
+    inside it); its padded rows aq_b .. Sq - 1 are rows with no key (O = 0,
+    m = -inf, l = 0).
 
 Scores are formed 128 query rows at a time so long sequences fit in memory;
 each slab is the plain definition on those rows.
@@ -128,7 +134,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, *, layo
               sparse_mode: int = 0, atten_mask: Optional[np.ndarray] = None,
               cu_seqlens_q: Optional[np.ndarray] = None, cu_seqlens_kv: Optional[np.ndarray] = None,
               block_keep: Optional[np.ndarray] = None, pre_tokens: Optional[int] = None,
-              next_tokens: Optional[int] = None):
+              next_tokens: Optional[int] = None, actual_seq_q: Optional[Sequence[int]] = None,
+              actual_seq_kv: Optional[Sequence[int]] = None):
     """Attention forward over a whole problem.
 
     BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D] -> o [B, Nq, Sq, D], m/l [B, Nq, Sq].
@@ -137,6 +144,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, *, layo
     ``atten_mask``: uint8, 1 = masked, [Sq, Skv] / [B, 1, Sq, Skv] / [B, Nq, Sq, Skv] (BNSD).
     ``block_keep``: uint8 [B, Nq, QB, KB], 1 = keep (BNSD).
     ``pre_tokens`` / ``next_tokens``: the sparse_mode 0 band (None = no limit).
+    ``actual_seq_q`` / ``actual_seq_kv`` (BNSD): per-batch valid lengths (None = Sq / Skv).
     """
     band = (pre_tokens, next_tokens)
     if layout == "BNSD":
@@ -145,18 +153,28 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, *, layo
         if Nq % Nkv:
             raise ValueError("Nq must be a multiple of Nkv")
         g = Nq // Nkv
+        Skv = k.shape[2]
+        aq = [Sq] * B if actual_seq_q is None else [int(x) for x in actual_seq_q]
+        akv = [Skv] * B if actual_seq_kv is None else [int(x) for x in actual_seq_kv]
+        if len(aq) != B or len(akv) != B or not all(0 <= a <= Sq for a in aq) or \
+                not all(0 <= a <= Skv for a in akv):
+            raise ValueError("actual lengths must be B values within [0, Sq] and [0, Skv]")
         o = np.zeros(q.shape[:3] + (v.shape[3],))
-        m = np.zeros((B, Nq, Sq))
+        m = np.full((B, Nq, Sq), -np.inf)
         l = np.zeros((B, Nq, Sq))
         for b in range(B):
+            lq, lk = aq[b], akv[b]
             for h in range(Nq):
                 keep = None if block_keep is None else block_keep[b, h]
-                o[b, h], m[b, h], l[b, h] = _head(q[b, h], k[b, h // g], v[b, h // g], scale, sparse_mode,
-                                                  _mask_for_head(atten_mask, b, h), keep, band)
+                mask = _mask_for_head(atten_mask, b, h)
+                mask = None if mask is None else mask[:lq, :lk]
+                o[b, h, :lq], m[b, h, :lq], l[b, h, :lq] = _head(q[b, h, :lq], k[b, h // g, :lk], v[b, h // g, :lk],
+                                                                 scale, sparse_mode, mask, keep, band)
         return o, m, l
     if layout == "TND":
-        if atten_mask is not None or block_keep is not None:
-            raise ValueError("TND supports causal masks only")
+        if atten_mask is not None or block_keep is not None or actual_seq_q is not None or \
+                actual_seq_kv is not None:
+            raise ValueError("TND supports causal masks and the band only")
         T, Nq, D = q.shape
         Nkv = k.shape[1]
         if Nq % Nkv:

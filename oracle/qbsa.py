@@ -77,24 +77,33 @@ def qbsa_qblock(qc: np.ndarray, kc: np.ndarray, vc: np.ndarray, sq: float, sk: n
 
 
 def qbsa_attention(qc, kc, vc, q_scale, k_scale, v_scale, keep, scale,
-                   qblocks: Optional[Sequence[tuple]] = None, *, round_p: bool = True):
+                   qblocks: Optional[Sequence[tuple]] = None, *, round_p: bool = True,
+                   actual_seq_q: Optional[Sequence[int]] = None, actual_seq_kv: Optional[Sequence[int]] = None):
     """QBSA over BNSD inputs.
 
     qc [B, Nq, S, D] int8, kc/vc [B, Nkv, S, D], q_scale [B, Nq, QB],
     k_scale [B, Nkv, KB], v_scale [B, Nkv, D], keep [B, Nq, QB, KB] (1 = keep).
     ``qblocks``: optional list of (b, h, qb) to compute; default all.
-    Returns a dict {(b, h, qb): (o, m, l)}.
+    ``actual_seq_q`` / ``actual_seq_kv`` (the API call's actual_seq_lengths and
+    actual_seq_lengths_kv): batch b uses only its first aq_b query rows and akv_b
+    keys; kept blocks past its keys hold no key. The scales stay those of the
+    padded tensors (the quantisers see the whole buffers).
+    Returns a dict {(b, h, qb): (o, m, l)} with the rows of q-block qb below aq_b
+    (possibly none).
     """
     B, Nq, S, D = qc.shape
+    Skv = kc.shape[2]
     g = Nq // kc.shape[1]
     QB = (S + BLOCK - 1) // BLOCK
+    aq = [S] * B if actual_seq_q is None else [int(x) for x in actual_seq_q]
+    akv = [Skv] * B if actual_seq_kv is None else [int(x) for x in actual_seq_kv]
     if qblocks is None:
         qblocks = [(b, h, qb) for b in range(B) for h in range(Nq) for qb in range(QB)]
     out = {}
     for (b, h, qb) in qblocks:
-        kept = np.nonzero(keep[b, h, qb])[0]
-        out[(b, h, qb)] = qbsa_qblock(qc[b, h], kc[b, h // g], vc[b, h // g], q_scale[b, h, qb],
-                                      k_scale[b, h // g], v_scale[b, h // g], scale, kept, qb,
+        kept = [kb for kb in np.nonzero(keep[b, h, qb])[0] if kb * BLOCK < akv[b]]
+        out[(b, h, qb)] = qbsa_qblock(qc[b, h, :aq[b]], kc[b, h // g, :akv[b]], vc[b, h // g, :akv[b]],
+                                      q_scale[b, h, qb], k_scale[b, h // g], v_scale[b, h // g], scale, kept, qb,
                                       round_p=round_p)
     return out
 

@@ -285,3 +285,52 @@ def test_band_with_defaults_equals_unmasked_and_rejects_causal():
         np.testing.assert_array_equal(x, y)
     with pytest.raises(ValueError):
         attention(q, k, v, 0.5, sparse_mode=2, pre_tokens=4)
+
+
+def test_actual_lengths_brute_force_with_padding():
+    """Per-batch actual lengths (EagleQBSA API call): padded keys get no weight even when they
+    would score highest, and padded rows come out empty; scalar brute force on the valid part."""
+    B, Nq, Sq, Skv, D = 3, 2, 9, 11, 3
+    q, k, v = RNG.normal(size=(B, Nq, Sq, D)), RNG.normal(size=(B, Nq, Skv, D)), RNG.normal(size=(B, Nq, Skv, D))
+    aq, akv = [9, 4, 0], [6, 11, 3]
+    for b in range(B):  # padding that would dominate the softmax if it were read
+        k[b, :, akv[b]:] = 50.0 * q[b, :, :1]
+        v[b, :, akv[b]:] = 1e3
+    for mode in (0, 2, 3):
+        o, m, l = attention(q, k, v, 0.6, sparse_mode=mode, actual_seq_q=aq, actual_seq_kv=akv)
+        for b in range(B):
+            off = akv[b] - aq[b] if mode == 3 else 0
+            for h in range(Nq):
+                keep = (lambda i, j: True) if mode == 0 else (lambda i, j, off=off: j <= i + off)
+                bo, bm, bl = _brute(q[b, h, :aq[b]], k[b, h, :akv[b]], v[b, h, :akv[b]], 0.6, keep)
+                np.testing.assert_allclose(o[b, h, :aq[b]], bo, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(l[b, h, :aq[b]], bl, rtol=1e-12)
+                np.testing.assert_array_equal(np.isneginf(m[b, h, :aq[b]]), np.isneginf(bm))
+                assert np.all(o[b, h, aq[b]:] == 0) and np.all(np.isneginf(m[b, h, aq[b]:]))
+                assert np.all(l[b, h, aq[b]:] == 0)
+
+
+def test_actual_lengths_equal_tnd_and_full_lengths():
+    """Padded BNSD with actual lengths equals TND over the same sequences (bottom-right causal
+    and the band anchored inside each sequence); full actual lengths change nothing."""
+    lq, lk = [5, 130, 64], [7, 100, 64]
+    Nq, Nkv, D, S, Skv = 2, 1, 4, 140, 120
+    q, k, v = RNG.normal(size=(3, Nq, S, D)), RNG.normal(size=(3, Nkv, Skv, D)), RNG.normal(size=(3, Nkv, Skv, D))
+    cuq = np.concatenate([[0], np.cumsum(lq)])
+    cuk = np.concatenate([[0], np.cumsum(lk)])
+    qt = np.concatenate([q[b, :, :lq[b]].transpose(1, 0, 2) for b in range(3)])
+    kt = np.concatenate([k[b, :, :lk[b]].transpose(1, 0, 2) for b in range(3)])
+    vt = np.concatenate([v[b, :, :lk[b]].transpose(1, 0, 2) for b in range(3)])
+    for kw in (dict(sparse_mode=3), dict(sparse_mode=2), dict(pre_tokens=9, next_tokens=-2)):
+        o, m, l = attention(q, k, v, 0.5, actual_seq_q=lq, actual_seq_kv=lk, **kw)
+        ot, mt, lt = attention(qt, kt, vt, 0.5, layout="TND", cu_seqlens_q=cuq, cu_seqlens_kv=cuk, **kw)
+        for b in range(3):
+            np.testing.assert_array_equal(o[b, :, :lq[b]], ot[cuq[b]:cuq[b + 1]].transpose(1, 0, 2))
+            np.testing.assert_array_equal(m[b, :, :lq[b]], mt[:, cuq[b]:cuq[b + 1]])
+            np.testing.assert_array_equal(l[b, :, :lq[b]], lt[:, cuq[b]:cuq[b + 1]])
+    full = attention(q, k, v, 0.5, sparse_mode=3)
+    same = attention(q, k, v, 0.5, sparse_mode=3, actual_seq_q=[S] * 3, actual_seq_kv=[Skv] * 3)
+    for x, y in zip(full, same):
+        np.testing.assert_array_equal(x, y)
+    with pytest.raises(ValueError):
+        attention(q, k, v, 0.5, actual_seq_q=[S + 1, 1, 1])

@@ -119,3 +119,33 @@ def test_qbsa_uses_kept_list_order():
     q, k, v, keep = _problem(S=256, D=8, N=1, p=1.0)
     counts, idx = kept_block_list(keep)
     assert counts[0, 0, 0] == 2 and list(idx[0, 0, 0]) == [0, 1]
+
+
+def test_actual_lengths_skip_padded_keys_and_rows():
+    """QBSA with actual lengths: padded key codes that would dominate the softmax get no weight
+    (the result equals the same codes cut to the valid keys), padded q-blocks are empty, and a
+    kept block wholly past the valid keys contributes nothing."""
+    q, k, v, keep = _problem(S=384, D=8, N=2, p=1.0)
+    qc, qs = quantize_qk_perblock_int8(q)
+    kc, ks = quantize_qk_perblock_int8(k)
+    vc, vs = quantize_v_perchannel_fp8(v)
+    akv, aq = 200, 250
+    kc = kc.copy()
+    kc[:, :, akv:] = 127 * np.sign(qc[:, :, :1]).astype(np.int8)  # aligned with query row 0
+    out = qbsa_attention(qc, kc, vc, qs, ks, vs, keep, 0.3, actual_seq_q=[aq], actual_seq_kv=[akv])
+    for h in range(2):
+        for qb in range(3):
+            o, m, l = out[(0, h, qb)]
+            rows = max(0, min(aq, 128 * qb + 128) - 128 * qb)
+            assert o.shape[0] == rows
+            if rows == 0:
+                continue
+            ro, rm, rl = qbsa_qblock(qc[0, h, :aq], kc[0, h, :akv], vc[0, h, :akv], qs[0, h, qb], ks[0, h], vs[0, h],
+                                     0.3, [0, 1], qb)
+            np.testing.assert_array_equal(o, ro)
+            np.testing.assert_array_equal(l, rl)
+            # and against the plain (non-tiled) form on the valid keys only
+            po, pm, pl = qbsa_plain_rows(qc[0, h, :aq], kc[0, h, :akv], vc[0, h, :akv], qs[0, h, qb], ks[0, h],
+                                         vs[0, h], 0.3, [0, 1], qb)
+            np.testing.assert_allclose(l, pl, rtol=1e-12)
+            np.testing.assert_allclose(m, pm, rtol=1e-12)
