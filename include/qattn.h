@@ -25,8 +25,8 @@
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller. The library
  *     allocates nothing, keeps no state between calls and keeps no pointer
- *     after it returns. cu_seqlens arrays are HOST pointers, read during the
- *     call only.
+ *     after it returns. cu_seqlens and actual_seq_lengths arrays are HOST
+ *     pointers, read during the call only.
  *   - Every call is asynchronous on the caller's HIP stream (`stream` is a
  *     hipStream_t; NULL means the default stream). Buffers must stay alive
  *     until the stream has passed the call.
@@ -72,6 +72,12 @@
  *     l_i = sum over kept j of exp(s_ij - m_i). A row with no kept key gets
  *     O = 0, m = -inf, l = 0.
  *   - q-head h reads kv-head h / (Nq / Nkv).
+ *   - actual_seq_lengths / actual_seq_lengths_kv (EagleQBSA article, API call;
+ *     BNSD, BSND and SBH; at most QATTN_MAX_SEQS batches): batch b is the
+ *     sequence of its first aq_b query rows and akv_b keys of the padded
+ *     tensors; masks, causal anchors (Skv - Sq becomes akv_b - aq_b) and the
+ *     band are counted inside it. Its rows aq_b .. Sq - 1 are written as rows
+ *     with no key. q-blocks stay those of the padded Sq.
  *   - block keep masks use 1 = keep (the opposite of atten_mask).
  *   - scale must be finite and > 0.
  */
@@ -133,6 +139,8 @@ typedef struct qattn_desc {
                                    quantised entry point takes BF16 only */
   int32_t Dv;                   /* value / output head dimension; 0 means D. Supported: Dv = D, or
                                    D = 128 with Dv = 64; the quantised entry point needs Dv = D */
+  const int32_t* actual_seq_lengths;    /* not TND: host [B] valid query rows per batch, or NULL (= Sq) */
+  const int32_t* actual_seq_lengths_kv; /* not TND: host [B] valid keys per batch, or NULL (= Skv) */
 } qattn_desc;
 
 /*

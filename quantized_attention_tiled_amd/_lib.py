@@ -65,6 +65,8 @@ class QattnDesc(ctypes.Structure):
         ("next_tokens", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("Dv", ctypes.c_int32),
+        ("actual_seq_lengths", ctypes.POINTER(ctypes.c_int32)),
+        ("actual_seq_lengths_kv", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 

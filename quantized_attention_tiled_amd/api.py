@@ -60,7 +60,8 @@ def _ranges(head_range, qblock_range):
 def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: int, scale: float,
               sparse_mode: int = 0, cu_q=None, cu_kv=None, atten_mask: Optional[torch.Tensor] = None,
               mask_kind: int = MASK_SS, head_range=None, qblock_range=None, pre_tokens: int = NO_LIMIT,
-              next_tokens: int = NO_LIMIT, dtype: int = DTYPE_BF16, Dv: int = 0) -> QattnDesc:
+              next_tokens: int = NO_LIMIT, dtype: int = DTYPE_BF16, Dv: int = 0, actual_q=None,
+              actual_kv=None) -> QattnDesc:
     d = QattnDesc()
     d.struct_size = ctypes.sizeof(QattnDesc)
     d.layout, d.B, d.Nq, d.Nkv, d.Sq, d.Skv, d.D = layout, B, Nq, Nkv, Sq, Skv, D
@@ -73,6 +74,8 @@ def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: i
     (d.head_begin, d.head_end), (d.qblock_begin, d.qblock_end) = _ranges(head_range, qblock_range)
     d.pre_tokens, d.next_tokens = int(pre_tokens), int(next_tokens)
     d.dtype, d.Dv = int(dtype), int(Dv)
+    d.actual_seq_lengths = ctypes.cast(actual_q, ctypes.POINTER(ctypes.c_int32)) if actual_q is not None else None
+    d.actual_seq_lengths_kv = ctypes.cast(actual_kv, ctypes.POINTER(ctypes.c_int32)) if actual_kv is not None else None
     return d
 
 
@@ -152,7 +155,9 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
              head_range: Optional[Tuple[int, int]] = None, qblock_range: Optional[Tuple[int, int]] = None,
              out: Optional[torch.Tensor] = None, softmax_max: Optional[torch.Tensor] = None,
              softmax_sum: Optional[torch.Tensor] = None, head_num: Optional[int] = None,
-             pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT):
+             pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT,
+             actual_seq_lengths: Optional[Sequence[int]] = None,
+             actual_seq_lengths_kv: Optional[Sequence[int]] = None):
     """Dense attention forward on bfloat16 or float16 q, k, v (one type); returns (out,
     softmax_max, softmax_sum), out in that type.
 
@@ -163,6 +168,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (not with TND).
     With sparse_mode 0, ``pre_tokens`` / ``next_tokens`` keep key j for query i when
     i - pre_tokens <= j <= i + next_tokens (2147483647 = no limit).
+    ``actual_seq_lengths`` / ``actual_seq_lengths_kv`` (not TND): per-batch valid query / key
+    lengths of padded tensors; padded rows come out as rows with no key.
     With a head or q-block range only that slice of the outputs is written.
     """
     lib = load()
@@ -199,9 +206,12 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
         _require(t, n, dt, dev)
     if out.shape != o_shape or tuple(softmax_max.shape) != ml_shape or tuple(softmax_sum.shape) != ml_shape:
         raise ValueError("output shapes do not match")
+    # host arrays, alive until the call returns
+    aq_arr, akv_arr = _cu(actual_seq_lengths), _cu(actual_seq_lengths_kv)
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, atten_mask=atten_mask, mask_kind=kind, head_range=head_range,
-                     qblock_range=qblock_range, pre_tokens=pre_tokens, next_tokens=next_tokens, dtype=dtype, Dv=Dv)
+                     qblock_range=qblock_range, pre_tokens=pre_tokens, next_tokens=next_tokens, dtype=dtype, Dv=Dv,
+                     actual_q=aq_arr, actual_kv=akv_arr)
     with torch.cuda.device(dev):
         check(lib.attn_fwd(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max), _vp(softmax_sum),
                            _stream(dev)))
@@ -231,7 +241,7 @@ def build_kv_block_list(keep: torch.Tensor, counts: Optional[torch.Tensor] = Non
 
 def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range=None, qblock_range=None,
                          out=None, softmax_max=None, softmax_sum=None, layout: str = "BNSD",
-                         head_num: Optional[int] = None):
+                         head_num: Optional[int] = None, actual_seq_lengths=None, actual_seq_lengths_kv=None):
     """Block-sparse attention over a kept-block list on bfloat16 or float16 q, k, v (BNSD, BSND,
     BSH or SBH, shapes and Dv as for attn_fwd); returns (out, m [B, Nq, Sq], l)."""
     lib = load()
@@ -251,8 +261,11 @@ def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range
         _require(t, n, dt, dev)
     if out.shape != o_shape:
         raise ValueError("output shape does not match")
+    # host arrays, alive until the call returns
+    aq_arr, akv_arr = _cu(actual_seq_lengths), _cu(actual_seq_lengths_kv)
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
-                     head_range=head_range, qblock_range=qblock_range, dtype=dtype, Dv=Dv)
+                     head_range=head_range, qblock_range=qblock_range, dtype=dtype, Dv=Dv,
+                     actual_q=aq_arr, actual_kv=akv_arr)
     with torch.cuda.device(dev):
         check(lib.attn_fwd_blocksparse(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max),
                                        _vp(softmax_sum), _vp(counts), _vp(idx), _stream(dev)))
@@ -295,8 +308,9 @@ def quantize_v_perchannel_fp8(v: torch.Tensor, v_q: Optional[torch.Tensor] = Non
 
 def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scale: float,
                   head_range=None, qblock_range=None, out=None, softmax_max=None, softmax_sum=None,
-                  return_softmax: bool = True):
-    """Quantised block-sparse attention (BNSD); returns (out, m, l) or (out, None, None)."""
+                  return_softmax: bool = True, actual_seq_lengths=None, actual_seq_lengths_kv=None):
+    """Quantised block-sparse attention (BNSD); returns (out, m, l) or (out, None, None).
+    ``actual_seq_lengths`` / ``actual_seq_lengths_kv``: per-batch valid lengths, as for attn_fwd."""
     lib = load()
     dev = q_q.device
     _require(q_q, "q_q", torch.int8, dev)
@@ -323,8 +337,10 @@ def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scal
             softmax_max = torch.empty((B, Nq, Sq), dtype=torch.float32, device=dev)
         if softmax_sum is None:
             softmax_sum = torch.empty((B, Nq, Sq), dtype=torch.float32, device=dev)
+    # host arrays, alive until the call returns
+    aq_arr, akv_arr = _cu(actual_seq_lengths), _cu(actual_seq_lengths_kv)
     desc = make_desc(layout=LAYOUT_BNSD, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
-                     head_range=head_range, qblock_range=qblock_range)
+                     head_range=head_range, qblock_range=qblock_range, actual_q=aq_arr, actual_kv=akv_arr)
     with torch.cuda.device(dev):
         check(lib.attn_fwd_qbsa(ctypes.byref(desc), _vp(q_q), _vp(k_q), _vp(v_q), _vp(q_scale), _vp(k_scale),
                                 _vp(v_scale), _vp(counts), _vp(idx), _vp(out), _vp(softmax_max), _vp(softmax_sum),

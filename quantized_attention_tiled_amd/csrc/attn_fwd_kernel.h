@@ -182,12 +182,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
     h = p.h0 + rem / p.tiles_per_head;
     qblk = p.qb0 + (rem % p.tiles_per_head) * NQB;
     nsub = min(NQB, p.qb1 - qblk);
-    Lq = p.Sq;
-    Lkv = p.Skv;
+    Lq = p.actual ? p.cu_q[b] : p.Sq;  // per-batch actual lengths of a padded batch
+    Lkv = p.actual ? p.cu_kv[b] : p.Skv;
   }
   const int g = h / p.group;
   const int row_begin = qblk * kBlock;
   const int row_end = min(row_begin + nsub * kBlock, Lq);
+  // rows this workgroup writes: its q-blocks' rows of the (padded) tensor; rows from row_end on
+  // are padding past a batch's actual length and come out as rows with no key
+  const int row_limit = (MODE & kVarlen) != 0 ? row_end : min(row_begin + nsub * kBlock, p.Sq);
 
   const uint16_t* qp = p.q + b * p.q_sb + h * p.q_sh + q_tok0 * p.q_ss;
   const uint16_t* kp = p.k + b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
   } else {
     ntiles = kv_end > t0 * kKT ? (kv_end - t0 * kKT + kKT - 1) / kKT : 0;
   }
+  if (row_end <= row_begin) ntiles = 0;  // every row is padding
   // key0 of tile i, or -1 when a kept-list entry is out of range (the tile contributes nothing)
   auto tile_key0 = [&](int i) __attribute__((always_inline)) -> int {
     if constexpr ((MODE & kSparse) != 0) {
@@ -654,7 +658,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
   // softmax_sum relative to the true row max
   const float lout = (mtrue == kNegInf) ? 0.f : lt * __builtin_amdgcn_exp2f(mref - mtrue);
   const int q = wrow0 + l32;
-  if (q < row_end) {
+  if (q < row_limit) {
+    const bool pad = q >= row_end;  // (its lane computed a copy of the last valid row)
     uint16_t* op = p.o + b * p.o_sb + h * p.o_sh + (q_tok0 + q) * p.o_ss;
 #pragma unroll
     for (int db = 0; db < DB; db++)
@@ -662,13 +667,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
       for (int g4 = 0; g4 < 4; g4++) {
         E v4[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) v4[e] = (E)(o[db][4 * g4 + e] * inv);
+        for (int e = 0; e < 4; e++) v4[e] = (E)(pad ? 0.f : o[db][4 * g4 + e] * inv);
         *(uint2*)(op + db * 32 + 8 * g4 + 4 * hl) = __builtin_bit_cast(uint2, v4);
       }
     if (hl == 0) {
       const int64_t mi = b * p.ml_sb + h * p.ml_sh + (q_tok0 + q) * p.ml_ss;
-      if (p.m_out) p.m_out[mi] = (mtrue == kNegInf) ? kNegInf : mtrue * kLn2;
-      if (p.l_out) p.l_out[mi] = lout;
+      if (p.m_out) p.m_out[mi] = (mtrue == kNegInf || pad) ? kNegInf : mtrue * kLn2;
+      if (p.l_out) p.l_out[mi] = pad ? 0.f : lout;
     }
   }
 }

@@ -140,8 +140,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
   const int h = p.h0 + rem / p.tiles_per_head;
   const int qb = p.qb0 + rem % p.tiles_per_head;
   const int g = h / p.group;
-  const int Lq = p.Sq, Lkv = p.Skv;
+  // per-batch actual lengths of a padded batch; rows from row_end to row_limit are padding and
+  // come out as rows with no key
+  const int Lq = p.actual ? p.cu_q[b] : p.Sq, Lkv = p.actual ? p.cu_kv[b] : p.Skv;
   const int row_end = min((qb + 1) * kBlock, Lq);
+  const int row_limit = min((qb + 1) * kBlock, p.Sq);
   const int wrow0 = qb * kBlock + wave * 32;
   const bool wave_active = wrow0 < row_end;
 
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
 
   const int64_t lrow_idx = ((int64_t)b * p.Nq + h) * p.QB + qb;
   const int32_t* list = p.idx + lrow_idx * p.KB;
-  const int ntiles = min(max(p.counts[lrow_idx], 0), p.KB);
+  const int ntiles = row_end > qb * kBlock ? min(max(p.counts[lrow_idx], 0), p.KB) : 0;
 
   // kept-list entries and key scales through vector buffer loads (index in the VGPR offset, so an
   // out-of-range index reads 0)
@@ -576,7 +579,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
   const float lt = pair_sum(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int q = wrow0 + l32;
-  if (q < row_end) {
+  if (q < row_limit) {
+    const bool pad = q >= row_end;
     uint16_t* op = p.o + b * p.o_sb + h * p.o_sh + (int64_t)q * p.o_ss;
     const float* vsc = p.v_scale + ((int64_t)b * p.Nkv + g) * D;
 #pragma unroll
@@ -586,16 +590,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
         const int d0 = db * 32 + 8 * g4 + 4 * hl;
         const float4 sv = *(const float4*)(vsc + d0);
         __bf16 v4[4];
-        v4[0] = (__bf16)(o[db][4 * g4 + 0] * sv.x * inv);
-        v4[1] = (__bf16)(o[db][4 * g4 + 1] * sv.y * inv);
-        v4[2] = (__bf16)(o[db][4 * g4 + 2] * sv.z * inv);
-        v4[3] = (__bf16)(o[db][4 * g4 + 3] * sv.w * inv);
+        v4[0] = (__bf16)(pad ? 0.f : o[db][4 * g4 + 0] * sv.x * inv);
+        v4[1] = (__bf16)(pad ? 0.f : o[db][4 * g4 + 1] * sv.y * inv);
+        v4[2] = (__bf16)(pad ? 0.f : o[db][4 * g4 + 2] * sv.z * inv);
+        v4[3] = (__bf16)(pad ? 0.f : o[db][4 * g4 + 3] * sv.w * inv);
         *(uint2*)(op + d0) = __builtin_bit_cast(uint2, v4);
       }
     if (hl == 0) {
       const int64_t mi = b * p.ml_sb + h * p.ml_sh + (int64_t)q * p.ml_ss;
-      if (p.m_out) p.m_out[mi] = (lt > 0.f) ? mrun * kLn2 : kNegInf;
-      if (p.l_out) p.l_out[mi] = lt;
+      if (p.m_out) p.m_out[mi] = (lt > 0.f && !pad) ? mrun * kLn2 : kNegInf;
+      if (p.l_out) p.l_out[mi] = pad ? 0.f : lt;
     }
   }
 }

@@ -104,6 +104,21 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
     p.KB = (d->Skv + qattn::kBlock - 1) / qattn::kBlock;
     p.nseq = 0;
     qblocks = p.QB;
+    // per-batch actual lengths of a padded batch (each array optional)
+    p.actual = d->actual_seq_lengths != nullptr || d->actual_seq_lengths_kv != nullptr;
+    if (p.actual) {
+      if (d->B > qattn::kMaxSeqs)
+        return fail(QATTN_UNSUPPORTED, "actual sequence lengths for %d batches (max %d)", d->B, qattn::kMaxSeqs);
+      for (int i = 0; i < d->B; i++) {
+        const int lq = d->actual_seq_lengths ? d->actual_seq_lengths[i] : d->Sq;
+        const int lk = d->actual_seq_lengths_kv ? d->actual_seq_lengths_kv[i] : d->Skv;
+        if (lq < 0 || lq > d->Sq || lk < 0 || lk > d->Skv)
+          return fail(QATTN_INVALID_ARGUMENT, "actual lengths (%d, %d) of batch %d outside [0, Sq=%d] x [0, Skv=%d]", lq,
+                      lk, i, d->Sq, d->Skv);
+        p.cu_q[i] = lq;
+        p.cu_kv[i] = lk;
+      }
+    }
     if (d->atten_mask) {
       p.mask_ss = d->Skv;
       const int64_t ss = (int64_t)d->Sq * d->Skv;
@@ -111,6 +126,8 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
       p.mask_sb = d->mask_kind == QATTN_MASK_SS ? 0 : (d->mask_kind == QATTN_MASK_B1SS ? ss : ss * d->Nq);
     }
   } else {
+    if (d->actual_seq_lengths || d->actual_seq_lengths_kv)
+      return fail(QATTN_INVALID_ARGUMENT, "TND takes cu_seqlens, not actual_seq_lengths");
     if (d->B > qattn::kMaxSeqs) return fail(QATTN_UNSUPPORTED, "TND with %d sequences (max %d)", d->B, qattn::kMaxSeqs);
     if (!d->cu_seqlens_q || !d->cu_seqlens_kv) return fail(QATTN_INVALID_ARGUMENT, "TND needs cu_seqlens_q and cu_seqlens_kv");
     if (d->cu_seqlens_q[0] != 0 || d->cu_seqlens_kv[0] != 0)

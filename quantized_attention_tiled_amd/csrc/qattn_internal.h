@@ -60,6 +60,9 @@ struct FwdParams {
   int causal;   // 0 none or the sparse_mode 0 band, 2 top-left, 3 bottom-right
   int band_pre, band_next;  // causal-family key range i - band_pre <= j <= i + band_next (see the ABI)
   int nseq;
+  int actual;  // BNSD family: cu_q / cu_kv hold per-batch actual lengths instead of Sq / Skv
+  // TND: cumulative query / key lengths (nseq + 1 entries); BNSD family with `actual`: the valid
+  // query / key length of each batch (B entries)
   int cu_q[kMaxSeqs + 1];
   int cu_kv[kMaxSeqs + 1];
 };

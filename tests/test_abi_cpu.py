@@ -140,6 +140,35 @@ def test_tnd_validation(q):
     assert lib.attn_fwd(ctypes.byref(d2), FAKE, FAKE, FAKE, FAKE, None, None, None) == 2
 
 
+def test_actual_lengths_validation(q):
+    lib = q.load()
+
+    def call(aq, akv, **kw):
+        d = _desc(q, B=2, **kw)
+        keep = []
+        if aq is not None:
+            keep.append((ctypes.c_int32 * len(aq))(*aq))
+            d.actual_seq_lengths = ctypes.cast(keep[-1], ctypes.POINTER(ctypes.c_int32))
+        if akv is not None:
+            keep.append((ctypes.c_int32 * len(akv))(*akv))
+            d.actual_seq_lengths_kv = ctypes.cast(keep[-1], ctypes.POINTER(ctypes.c_int32))
+        return lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None)
+
+    assert call([257, 3], None) == 1       # longer than Sq = 256
+    assert call([3, -1], None) == 1
+    assert call(None, [0, 257]) == 1
+    d = _desc(q, B=257, Nq=2, Nkv=2, Sq=4, Skv=4)
+    arr = (ctypes.c_int32 * 257)(*([1] * 257))
+    d.actual_seq_lengths = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 2   # > 256 batches
+    d = _desc(q, layout=1, B=1, Sq=5, Skv=5)  # TND takes cu_seqlens instead
+    a5 = (ctypes.c_int32 * 2)(0, 5)
+    d.cu_seqlens_q = ctypes.cast(a5, ctypes.POINTER(ctypes.c_int32))
+    d.cu_seqlens_kv = ctypes.cast(a5, ctypes.POINTER(ctypes.c_int32))
+    d.actual_seq_lengths = ctypes.cast(a5, ctypes.POINTER(ctypes.c_int32))
+    assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 1
+
+
 def test_blocksparse_and_qbsa_validation(q):
     lib = q.load()
     d = _desc(q, sparse_mode=2)
