@@ -320,6 +320,114 @@ def operator_sweep(seqs, sparsities=(0.0, 0.5, 0.9), reps=5):
     return 0
 
 
+def power_study(S, gaps_ms, chunk_counts=(10,), seconds=3.0):
+    """The single-GPU part of the power-cap page's schedules (FA_Power_Cap: InsertComm splits the
+    attention by head chunks with each chunk's all-to-all in front of it; BlockAttn also splits the
+    local queries into 2 blocks), compared with one call (Baseline: all communication, then one
+    attention). The shape is one GPU's share of the page's Wan2.2 attention at Ulysses degree 4:
+    B=1, N=10 of 40 heads, D=128, S tokens; 10 chunks of one head (loop_time 10), or fewer, larger
+    chunks (`chunk_counts`, each dividing N). The communication
+    is stood in for by idle gaps (one spinning thread): `gap` ms per layer, split evenly over the
+    chunks (Baseline: one gap before its one call), so every schedule idles for the same time. For each schedule and gap, prints one JSON line: time per layer, the
+    attention and gap parts of it (HIP events around every launch and gap), and the gfx clock and
+    socket power while the schedule runs back to back."""
+    import torch
+    import quantized_attention_tiled_amd as qa
+    qa.load()
+    dev = torch.device("cuda:0")
+    B, N, D = 1, 10, 128
+    gen = torch.Generator(device=dev).manual_seed(2024)
+    q, k, v = (torch.randn((B, N, S, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(q)
+    m = torch.empty((B, N, S), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    nqb = (S + 127) // 128
+    scale = D ** -0.5
+    stream = torch.cuda.current_stream(dev)
+
+    def fa(hr=None, br=None):
+        qa.attn_fwd(q, k, v, scale=scale, head_range=hr, qblock_range=br, out=o, softmax_max=m, softmax_sum=l)
+
+    # spin-kernel cycles per ms, from a timed calibration (its counter need not run at a fixed rate)
+    def cycles_for(ms_target):
+        if ms_target <= 0:
+            return 0
+        c = 1_000_000
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            torch.cuda._sleep(c)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            c = max(1000, int(c * ms_target / max(e0.elapsed_time(e1), 1e-3)))
+        return c
+
+    def schedule(kind, gap_cycles, chunks, events=None):
+        parts = []  # ("gap" | "fa", start event, end event)
+
+        def seg(tag, fn):
+            if events is None:
+                fn()
+                return
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            parts.append((tag, e0, e1))
+
+        if kind == "baseline":
+            if gap_cycles:
+                seg("gap", lambda: torch.cuda._sleep(gap_cycles))
+            seg("fa", fa)
+        else:
+            per = N // chunks
+            for c in range(chunks):
+                if gap_cycles:
+                    seg("gap", lambda: torch.cuda._sleep(gap_cycles))
+                hr = (c * per, (c + 1) * per)
+                if kind == "insertcomm":
+                    seg("fa", lambda: fa(hr))
+                else:
+                    seg("fa", lambda: fa(hr, (0, nqb // 2)))
+                    seg("fa", lambda: fa(hr, (nqb // 2, nqb)))
+        if events is not None:
+            events.extend(parts)
+
+    cases = [(gap, "baseline", 1) for gap in gaps_ms] + \
+        [(gap, kind, c) for c in chunk_counts for gap in gaps_ms for kind in ("insertcomm", "blockattn")]
+    for gap, kind, chunks in cases:
+        if N % chunks:
+            raise ValueError(f"{chunks} chunks do not divide {N} heads")
+        cyc = cycles_for(gap / chunks)
+        if True:
+            for _ in range(3):
+                schedule(kind, cyc, chunks)
+            torch.cuda.synchronize()
+            reps = 5
+            evs = []
+            e_all0, e_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e_all0.record(stream)
+            for _ in range(reps):
+                schedule(kind, cyc, chunks, evs)
+            e_all1.record(stream)
+            torch.cuda.synchronize()
+            total = e_all0.elapsed_time(e_all1) / reps
+            fa_ms = sum(a.elapsed_time(b) for t, a, b in evs if t == "fa") / reps
+            gap_total = sum(a.elapsed_time(b) for t, a, b in evs if t == "gap") / reps
+            sustained = sustained_clock_power(lambda: schedule(kind, cyc, chunks), total, seconds=seconds)
+            flop = 4.0 * D * B * N * S * S
+            line = {"study": "power_cap", "schedule": kind, "chunks": chunks, "gap_ms_per_layer": gap, "S": S, "N": N,
+                    "launches": 1 if kind == "baseline" else chunks * (1 if kind == "insertcomm" else 2),
+                    "ms_per_layer": round(total, 3), "attention_ms": round(fa_ms, 3), "gap_ms": round(gap_total, 3),
+                    "attention_tflops": round(flop / fa_ms / 1e9, 1)}
+            if sustained:
+                line["sclk_mhz"] = sustained["sclk_mhz"]
+                line["socket_power_w"] = sustained["socket_power_w"]
+                line["energy_j_per_layer"] = round(sustained["socket_power_w"] * total * 1e-3, 3)
+            print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +441,11 @@ def main(argv=None):
     ap.add_argument("--no-smi", action="store_true", help="skip the sustained clock / power sample")
     ap.add_argument("--sweep", action="store_true", help="operator sweep (S x sparsity x kernel) instead of one line")
     ap.add_argument("--sweep-seqs", default="8192,16384,32768,65536")
+    ap.add_argument("--power-study", action="store_true",
+                    help="power-cap schedules (one call vs head chunks vs head chunks x 2 q-blocks, with gaps)")
+    ap.add_argument("--power-seq", type=int, default=75600, help="S of the power-cap study")
+    ap.add_argument("--power-gaps", default="0,2.5,10", help="idle ms per layer (the communication), comma separated")
+    ap.add_argument("--power-chunks", default="10", help="head-chunk counts of the study, comma separated")
     ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16",
                     help="input / output type of the dense and block-sparse configs (fp16: the same values in float16)")
     ap.add_argument("--dv", type=int, default=None, help="value head dimension below D (dense / block-sparse configs)")
@@ -350,6 +463,9 @@ def main(argv=None):
         return 0
     if a.sweep:
         return operator_sweep([int(x) for x in a.sweep_seqs.split(",") if x])
+    if a.power_study:
+        return power_study(a.power_seq, [float(x) for x in a.power_gaps.split(",") if x],
+                           [int(x) for x in a.power_chunks.split(",") if x])
 
     import quantized_attention_tiled_amd as qa
     from workloads import CONFIGS, make_workload
