@@ -17,6 +17,9 @@ EagleQBSA article, "EagleQBSA quantised block-sparse attention"):
                      quantisers in exact float32 steps; E4M3 encode/decode from
                      the format's definition; the kept-block list (EagleQBSA
                      article, scheme-design section and the API call at its end).
+* ``backward``       the gradients dQ, dK, dV of the ``attention`` definition,
+                     written out in float64 (the guide presents the operator
+                     as a training operator but gives no backward algorithm).
 * ``qbsa``           the quantised block-sparse forward, following the tiled
                      schedule with P cast to FP8 inside the loop (EagleQBSA
                      article, scheme-design and operator-optimisation sections).
@@ -25,6 +28,7 @@ Every function is pinned by tests in ``tests/test_oracle_*.py`` against
 invariants, closed forms, brute force and independent library routines.
 """
 
+from .backward import attention_backward, softmax_attention_backward  # noqa: F401
 from .attention import (  # noqa: F401
     attention,
     attention_block_sparse,

@@ -1,0 +1,78 @@
+"""Gradients of the plain attention definition (oracle; tests only).
+
+The fused attention guide ("Ascend NPU fused attention operator", section 2)
+presents the fused operator as a training operator: the softmax max and sum of
+section 5 are kept for the backward pass, and the tiled form is said to bring
+the backward memory from O(N^2) down to O(N). The pages give no backward
+algorithm, so this module is the derivative of the section 2 definition
+O = P V, P = softmax(mask(Q K^T scale)) row by row, written out in float64
+with the explicit score matrix (masked pairs have P = 0):
+
+    dV = P^T dO
+    dP = dO V^T
+    dS = P * (dP - rowsum(P * dP))      (the softmax Jacobian applied row-wise)
+    dQ = scale * dS K
+    dK = scale * dS^T Q
+
+A row with no kept key has O = 0 and contributes nothing. Masks, causal modes,
+GQA and layouts follow ``attention``'s readings (contiguous head groups: a
+kv-head's gradient sums over the q-heads that read it).
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from .attention import BLOCK, _allowed, _mask_for_head
+
+
+def softmax_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                               allowed: np.ndarray):
+    """Gradients for one head: q [R, D], k [Skv, D], v [Skv, Dv], do [R, Dv], allowed [R, Skv].
+
+    Returns (dq [R, D], dk [Skv, D], dv [Skv, Dv])."""
+    s = (q @ k.T) * scale
+    s = np.where(allowed, s, -np.inf)
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    live = np.isfinite(m)
+    p = np.exp(s - np.where(live, m, 0.0)[:, None])
+    l = p.sum(axis=1)
+    p = p / np.where(live, l, 1.0)[:, None]
+    p[~live] = 0.0
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float, *,
+                       sparse_mode: int = 0, atten_mask: Optional[np.ndarray] = None,
+                       pre_tokens: Optional[int] = None, next_tokens: Optional[int] = None):
+    """BNSD gradients: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D(v)], do [B, Nq, Sq, Dv].
+
+    Returns (dq, dk, dv) shaped like q, k, v."""
+    B, Nq, Sq, D = q.shape
+    Nkv, Skv = k.shape[1], k.shape[2]
+    if Nq % Nkv:
+        raise ValueError("Nq must be a multiple of Nkv")
+    g = Nq // Nkv
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    rows = np.arange(Sq)
+    for b in range(B):
+        for h in range(Nq):
+            mask = _mask_for_head(atten_mask, b, h)
+            a = _allowed(rows, Sq, Skv, sparse_mode, mask, None, pre_tokens, next_tokens)
+            gq, gk, gv = softmax_attention_backward(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, a)
+            dq[b, h] = gq
+            dk[b, h // g] += gk
+            dv[b, h // g] += gv
+    return dq, dk, dv
+
+
+__all__ = ["attention_backward", "softmax_attention_backward", "BLOCK"]
