@@ -223,6 +223,29 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
                   const int32_t* idx, qattn_bf16* o, float* softmax_max, float* softmax_sum, void* stream);
 
 /* Message for the calling thread's most recent failed call ("" if none). */
+/*
+ * attn_bwd -- gradients of attn_fwd (fused attention guide, section 2: the
+ * fused operator is a training operator whose section 5 outputs, softmax max
+ * and sum, are kept for the backward pass; the pages give no backward
+ * algorithm, so this is the derivative of the section 2 definition):
+ *   dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale dS K, dK = scale dS^T Q,
+ * with P recomputed from softmax_max / softmax_sum, never stored.
+ *   desc: BNSD, bf16, Dv = D, sparse_mode 0, 2 or 3, GQA allowed; no atten_mask,
+ *   band, actual lengths or subrange (else QATTN_UNSUPPORTED).
+ *   q, k, v, o, dout: bf16 inputs (o and the softmax outputs from attn_fwd on
+ *   the same description); dq, dk, dv: bf16 outputs shaped like q, k, v (a
+ *   kv-head's gradients sum over the q-heads that read it).
+ *   workspace: device fp32 scratch of attn_bwd_workspace_bytes(desc) bytes
+ *   (8 B Nq Sq), owned by the caller; its contents on entry do not matter.
+ * Deterministic: no atomics; every output element is written by one thread.
+ */
+int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
+             const qattn_bf16* o, const qattn_bf16* dout, const float* softmax_max, const float* softmax_sum,
+             qattn_bf16* dq, qattn_bf16* dk, qattn_bf16* dv, float* workspace, void* stream);
+/* Bytes of workspace attn_bwd needs for `desc` (0 for a NULL or malformed description). */
+size_t attn_bwd_workspace_bytes(const qattn_desc* desc);
+
 const char* qattn_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

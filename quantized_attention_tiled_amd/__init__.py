@@ -1,15 +1,17 @@
-"""Fused, tiled attention forward for AMD MI355X (gfx950).
+"""Fused, tiled attention for AMD MI355X (gfx950): forward, plus the bf16 backward.
 
 Python binding of the qattn C ABI (include/qattn.h). The kernels live in
 ``csrc/`` and are built into ``libqattn.so`` in this directory by
 ``python -m quantized_attention_tiled_amd.build``. Entry points:
 
-* ``attn_fwd``                   dense bf16: BNSD / TND varlen, GQA, causal, boolean masks
+* ``attn_fwd``                   dense bf16 / fp16: BNSD, BSND, BSH, SBH, TND varlen, GQA,
+                                 causal, band, boolean masks, actual lengths, Dv <= D
 * ``build_kv_block_list``        128 x 128 block keep mask -> kept kv-block list
-* ``attn_fwd_blocksparse``       bf16 block-sparse attention over a kept list
+* ``attn_fwd_blocksparse``       bf16 / fp16 block-sparse attention over a kept list
 * ``quantize_qk_perblock_int8``  Q/K INT8 per 128-token block
 * ``quantize_v_perchannel_fp8``  V FP8 E4M3 per channel
 * ``attn_fwd_qbsa``              INT8 Q.K / FP8 P.V quantised block-sparse attention
+* ``attn_bwd``                   dQ, dK, dV of the dense bf16 forward (BNSD, causal, GQA)
 
 Each returns the attention output plus the per-row softmax max and sum where
 the operation has them. Head and q-block subrange launches write only their
@@ -17,6 +19,7 @@ slice and reproduce the full call bit for bit.
 """
 
 from .api import (  # noqa: F401
+    attn_bwd,
     attn_fwd,
     attn_fwd_blocksparse,
     attn_fwd_qbsa,

@@ -348,5 +348,43 @@ def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scal
     return out, softmax_max, softmax_sum
 
 
-__all__ = ["attn_fwd", "attn_fwd_blocksparse", "attn_fwd_qbsa", "build_kv_block_list", "quantize_qk_perblock_int8",
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+             softmax_max: torch.Tensor, softmax_sum: torch.Tensor, *, scale: float = 1.0, sparse_mode: int = 0,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of attn_fwd for BNSD bf16 q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D], given the
+    forward's out and softmax_max / softmax_sum and the output gradient dout (shaped like out).
+    ``workspace``: optional fp32 device tensor of at least 2 * B * Nq * Sq elements."""
+    lib = load()
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _require(t, n, torch.bfloat16, dev)
+    for t, n in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
+        _require(t, n, torch.float32, dev)
+    lay, B, Nq, Sq, Nkv, Skv, D = _dims("BNSD", q, k, None)
+    if v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("v must match k, out and dout must match q")
+    if tuple(softmax_max.shape) != (B, Nq, Sq) or tuple(softmax_sum.shape) != (B, Nq, Sq):
+        raise ValueError("softmax_max / softmax_sum must be [B, Nq, Sq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _require(t, n, torch.bfloat16, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must be shaped like {tuple(ref.shape)}")
+    desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode)
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(desc)) // 4
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.float32, device=dev)
+    _require(workspace, "workspace", torch.float32, dev)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace needs {need} float32 elements")
+    with torch.cuda.device(dev):
+        check(lib.attn_bwd(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(dout), _vp(softmax_max),
+                           _vp(softmax_sum), _vp(dq), _vp(dk), _vp(dv), _vp(workspace), _stream(dev)))
+    return dq, dk, dv
+
+
+__all__ = ["attn_bwd", "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_qbsa", "build_kv_block_list", "quantize_qk_perblock_int8",
            "quantize_v_perchannel_fp8", "make_desc", "_lib"]

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
-SOURCES = ["qattn_abi.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_qbsa.hip", "quant.hip"]
+SOURCES = ["qattn_abi.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_qbsa.hip", "quant.hip", "attn_bwd.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are switched off for all device code; the host
@@ -28,7 +28,8 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # accumulator in ordinary VGPRs, so no accumulator is copied between register files.
 SOURCE_FLAGS = {"attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
                 "attn_fwd_f16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-                "attn_qbsa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+                "attn_qbsa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+                "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def hipcc() -> str:

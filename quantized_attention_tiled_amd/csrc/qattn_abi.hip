@@ -377,4 +377,62 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
   return hip_status(qattn::launch_attn_qbsa(p, (hipStream_t)stream), "attn_fwd_qbsa launch");
 }
 
+size_t attn_bwd_workspace_bytes(const qattn_desc* desc) {
+  if (!desc || desc->struct_size != sizeof(qattn_desc) || desc->B < 0 || desc->Nq < 0 || desc->Sq < 0) return 0;
+  return (size_t)2 * sizeof(float) * (size_t)desc->B * (size_t)desc->Nq * (size_t)desc->Sq;
+}
+
+int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
+             const qattn_bf16* o, const qattn_bf16* dout, const float* softmax_max, const float* softmax_sum,
+             qattn_bf16* dq, qattn_bf16* dk, qattn_bf16* dv, float* workspace, void* stream) {
+  qattn::FwdParams f{};
+  int total_qb = 0;
+  int rc = setup_common(desc, f, false, true, &total_qb);
+  if (rc) return rc;
+  if (desc->layout != QATTN_LAYOUT_BNSD) return fail(QATTN_UNSUPPORTED, "attn_bwd needs the BNSD layout");
+  if (desc->dtype != QATTN_DTYPE_BF16) return fail(QATTN_UNSUPPORTED, "attn_bwd takes bf16 tensors");
+  if (f.Dv != f.D) return fail(QATTN_UNSUPPORTED, "attn_bwd needs Dv == D");
+  if (desc->atten_mask || desc->pre_tokens != INT32_MAX || desc->next_tokens != INT32_MAX || f.actual)
+    return fail(QATTN_UNSUPPORTED, "attn_bwd takes sparse_mode 0, 2 or 3 only (no atten_mask, band or actual lengths)");
+  if (!(desc->head_begin == -1 && desc->head_end == -1 && desc->qblock_begin == -1 && desc->qblock_end == -1))
+    return fail(QATTN_UNSUPPORTED, "attn_bwd covers the whole problem (no head or q-block subrange)");
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  const char* names[] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};
+  if ((rc = check_ptrs(ptrs, names, 8))) return rc;
+  if (!softmax_max || !softmax_sum || !workspace)
+    return fail(QATTN_INVALID_ARGUMENT, "softmax_max, softmax_sum and workspace must be non-NULL");
+  if ((rc = check_optional(softmax_max, "softmax_max")) || (rc = check_optional(softmax_sum, "softmax_sum")) ||
+      (rc = check_optional(workspace, "workspace")))
+    return rc;
+  qattn::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.m_in = softmax_max;
+  p.l_in = softmax_sum;
+  const int64_t rows = (int64_t)desc->B * desc->Nq * desc->Sq;
+  p.lse2 = workspace;
+  p.delta = workspace + rows;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.B = desc->B;
+  p.Nq = desc->Nq;
+  p.Nkv = desc->Nkv;
+  p.group = desc->Nq / desc->Nkv;
+  p.Sq = desc->Sq;
+  p.Skv = desc->Skv;
+  p.D = desc->D;
+  p.causal = desc->sparse_mode;
+  p.scale = f.scale;
+  p.c = f.c;
+  const int64_t items_q = (int64_t)desc->B * desc->Nq * ((desc->Sq + qattn::kBlock - 1) / qattn::kBlock);
+  const int64_t items_k = (int64_t)desc->B * desc->Nkv * ((desc->Skv + qattn::kBlock - 1) / qattn::kBlock);
+  if (items_q > (int64_t)0x7fffff00 || items_k > (int64_t)0x7fffff00 || rows / 16 > (int64_t)0x7fffffff)
+    return fail(QATTN_UNSUPPORTED, "problem too large for one launch");
+  return hip_status(qattn::launch_attn_bwd(p, (hipStream_t)stream), "attn_bwd launch");
+}
+
 }  // extern "C"

@@ -67,6 +67,28 @@ struct FwdParams {
   int cu_kv[kMaxSeqs + 1];
 };
 
+// Everything a backward launch needs (BNSD, bf16, D = Dv), passed by value.
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* m_in;  // forward softmax max / sum [B, Nq, Sq]
+  const float* l_in;
+  float* lse2;        // workspace [B, Nq, Sq]: log2 of the softmax denominator, +inf for empty rows
+  float* delta;       // workspace [B, Nq, Sq]: rowsum(dO * O)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int B, Nq, Nkv, group, Sq, Skv, D;
+  int causal;         // 0, 2 top-left, 3 bottom-right
+  int total_items;
+  float scale;
+  float c;            // scale * log2(e)
+};
+
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, int mode, hipStream_t stream);
 hipError_t launch_attn_fwd_f16(const FwdParams& p, int mode, hipStream_t stream);
 // q-blocks per workgroup of the 16-bit kernels in `mode` (the host sets qblocks_per_tile to

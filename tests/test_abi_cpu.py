@@ -169,6 +169,27 @@ def test_actual_lengths_validation(q):
     assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 1
 
 
+def test_backward_validation(q):
+    lib = q.load()
+
+    def bwd(d, ws=FAKE, m=FAKE):
+        return lib.attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, m, FAKE, FAKE, FAKE, FAKE, ws, None)
+
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(_desc(q, B=2, Nq=4, Sq=100))) == 8 * 2 * 4 * 100
+    assert lib.attn_bwd_workspace_bytes(None) == 0
+    for kw in (dict(layout=2), dict(dtype=1), dict(Dv=64), dict(pre_tokens=3), dict(head_begin=0, head_end=1),
+               dict(qblock_begin=0, qblock_end=1)):
+        assert bwd(_desc(q, **kw)) == 2, kw
+    d = _desc(q)
+    d.atten_mask = FAKE
+    assert bwd(d) == 2
+    assert bwd(_desc(q), ws=None) == 1
+    assert bwd(_desc(q), m=FAKE + 2) == 3
+    assert bwd(_desc(q, sparse_mode=1)) == 1
+    assert lib.attn_bwd(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        None) == 3  # dout misaligned
+
+
 def test_blocksparse_and_qbsa_validation(q):
     lib = q.load()
     d = _desc(q, sparse_mode=2)

@@ -1,0 +1,86 @@
+"""GPU parity of the bf16 attention backward (dQ, dK, dV) against the float64 gradient oracle.
+
+The forward runs on the GPU (its bf16 O and softmax max / sum are the backward's inputs, as in
+training); the oracle differentiates the exact definition from the same bf16 Q, K, V and dO.
+
+Tolerance, per gradient tensor: max-abs error <= 2e-2 * max(1, max |reference|). The kernels round
+P and dS to bf16 before their products (relative 2^-9 each) and write bf16 (half an ulp, 2^-9
+relative); the row term rowsum(dO * O) uses the forward's bf16 O. Each is a relative error of the
+gradient's own magnitude, and together they stay below about 2^-7 of the largest entry; 2e-2 leaves
+room for the sums over up to a few hundred keys or queries. Rows with no kept key must give dQ = 0
+exactly, and repeated calls must give the same bits.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import banner, dev_bf16, f64, to_np
+from workloads import random_bf16
+
+pytestmark = pytest.mark.gpu
+
+G_RTOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def qa():
+    import quantized_attention_tiled_amd as qa
+    qa.load()
+    return qa
+
+
+def _check(g, ref, what):
+    g = to_np(g)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    bound = G_RTOL * max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
+    err = float(np.abs(g - ref).max()) if ref.size else 0.0
+    banner(f"{what}: max-abs err {err:.3e} (bound {bound:.3e}, max |ref| {np.abs(ref).max() if ref.size else 0:.3e})")
+    assert err <= bound, f"{what}: max abs error {err:.3e} > {bound:.3e}"
+
+
+def _run(qa, B, Nq, Nkv, Sq, Skv, D, mode, seed):
+    qb = random_bf16(seed, (B, Nq, Sq, D))
+    kb = random_bf16(seed + 1, (B, Nkv, Skv, D))
+    vb = random_bf16(seed + 2, (B, Nkv, Skv, D))
+    gb = random_bf16(seed + 3, (B, Nq, Sq, D))
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(gb)
+    o, m, l = qa.attn_fwd(q, k, v, scale=scale, sparse_mode=mode)
+    dq, dk, dv = qa.attn_bwd(q, k, v, o, do, m, l, scale=scale, sparse_mode=mode)
+    torch.cuda.synchronize()
+    return (q, k, v, o, do, m, l, scale), (dq, dk, dv), (qb, kb, vb, gb)
+
+
+@pytest.mark.parametrize("B,Nq,Nkv,Sq,Skv,D,mode", [
+    (1, 2, 2, 256, 256, 64, 0),
+    (2, 4, 2, 300, 300, 128, 0),     # ragged tails, GQA 2
+    (1, 4, 1, 200, 333, 128, 0),     # Sq != Skv, GQA 4
+    (1, 2, 2, 384, 384, 128, 2),
+    (2, 4, 2, 300, 300, 64, 2),
+    (1, 2, 1, 200, 450, 128, 3),     # bottom-right, Skv > Sq
+    (1, 2, 2, 450, 200, 128, 3),     # bottom-right, Sq > Skv: leading rows see no key
+    (1, 1, 1, 1, 1, 128, 0),
+    (1, 1, 1, 5, 700, 64, 3),
+])
+def test_backward_against_oracle(qa, B, Nq, Nkv, Sq, Skv, D, mode):
+    what = f"bwd B={B} Nq={Nq} Nkv={Nkv} Sq={Sq} Skv={Skv} D={D} mode={mode}"
+    banner(what)
+    fwd, (dq, dk, dv), (qb, kb, vb, gb) = _run(qa, B, Nq, Nkv, Sq, Skv, D, mode, 700 + Sq + Skv + D + mode)
+    rq, rk, rv = oracle.attention_backward(f64(qb), f64(kb), f64(vb), f64(gb), fwd[7], sparse_mode=mode)
+    _check(dq, rq, what + " dQ")
+    _check(dk, rk, what + " dK")
+    _check(dv, rv, what + " dV")
+    if mode == 3 and Sq > Skv:  # rows i < Sq - Skv keep no key: their dQ is exactly 0
+        assert torch.all(dq[:, :, :Sq - Skv] == 0)
+
+
+def test_backward_deterministic(qa):
+    fwd, g1, _ = _run(qa, 1, 4, 2, 640, 640, 128, 2, 901)
+    q, k, v, o, do, m, l, scale = fwd
+    for _ in range(2):
+        g2 = qa.attn_bwd(q, k, v, o, do, m, l, scale=scale, sparse_mode=2)
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
