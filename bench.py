@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "dense": ["attn_fwd_kernel.h", "attn_fwd_bf16.hip"],
     "blocksparse": ["attn_fwd_kernel.h", "attn_fwd_bf16.hip", "quant.hip"],
     "qbsa": ["attn_qbsa.hip", "quant.hip"],
+    "backward": ["attn_bwd.hip"],
 }
 
 
@@ -428,6 +429,63 @@ def power_study(S, gaps_ms, chunk_counts=(10,), seconds=3.0):
     return 0
 
 
+def backward_bench(a):
+    """The attention backward (dQ, dK, dV) on a dense BNSD config: the forward runs once, untimed,
+    then W warm-up and K timed backward calls (all three kernels) between HIP events. Flops: the
+    usual 10 D per (q, k) pair (five products: S, dP, dV, dK, dQ; 2.5 times the forward's 4 D), and
+    the executed 14 D of these kernels (S and dP are formed once for dQ and once for dK / dV);
+    causal counts the pairs at or below the diagonal. Prints one JSON line."""
+    import torch
+    import quantized_attention_tiled_amd as qa
+    from workloads import CONFIGS, make_workload
+    qa.load()
+    if CONFIGS[a.config]["kind"] != "dense" or CONFIGS[a.config].get("layout", "BNSD") != "BNSD":
+        log("--backward takes a dense BNSD config")
+        return 2
+    w = make_workload(a.config, S=a.seq) if a.seq else make_workload(a.config)
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(w.q), up(w.k), up(w.v)
+    gen = torch.Generator(device=dev).manual_seed(77)
+    do = torch.randn(q.shape, generator=gen, device=dev).to(torch.bfloat16)
+    mode = a.bwd_mode
+    o, m, l = qa.attn_fwd(q, k, v, scale=w.scale, sparse_mode=mode)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(2 * w.B * w.Nq * w.Sq, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        qa.attn_bwd(q, k, v, o, do, m, l, scale=w.scale, sparse_mode=mode, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    ev[0].record(stream)
+    for i in range(a.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)])
+    ms = ev[0].elapsed_time(ev[a.steps]) / a.steps
+    pairs = w.B * w.Nq * (w.Sq * (w.Sq + 1) // 2 if mode == 2 else w.Sq * w.Skv)
+    std, exe = 10 * w.D * pairs, 14 * w.D * pairs
+    line = {"metric": "attention bwd TFLOP/s (dQ, dK, dV; 10 D flops per pair), % bf16 MFMA peak",
+            "value": round(std / ms / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+            "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic (seeded forward inputs; dO N(0,1) drawn on the GPU)",
+            "config": {"workload": f"{a.config}: {w.description}" + (f" (S {w.Sq})" if a.seq else ""),
+                       "sparse_mode": mode},
+            "detail": {"executed_tflops": round(exe / ms / 1e9, 2), "pct_mfma_peak_executed":
+                       round(100 * exe / ms / 1e9 / PEAK_BF16, 2), "median_ms": round(float(np.median(per)), 4),
+                       "cv": round(float(per.std() / per.mean()), 4), "kernel_source_sha": source_hash("backward")}}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -441,6 +499,8 @@ def main(argv=None):
     ap.add_argument("--no-smi", action="store_true", help="skip the sustained clock / power sample")
     ap.add_argument("--sweep", action="store_true", help="operator sweep (S x sparsity x kernel) instead of one line")
     ap.add_argument("--sweep-seqs", default="8192,16384,32768,65536")
+    ap.add_argument("--backward", action="store_true", help="time the attention backward on the config instead")
+    ap.add_argument("--bwd-mode", type=int, default=0, choices=[0, 2], help="sparse_mode of the backward bench")
     ap.add_argument("--power-study", action="store_true",
                     help="power-cap schedules (one call vs head chunks vs head chunks x 2 q-blocks, with gaps)")
     ap.add_argument("--power-seq", type=int, default=75600, help="S of the power-cap study")
@@ -463,6 +523,8 @@ def main(argv=None):
         return 0
     if a.sweep:
         return operator_sweep([int(x) for x in a.sweep_seqs.split(",") if x])
+    if a.backward:
+        return backward_bench(a)
     if a.power_study:
         return power_study(a.power_seq, [float(x) for x in a.power_gaps.split(",") if x],
                            [int(x) for x in a.power_chunks.split(",") if x])

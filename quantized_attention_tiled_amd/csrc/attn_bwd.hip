@@ -53,20 +53,32 @@ struct BTile {
   __device__ static uint32_t at(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
 };
 
-// Stage rows [row0, row0 + 64) of a row-major [rows, D] bf16 matrix (rows past `valid` as zeros)
-// into an LDS tile; all 256 threads take part.
+// Direct HBM -> LDS loads of 64-row tiles (buffer_load_dwordx4 ... lds, no staging registers):
+// wave w's load n fills the 1 KiB slab 4 n + w of a tile, i.e. rows (4 n + w) R .. + R - 1 with
+// R = 1024 / row bytes, lane l taking physical chunk l % chunks of row l / chunks, so the global
+// chunk it reads is the swizzled one. The swizzle repeats within 4 R rows, so one per-lane offset
+// serves every load; rows past the buffer's extent read as zeros.
 template <int D>
-__device__ __forceinline__ void stage_tile(uint8_t* lds, const uint16_t* src, int row0, int valid, int tid) {
+struct TileLoad {
   using T = BTile<D>;
-  constexpr int kTotal = kTileRows * T::kChunks;
-#pragma unroll
-  for (int i = tid; i < kTotal; i += 256) {
-    const int r = i / T::kChunks, c = i % T::kChunks;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < valid) v = *(const uint4*)(src + (int64_t)(row0 + r) * D + c * 8);
-    *(uint4*)(lds + T::at(r, c)) = v;
+  static constexpr int kRowsPerLoad = 1024 / T::kRowBytes;
+  static constexpr int kLoads = kTileRows / (4 * kRowsPerLoad);  // loads per wave per tile
+  uint32_t lane_off;
+  __device__ explicit TileLoad(int wave, int lane) {
+    const int row = wave * kRowsPerLoad + lane / T::kChunks;
+    lane_off = (uint32_t)(row * T::kRowBytes) + (uint32_t)(((lane % T::kChunks) ^ T::swz(row)) << 4);
   }
-}
+  // tile whose first row is `row0` of the buffer, into LDS at `lds`
+  __device__ void issue(const rsrc4& rsrc, uint8_t* lds, int row0, int wave) const {
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(row0) * (uint32_t)T::kRowBytes;
+#pragma unroll
+    for (int n = 0; n < kLoads; n++)
+      load_lds16(rsrc, lds_address(lds + (4 * n + wave) * 1024), lane_off,
+                 soff + (uint32_t)(n * 4 * kRowsPerLoad * T::kRowBytes));
+  }
+};
+
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // A operand of a product whose contraction runs over tile rows: rows 16 kc .. 16 kc + 15 of the
 // tile, columns 32 db .. 32 db + 31 as the 32 output rows (transposed reads).
@@ -144,11 +156,11 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   using T = BTile<D>;
   constexpr int DT = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::kBytes];
-  uint8_t* const kt = smem;
-  uint8_t* const vt = smem + T::kBytes;
+  // K slots 0, 1, then V slots 0, 1: tile it + 1 loads while tile it is read
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * T::kBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hl = lane >> 5;
   const int item = xcd_remap(blockIdx.x, gridDim.x, p.total_items);
   if (item < 0) return;
@@ -186,12 +198,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 
   const int kv_end = CAUSAL ? min(Lkv, row_end - 1 + off + 1) : Lkv;
   const int ntiles = (row_end > qb * kBlock && kv_end > 0) ? (kv_end + kTileRows - 1) / kTileRows : 0;
+  const TileLoad<D> ld(wave, lane);
+  const rsrc4 k_rsrc = make_rsrc(kp, (uint32_t)Lkv * T::kRowBytes);
+  const rsrc4 v_rsrc = make_rsrc(vp, (uint32_t)Lkv * T::kRowBytes);
+  if (ntiles > 0) {
+    ld.issue(k_rsrc, smem, 0, wave);
+    ld.issue(v_rsrc, smem + 2 * T::kBytes, 0, wave);
+  }
   for (int it = 0; it < ntiles; it++) {
     const int key0 = it * kTileRows;
-    __syncthreads();  // the previous tile is no longer read
-    stage_tile<D>(kt, kp, key0, Lkv, tid);
-    stage_tile<D>(vt, vp, key0, Lkv, tid);
+    // tile it has landed everywhere, and every wave is done with tile it - 1, whose slots the
+    // loads of tile it + 1 now take
+    wait_loads();
     __syncthreads();
+    if (it + 1 < ntiles) {
+      ld.issue(k_rsrc, smem + ((it + 1) & 1) * T::kBytes, key0 + kTileRows, wave);
+      ld.issue(v_rsrc, smem + (2 + ((it + 1) & 1)) * T::kBytes, key0 + kTileRows, wave);
+    }
+    const uint8_t* kt = smem + (it & 1) * T::kBytes;
+    const uint8_t* vt = smem + (2 + (it & 1)) * T::kBytes;
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
       const int k0 = key0 + 32 * hf;
@@ -217,6 +242,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
         for (int db = 0; db < DB; db++) acc[db] = mfma(read_tr<D>(kt, 2 * hf + c, db, lane), dsc[c], acc[db]);
     }
   }
+  wait_loads();  // nothing may still be loading into LDS when the workgroup ends
   if (q < row_end) store_rows<D>(p.dq + ((int64_t)bh * Lq + q) * D, acc, p.scale, hl);
 }
 
@@ -225,12 +251,12 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   using T = BTile<D>;
   constexpr int DT = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::kBytes];
-  __shared__ float s_lse[kTileRows], s_dlt[kTileRows];
-  uint8_t* const qt = smem;
-  uint8_t* const gt = smem + T::kBytes;
+  // Q slots 0, 1, dO slots 0, 1, then per slot 1 KiB holding the tile rows' lse2 (bytes 0..255)
+  // and rowsum(dO * O) (256..511): tile u + 1 loads while tile u is read
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * T::kBytes + 2 * 1024];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hl = lane >> 5;
   const int item = xcd_remap(blockIdx.x, gridDim.x, p.total_items);
   if (item < 0) return;
@@ -267,51 +293,67 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int q_first = CAUSAL ? max(0, kb * kBlock - off) : 0;
   const int t_first = q_first / kTileRows;
   const int ntiles = key_end > kb * kBlock ? max(0, (Lq + kTileRows - 1) / kTileRows - t_first) : 0;
-  for (int hh = 0; hh < p.group; hh++) {
-    const int h = g * p.group + hh;
-    const int64_t bh = (int64_t)b * p.Nq + h;
-    const uint16_t* qp = p.q + bh * Lq * D;
-    const uint16_t* gp = p.dout + bh * Lq * D;
-    for (int it = 0; it < ntiles; it++) {
-      const int row0 = (t_first + it) * kTileRows;
-      __syncthreads();  // the previous tile is no longer read
-      stage_tile<D>(qt, qp, row0, Lq, tid);
-      stage_tile<D>(gt, gp, row0, Lq, tid);
-      if (tid < kTileRows) {
-        const int r = row0 + tid;
-        s_lse[tid] = r < Lq ? p.lse2[bh * Lq + r] : kPosInf;
-        s_dlt[tid] = r < Lq ? p.delta[bh * Lq + r] : 0.f;
+  const int total = ntiles * p.group;  // tiles u = hh * ntiles + it over the group's q-heads
+  const TileLoad<D> ld(wave, lane);
+  const int64_t rows_all = (int64_t)p.B * p.Nq * Lq;
+  // lse2 and rowsum(dO * O) sit back to back in the workspace (delta = lse2 + rows_all)
+  const rsrc4 ml_rsrc = make_rsrc(p.lse2, (uint32_t)(rows_all * 8));
+  auto issue = [&](int u) __attribute__((always_inline)) {
+    const int hh = u / ntiles, row0 = (t_first + u % ntiles) * kTileRows;
+    const int64_t bh = (int64_t)b * p.Nq + g * p.group + hh;
+    const uint32_t bytes = (uint32_t)Lq * T::kRowBytes;
+    ld.issue(make_rsrc(p.q + bh * Lq * D, bytes), smem + (u & 1) * T::kBytes, row0, wave);
+    ld.issue(make_rsrc(p.dout + bh * Lq * D, bytes), smem + (2 + (u & 1)) * T::kBytes, row0, wave);
+    if (wave == 0) {
+      // lanes 0..15: 4 lse2 values each, lanes 16..31: 4 rowsum values, lanes 32..63 read past
+      // the extent (zeros into the unused half of the 1 KiB)
+      const int64_t e = lane < 16 ? bh * Lq + row0 + 4 * lane : rows_all + bh * Lq + row0 + 4 * (lane - 16);
+      const uint32_t voff = lane < 32 ? (uint32_t)(e * 4) : (uint32_t)(rows_all * 8);
+      load_lds16(ml_rsrc, lds_address(smem + 4 * T::kBytes + (u & 1) * 1024), voff, 0u);
+    }
+  };
+  if (total > 0) issue(0);
+  for (int u = 0; u < total; u++) {
+    const int row0 = (t_first + u % ntiles) * kTileRows;
+    // tile u has landed everywhere, and every wave is done with tile u - 1, whose slots the
+    // loads of tile u + 1 now take
+    wait_loads();
+    __syncthreads();
+    if (u + 1 < total) issue(u + 1);
+    const uint8_t* qt = smem + (u & 1) * T::kBytes;
+    const uint8_t* gt = smem + (2 + (u & 1)) * T::kBytes;
+    const float* s_lse = (const float*)(smem + 4 * T::kBytes + (u & 1) * 1024);
+    const float* s_dlt = s_lse + 64;
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      const int r0 = row0 + 32 * hf;
+      if (r0 >= Lq) break;
+      if (CAUSAL && r0 + 31 + off < wkey0) continue;  // every row of the half is above these keys
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DT; t++) {
+        s = mfma(read_row<D>(qt, 32 * hf + l32, t, hl), kreg[t], s);
+        dp = mfma(read_row<D>(gt, 32 * hf + l32, t, hl), vreg[t], dp);
       }
-      __syncthreads();
+      bf16x8 pc[2], dsc[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; hf++) {
-        const int r0 = row0 + 32 * hf;
-        if (CAUSAL && r0 + 31 + off < wkey0) continue;  // every row of the half is above these keys
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int t = 0; t < DT; t++) {
-          s = mfma(read_row<D>(qt, 32 * hf + l32, t, hl), kreg[t], s);
-          dp = mfma(read_row<D>(gt, 32 * hf + l32, t, hl), vreg[t], dp);
-        }
-        bf16x8 pc[2], dsc[2];
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int qr = 32 * hf + c_row(r, hl);  // query row inside the tile
-          const bool keep = !CAUSAL || key <= row0 + qr + off;
-          const float pr = keep ? __builtin_amdgcn_exp2f(s[r] * p.c - s_lse[qr]) : 0.f;
-          pc[r >> 3][r & 7] = (__bf16)pr;
-          dsc[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - s_dlt[qr]));
-        }
-#pragma unroll
-        for (int c = 0; c < 2; c++)
-#pragma unroll
-          for (int db = 0; db < DB; db++) {
-            dv[db] = mfma(read_tr<D>(gt, 2 * hf + c, db, lane), pc[c], dv[db]);
-            dk[db] = mfma(read_tr<D>(qt, 2 * hf + c, db, lane), dsc[c], dk[db]);
-          }
+      for (int r = 0; r < 16; r++) {
+        const int qr = 32 * hf + c_row(r, hl);  // query row inside the tile
+        const bool keep = row0 + qr < Lq && (!CAUSAL || key <= row0 + qr + off);
+        const float pr = keep ? __builtin_amdgcn_exp2f(s[r] * p.c - s_lse[qr]) : 0.f;
+        pc[r >> 3][r & 7] = (__bf16)pr;
+        dsc[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - s_dlt[qr]));
       }
+#pragma unroll
+      for (int c = 0; c < 2; c++)
+#pragma unroll
+        for (int db = 0; db < DB; db++) {
+          dv[db] = mfma(read_tr<D>(gt, 2 * hf + c, db, lane), pc[c], dv[db]);
+          dk[db] = mfma(read_tr<D>(qt, 2 * hf + c, db, lane), dsc[c], dk[db]);
+        }
     }
   }
+  wait_loads();  // nothing may still be loading into LDS when the workgroup ends
   if (key < key_end) {
     store_rows<D>(p.dk + ((int64_t)bg * Lkv + key) * D, dk, p.scale, hl);
     store_rows<D>(p.dv + ((int64_t)bg * Lkv + key) * D, dv, 1.f, hl);

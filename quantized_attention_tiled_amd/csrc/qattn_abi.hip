@@ -430,7 +430,8 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.c = f.c;
   const int64_t items_q = (int64_t)desc->B * desc->Nq * ((desc->Sq + qattn::kBlock - 1) / qattn::kBlock);
   const int64_t items_k = (int64_t)desc->B * desc->Nkv * ((desc->Skv + qattn::kBlock - 1) / qattn::kBlock);
-  if (items_q > (int64_t)0x7fffff00 || items_k > (int64_t)0x7fffff00 || rows / 16 > (int64_t)0x7fffffff)
+  // the kernels address the workspace (8 bytes per row) through 32-bit byte offsets
+  if (items_q > (int64_t)0x7fffff00 || items_k > (int64_t)0x7fffff00 || rows * 8 >= ((int64_t)1 << 32))
     return fail(QATTN_UNSUPPORTED, "problem too large for one launch");
   return hip_status(qattn::launch_attn_bwd(p, (hipStream_t)stream), "attn_bwd launch");
 }

@@ -115,7 +115,22 @@ def _asm(src):
     return _compile(src)[1]
 
 
-@pytest.mark.parametrize("src", FWD_SOURCES + ["attn_qbsa.hip"])
+def test_bwd_kernels_use_no_scratch_and_fit():
+    """The backward kernels keep everything in registers; the dQ kernel runs two workgroups per CU
+    (two waves per SIMD, 64 KiB of LDS each), the dK/dV kernel one (its accumulators take 512
+    registers per lane)."""
+    ks = _resources("attn_bwd.hip")
+    assert len(ks) == 10, list(ks)  # preparation, dQ and dK/dV (two modes each), for D = 64 and 128
+    for name, res in ks.items():
+        assert res.get("ScratchSize", 0) == 0, (name, res)
+        assert res.get("VGPRs Spill", 0) == 0, (name, res)
+        if "bwd_dq_kernel" in name:
+            assert res.get("Occupancy", 0) >= 2 and res.get("LDS Size", 0) <= 80 * 1024, (name, res)
+        if "bwd_dkdv_kernel" in name:
+            assert res.get("Occupancy", 0) >= 1 and res.get("LDS Size", 0) <= 160 * 1024, (name, res)
+
+
+@pytest.mark.parametrize("src", FWD_SOURCES + ["attn_qbsa.hip", "attn_bwd.hip"])
 def test_m0_only_feeds_direct_lds_loads(src):
     """The direct HBM -> LDS loads set M0 in inline asm, where the compiler does not preserve it:
     no other instruction of these kernels may read or write M0."""
