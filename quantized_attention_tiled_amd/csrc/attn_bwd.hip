@@ -217,24 +217,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     }
     const uint8_t* kt = smem + (it & 1) * T::kBytes;
     const uint8_t* vt = smem + (2 + (it & 1)) * T::kBytes;
+    if (CAUSAL && key0 > qb * kBlock + wave * 32 + 31 + off) continue;  // above this wave's diagonal
+    // S^T and dP^T of both 32-key halves first, then per half the softmax gradient and the dQ
+    // products, straight-line so that vector and matrix work of the two halves can overlap
+    f32x16 s[2], dp[2];
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-      const int k0 = key0 + 32 * hf;
-      if (k0 >= kv_end) break;
-      if (CAUSAL && k0 > qb * kBlock + wave * 32 + 31 + off) continue;  // above this wave's diagonal
-      f32x16 s = f32x16{}, dp = f32x16{};
+      s[hf] = f32x16{};
+      dp[hf] = f32x16{};
 #pragma unroll
       for (int t = 0; t < DT; t++) {
-        s = mfma(read_row<D>(kt, 32 * hf + l32, t, hl), qreg[t], s);
-        dp = mfma(read_row<D>(vt, 32 * hf + l32, t, hl), greg[t], dp);
+        s[hf] = mfma(read_row<D>(kt, 32 * hf + l32, t, hl), qreg[t], s[hf]);
+        dp[hf] = mfma(read_row<D>(vt, 32 * hf + l32, t, hl), greg[t], dp[hf]);
       }
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
       bf16x8 dsc[2];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int key = k0 + c_row(r, hl);
+        const int key = key0 + 32 * hf + c_row(r, hl);
         const bool keep = key < Lkv && (!CAUSAL || key <= q + off);
-        const float pr = keep ? __builtin_amdgcn_exp2f(s[r] * p.c - lse2) : 0.f;
-        dsc[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dlt));
+        const float pr = keep ? __builtin_amdgcn_exp2f(s[hf][r] * p.c - lse2) : 0.f;
+        dsc[r >> 3][r & 7] = (__bf16)(pr * (dp[hf][r] - dlt));
       }
 #pragma unroll
       for (int c = 0; c < 2; c++)
@@ -324,25 +329,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const uint8_t* gt = smem + (2 + (u & 1)) * T::kBytes;
     const float* s_lse = (const float*)(smem + 4 * T::kBytes + (u & 1) * 1024);
     const float* s_dlt = s_lse + 64;
+    if (CAUSAL && row0 + kTileRows - 1 + off < wkey0) continue;  // every row is above these keys
+    // S and dP of both 32-row halves first (independent chains), then per half the softmax
+    // gradient and the dV / dK products, straight-line so that the scheduler can overlap one
+    // half's vector work with the other half's matrix products
+    f32x16 s[2], dp[2];
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-      const int r0 = row0 + 32 * hf;
-      if (r0 >= Lq) break;
-      if (CAUSAL && r0 + 31 + off < wkey0) continue;  // every row of the half is above these keys
-      f32x16 s = f32x16{}, dp = f32x16{};
+      s[hf] = f32x16{};
+      dp[hf] = f32x16{};
 #pragma unroll
       for (int t = 0; t < DT; t++) {
-        s = mfma(read_row<D>(qt, 32 * hf + l32, t, hl), kreg[t], s);
-        dp = mfma(read_row<D>(gt, 32 * hf + l32, t, hl), vreg[t], dp);
+        s[hf] = mfma(read_row<D>(qt, 32 * hf + l32, t, hl), kreg[t], s[hf]);
+        dp[hf] = mfma(read_row<D>(gt, 32 * hf + l32, t, hl), vreg[t], dp[hf]);
       }
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
       bf16x8 pc[2], dsc[2];
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int qr = 32 * hf + c_row(r, hl);  // query row inside the tile
         const bool keep = row0 + qr < Lq && (!CAUSAL || key <= row0 + qr + off);
-        const float pr = keep ? __builtin_amdgcn_exp2f(s[r] * p.c - s_lse[qr]) : 0.f;
+        const float pr = keep ? __builtin_amdgcn_exp2f(s[hf][r] * p.c - s_lse[qr]) : 0.f;
         pc[r >> 3][r & 7] = (__bf16)pr;
-        dsc[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - s_dlt[qr]));
+        dsc[r >> 3][r & 7] = (__bf16)(pr * (dp[hf][r] - s_dlt[qr]));
       }
 #pragma unroll
       for (int c = 0; c < 2; c++)
