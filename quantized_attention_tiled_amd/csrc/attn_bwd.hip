@@ -41,6 +41,15 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// two floats rounded to bf16 (nearest even) in one dword, low half first
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
 // Row-major 64 x D bf16 tile in LDS with 16-byte chunks XOR-swizzled by row. The swizzle repeats
 // every 8 rows, which the transposed reads below need (their two halves are 8 rows apart).
 template <int D>
@@ -98,6 +107,19 @@ __device__ __forceinline__ bf16x8 read_tr(const uint8_t* lds, int kc, int db, in
 template <int D>
 __device__ __forceinline__ bf16x8 read_row(const uint8_t* lds, int row, int t, int hl) {
   return *(const bf16x8*)(lds + BTile<D>::at(row, 2 * t + hl));
+}
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+// Empty volatile asm statements keep their relative order: pin_use(x) needs x at this point, so the
+// work that produces x cannot sink below it; together with the scheduling barriers this keeps each
+// slot's vector work next to its matrix product.
+template <typename T>
+__device__ __forceinline__ void pin_use(const T& x) {
+  asm volatile("" ::"v"(x));
 }
 
 // register r of a C-layout accumulator holds row 8 (r / 4) + 4 hl + r % 4 of its 32-row block
@@ -218,34 +240,88 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     const uint8_t* kt = smem + (it & 1) * T::kBytes;
     const uint8_t* vt = smem + (2 + (it & 1)) * T::kBytes;
     if (CAUSAL && key0 > qb * kBlock + wave * 32 + 31 + off) continue;  // above this wave's diagonal
-    // S^T and dP^T of both 32-key halves first, then per half the softmax gradient and the dQ
-    // products, straight-line so that vector and matrix work of the two halves can overlap
+    // a tile that crosses this wave's causal diagonal needs the per-element causal mask
+    const bool diag = CAUSAL && key0 + kTileRows - 1 > qb * kBlock + wave * 32 + off;
+    // Four phases, one matrix product per slot (as in the dK / dV kernel):
+    //   A: S^T = K Q^T and dP^T = V dO^T of keys 0..31 (h0), alternating (D / 8 products);
+    //   B: the same for keys 32..63 (h1), while the vector units turn h0 into dS^T (bf16);
+    //   C: dQ^T += K^T dS^T of h0 (D / 16 products), while the vector units do h1;
+    //   D: the same products of h1.
+    constexpr int MS = D / 8, MQ = D / 16;
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; hf++) {
-      s[hf] = f32x16{};
-      dp[hf] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < DT; t++) {
-        s[hf] = mfma(read_row<D>(kt, 32 * hf + l32, t, hl), qreg[t], s[hf]);
-        dp[hf] = mfma(read_row<D>(vt, 32 * hf + l32, t, hl), greg[t], dp[hf]);
+    u32x4 dsc[2][2];  // dS^T as bf16 B operands, two registers per dword
+    auto operand = [&](auto G, int k) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int g_ = decltype(G)::value;
+      if constexpr (g_ < 2)
+        return read_row<D>((k & 1) ? vt : kt, 32 * g_ + l32, k >> 1, hl);
+      else
+        return read_tr<D>(kt, 2 * (g_ - 2) + k / DB, k % DB, lane);
+    };
+    auto product = [&](auto G, int k, const bf16x8& a) __attribute__((always_inline)) {
+      constexpr int g_ = decltype(G)::value;
+      if constexpr (g_ < 2) {
+        const int t = k >> 1;
+        if (k & 1)
+          dp[g_] = mfma(a, greg[t], t == 0 ? f32x16{} : dp[g_]);
+        else
+          s[g_] = mfma(a, qreg[t], t == 0 ? f32x16{} : s[g_]);
+      } else {
+        acc[k % DB] = mfma(a, __builtin_bit_cast(bf16x8, dsc[g_ - 2][k / DB]), acc[k % DB]);
       }
-    }
+    };
+    // dS^T of registers e0 .. e0 + n - 1 of half h (n even). Keys past the sequence are zero in K
+    // and V, so their dS multiplies zero rows of K^T; the clamp at 0 (never binding for a real key,
+    // whose score lies below the row's log-sum) keeps their P finite.
+    auto softmax_grad = [&](int h, int e0, int n) __attribute__((always_inline)) {
 #pragma unroll
-    for (int hf = 0; hf < 2; hf++) {
-      bf16x8 dsc[2];
+      for (int e = e0; e < e0 + n; e += 2) {
+        float d2[2];
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int key = key0 + 32 * hf + c_row(r, hl);
-        const bool keep = key < Lkv && (!CAUSAL || key <= q + off);
-        const float pr = keep ? __builtin_amdgcn_exp2f(s[hf][r] * p.c - lse2) : 0.f;
-        dsc[r >> 3][r & 7] = (__bf16)(pr * (dp[hf][r] - dlt));
+        for (int i = 0; i < 2; i++) {
+          float pr = __builtin_amdgcn_exp2f(fminf(s[h][e + i] * p.c - lse2, 0.f));
+          if (CAUSAL && diag) pr = key0 + 32 * h + c_row(e + i, hl) <= q + off ? pr : 0.f;
+          d2[i] = pr * (dp[h][e + i] - dlt);
+        }
+        dsc[h][e >> 3][(e & 7) >> 1] = pack_bf16(d2[0], d2[1]);
+        pin_use(dsc[h][e >> 3][(e & 7) >> 1]);
       }
+    };
+    bf16x8 carry[2];
+    auto phase = [&](auto G, auto VH, auto NG, bool pin) __attribute__((always_inline)) {
+      constexpr int g_ = decltype(G)::value, vh = decltype(VH)::value, ng = decltype(NG)::value;
+      constexpr int M = g_ < 2 ? MS : MQ;
+      constexpr int NM = ng < 2 ? MS : MQ;
+      bf16x8 op[M];
+      if (pin) {
+        op[0] = carry[0];
+        op[1] = carry[1];
+      } else {
+        op[0] = operand(G, 0);
+        op[1] = operand(G, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 2; c++)
+      for (int k = 0; k < M; k++) {
+        if (k + 2 < M) {
+          op[k + 2] = operand(G, k + 2);
+        } else if constexpr (ng >= 0) {
+          if (k + 2 - M < NM) carry[k + 2 - M] = operand(IC<(ng < 0 ? 0 : ng)>{}, k + 2 - M);
+        }
+        product(G, k, op[k]);
+        if constexpr (vh >= 0) {
+          // 16 registers over M slots, in pairs: spread the pairs evenly
+          constexpr int P = 8;  // pairs
 #pragma unroll
-        for (int db = 0; db < DB; db++) acc[db] = mfma(read_tr<D>(kt, 2 * hf + c, db, lane), dsc[c], acc[db]);
-    }
+          for (int q2 = 0; q2 < P; q2++)
+            if ((q2 * M) / P == k) softmax_grad(vh, 2 * q2, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    phase(IC<0>{}, IC<-1>{}, IC<1>{}, false);
+    phase(IC<1>{}, IC<0>{}, IC<2>{}, true);
+    phase(IC<2>{}, IC<1>{}, IC<3>{}, true);
+    phase(IC<3>{}, IC<-1>{}, IC<-1>{}, true);
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
   if (q < row_end) store_rows<D>(p.dq + ((int64_t)bh * Lq + q) * D, acc, p.scale, hl);
@@ -330,39 +406,113 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const float* s_lse = (const float*)(smem + 4 * T::kBytes + (u & 1) * 1024);
     const float* s_dlt = s_lse + 64;
     if (CAUSAL && row0 + kTileRows - 1 + off < wkey0) continue;  // every row is above these keys
-    // S and dP of both 32-row halves first (independent chains), then per half the softmax
-    // gradient and the dV / dK products, straight-line so that the scheduler can overlap one
-    // half's vector work with the other half's matrix products
+    // a tile that crosses this wave's causal diagonal needs the per-element causal mask
+    const bool diag = CAUSAL && row0 + off < wkey0 + 31;
+    // Four phases of M = D / 8 matrix products each, one product per slot:
+    //   A: S = Q K^T and dP = dO V^T of rows 0..31 (h0), alternating;
+    //   B: the same for rows 32..63 (h1), while the vector units turn h0's S and dP into P and
+    //      dS (bf16), 16 / M rows' worth of registers per slot;
+    //   C: dV^T += dO^T P and dK^T += Q^T dS of h0, while the vector units do h1;
+    //   D: the same products of h1.
+    // A operands are read from LDS two slots ahead; scheduling barriers keep each slot's work.
+    constexpr int M = D / 8;
+    constexpr int E = 16 / M;  // registers of one half handled per slot
     f32x16 s[2], dp[2];
+    u32x4 pc[2][2], dsc[2][2];  // P and dS as bf16 B operands, two registers per dword
+    float lse_r[2][16], dlt_r[2][16];
+    // lse2 and rowsum of group j (4 consecutive rows) of half h, read before they are needed
+    auto read_ml = [&](int h, int j) __attribute__((always_inline)) {
+      const float4 a4 = *(const float4*)(s_lse + 32 * h + 8 * j + 4 * hl);
+      const float4 d4 = *(const float4*)(s_dlt + 32 * h + 8 * j + 4 * hl);
+      lse_r[h][4 * j] = a4.x, lse_r[h][4 * j + 1] = a4.y, lse_r[h][4 * j + 2] = a4.z, lse_r[h][4 * j + 3] = a4.w;
+      dlt_r[h][4 * j] = d4.x, dlt_r[h][4 * j + 1] = d4.y, dlt_r[h][4 * j + 2] = d4.z, dlt_r[h][4 * j + 3] = d4.w;
+    };
 #pragma unroll
-    for (int hf = 0; hf < 2; hf++) {
-      s[hf] = f32x16{};
-      dp[hf] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < DT; t++) {
-        s[hf] = mfma(read_row<D>(qt, 32 * hf + l32, t, hl), kreg[t], s[hf]);
-        dp[hf] = mfma(read_row<D>(gt, 32 * hf + l32, t, hl), vreg[t], dp[hf]);
+    for (int j = 0; j < 4; j++) read_ml(0, j);
+    // A operand of product k of group G (0, 1: S / dP of half G; 2, 3: dV / dK of half G - 2)
+    auto operand = [&](auto G, int k) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int g_ = decltype(G)::value;
+      if constexpr (g_ < 2) {
+        return read_row<D>((k & 1) ? gt : qt, 32 * g_ + l32, k >> 1, hl);
+      } else {
+        const int j = k >> 1;
+        return read_tr<D>((k & 1) ? qt : gt, 2 * (g_ - 2) + j / DB, j % DB, lane);
       }
-    }
-#pragma unroll
-    for (int hf = 0; hf < 2; hf++) {
-      bf16x8 pc[2], dsc[2];
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int qr = 32 * hf + c_row(r, hl);  // query row inside the tile
-        const bool keep = row0 + qr < Lq && (!CAUSAL || key <= row0 + qr + off);
-        const float pr = keep ? __builtin_amdgcn_exp2f(s[hf][r] * p.c - s_lse[qr]) : 0.f;
-        pc[r >> 3][r & 7] = (__bf16)pr;
-        dsc[r >> 3][r & 7] = (__bf16)(pr * (dp[hf][r] - s_dlt[qr]));
+    };
+    auto product = [&](auto G, int k, const bf16x8& a) __attribute__((always_inline)) {
+      constexpr int g_ = decltype(G)::value;
+      if constexpr (g_ < 2) {
+        const int t = k >> 1;
+        if (k & 1)
+          dp[g_] = mfma(a, vreg[t], t == 0 ? f32x16{} : dp[g_]);
+        else
+          s[g_] = mfma(a, kreg[t], t == 0 ? f32x16{} : s[g_]);
+      } else {
+        const int j = k >> 1, c = j / DB, db = j % DB;
+        if (k & 1)
+          dk[db] = mfma(a, __builtin_bit_cast(bf16x8, dsc[g_ - 2][c]), dk[db]);
+        else
+          dv[db] = mfma(a, __builtin_bit_cast(bf16x8, pc[g_ - 2][c]), dv[db]);
       }
+    };
+    // P and dS of registers e0 .. e0 + E - 1 of half h; a register pair is packed to bf16 once
+    // both are done
+    float pr_t[2], ds_t[2];
+    auto softmax_grad = [&](int h, int e0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int c = 0; c < 2; c++)
-#pragma unroll
-        for (int db = 0; db < DB; db++) {
-          dv[db] = mfma(read_tr<D>(gt, 2 * hf + c, db, lane), pc[c], dv[db]);
-          dk[db] = mfma(read_tr<D>(qt, 2 * hf + c, db, lane), dsc[c], dk[db]);
+      for (int e = e0; e < e0 + E; e++) {
+        const int qr = 32 * h + c_row(e, hl);  // query row inside the tile
+        // Rows past the sequence are zero in Q and dO, so their P and dS multiply zeros; their
+        // lse2 slot holds another row's value, and the clamp at 0 (never binding for a real row,
+        // whose scores lie below its log-sum) keeps their P finite.
+        float pr = __builtin_amdgcn_exp2f(fminf(s[h][e] * p.c - lse_r[h][e], 0.f));
+        if (CAUSAL && diag) pr = key <= row0 + qr + off ? pr : 0.f;
+        pr_t[e & 1] = pr;
+        ds_t[e & 1] = pr * (dp[h][e] - dlt_r[h][e]);
+        if (e & 1) {
+          pc[h][e >> 3][(e & 7) >> 1] = pack_bf16(pr_t[0], pr_t[1]);
+          dsc[h][e >> 3][(e & 7) >> 1] = pack_bf16(ds_t[0], ds_t[1]);
+          pin_use(pc[h][e >> 3][(e & 7) >> 1]);
+          pin_use(dsc[h][e >> 3][(e & 7) >> 1]);
+        } else {
+          pin_use(pr_t[0]);
+          pin_use(ds_t[0]);
         }
-    }
+      }
+    };
+    bf16x8 carry[2];
+    // one phase: the M products of group G, half VH's vector work (VH < 0: none), and the first two
+    // operands of group NG (NG < 0: none) read at its end
+    auto phase = [&](auto G, auto VH, auto NG, bool pin) __attribute__((always_inline)) {
+      constexpr int vh = decltype(VH)::value, ng = decltype(NG)::value;
+      bf16x8 op[M];
+      if (pin) {
+        op[0] = carry[0];
+        op[1] = carry[1];
+      } else {
+        op[0] = operand(G, 0);
+        op[1] = operand(G, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < M; k++) {
+        if (k + 2 < M) {
+          op[k + 2] = operand(G, k + 2);
+        } else if constexpr (ng >= 0) {
+          carry[k + 2 - M] = operand(IC<(ng < 0 ? 0 : ng)>{}, k + 2 - M);
+        }
+        product(G, k, op[k]);
+        if constexpr (vh >= 0) softmax_grad(vh, k * E);
+        if constexpr (vh == 0) {
+          if (k >= M - 4) read_ml(1, k - (M - 4));  // half 1's rows, for the next phase
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    phase(IC<0>{}, IC<-1>{}, IC<1>{}, false);
+    phase(IC<1>{}, IC<0>{}, IC<2>{}, true);
+    phase(IC<2>{}, IC<1>{}, IC<3>{}, true);
+    phase(IC<3>{}, IC<-1>{}, IC<-1>{}, true);
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
   if (key < key_end) {
