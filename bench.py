@@ -439,8 +439,8 @@ def backward_bench(a):
     import quantized_attention_tiled_amd as qa
     from workloads import CONFIGS, make_workload
     qa.load()
-    if CONFIGS[a.config]["kind"] != "dense" or CONFIGS[a.config].get("layout", "BNSD") != "BNSD":
-        log("--backward takes a dense BNSD config")
+    if CONFIGS[a.config]["kind"] != "dense":
+        log("--backward takes a dense config (BNSD or TND)")
         return 2
     w = make_workload(a.config, S=a.seq) if a.seq else make_workload(a.config)
     dev = torch.device("cuda:0")
@@ -451,14 +451,18 @@ def backward_bench(a):
     q, k, v = up(w.q), up(w.k), up(w.v)
     gen = torch.Generator(device=dev).manual_seed(77)
     do = torch.randn(q.shape, generator=gen, device=dev).to(torch.bfloat16)
-    mode = a.bwd_mode
-    o, m, l = qa.attn_fwd(q, k, v, scale=w.scale, sparse_mode=mode)
+    tnd = w.layout == "TND"
+    mode = w.sparse_mode if tnd else a.bwd_mode
+    kw = dict(scale=w.scale, sparse_mode=mode)
+    if tnd:
+        kw.update(layout="TND", cu_seqlens_q=w.cu_seqlens_q.tolist(), cu_seqlens_kv=w.cu_seqlens_kv.tolist())
+    o, m, l = qa.attn_fwd(q, k, v, **kw)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(2 * w.B * w.Nq * w.Sq, dtype=torch.float32, device=dev)
+    ws = torch.empty(2 * m.numel(), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        qa.attn_bwd(q, k, v, o, do, m, l, scale=w.scale, sparse_mode=mode, dq=dq, dk=dk, dv=dv, workspace=ws)
+        qa.attn_bwd(q, k, v, o, do, m, l, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
 
     for _ in range(a.warmup):
         step()
@@ -471,7 +475,11 @@ def backward_bench(a):
     torch.cuda.synchronize()
     per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)])
     ms = ev[0].elapsed_time(ev[a.steps]) / a.steps
-    pairs = w.B * w.Nq * (w.Sq * (w.Sq + 1) // 2 if mode == 2 else w.Sq * w.Skv)
+    if tnd:  # equal query and key lengths per sequence, so both causal modes keep L (L + 1) / 2 pairs
+        lens = np.diff(w.cu_seqlens_q)
+        pairs = w.Nq * int(sum(int(L) * (int(L) + 1) // 2 if mode in (2, 3) else int(L) * int(L) for L in lens))
+    else:
+        pairs = w.B * w.Nq * (w.Sq * (w.Sq + 1) // 2 if mode == 2 else w.Sq * w.Skv)
     std, exe = 10 * w.D * pairs, 14 * w.D * pairs
     line = {"metric": "attention bwd TFLOP/s (dQ, dK, dV; 10 D flops per pair), % bf16 MFMA peak",
             "value": round(std / ms / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,

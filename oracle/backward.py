@@ -50,11 +50,31 @@ def softmax_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: 
 
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float, *,
-                       sparse_mode: int = 0, atten_mask: Optional[np.ndarray] = None,
-                       pre_tokens: Optional[int] = None, next_tokens: Optional[int] = None):
-    """BNSD gradients: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D(v)], do [B, Nq, Sq, Dv].
+                       layout: str = "BNSD", sparse_mode: int = 0, atten_mask: Optional[np.ndarray] = None,
+                       pre_tokens: Optional[int] = None, next_tokens: Optional[int] = None,
+                       cu_seqlens_q: Optional[np.ndarray] = None, cu_seqlens_kv: Optional[np.ndarray] = None):
+    """Gradients (dq, dk, dv) shaped like q, k, v.
 
-    Returns (dq, dk, dv) shaped like q, k, v."""
+    BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D(v)], do [B, Nq, Sq, Dv].
+    TND:  q [T, Nq, D], k/v [Tk, Nkv, D(v)], do [T, Nq, Dv], with cumulative lengths; each
+          sequence is its own problem (causal anchors counted inside it)."""
+    if layout == "TND":
+        if atten_mask is not None:
+            raise ValueError("TND takes no boolean mask")
+        dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+        for b in range(len(cu_seqlens_q) - 1):
+            q0, q1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+            k0, k1 = int(cu_seqlens_kv[b]), int(cu_seqlens_kv[b + 1])
+            gq, gk, gv = attention_backward(q[q0:q1].transpose(1, 0, 2)[None], k[k0:k1].transpose(1, 0, 2)[None],
+                                            v[k0:k1].transpose(1, 0, 2)[None], do[q0:q1].transpose(1, 0, 2)[None],
+                                            scale, sparse_mode=sparse_mode, pre_tokens=pre_tokens,
+                                            next_tokens=next_tokens)
+            dq[q0:q1] = gq[0].transpose(1, 0, 2)
+            dk[k0:k1] = gk[0].transpose(1, 0, 2)
+            dv[k0:k1] = gv[0].transpose(1, 0, 2)
+        return dq, dk, dv
+    if layout != "BNSD":
+        raise ValueError("layout must be BNSD or TND")
     B, Nq, Sq, D = q.shape
     Nkv, Skv = k.shape[1], k.shape[2]
     if Nq % Nkv:

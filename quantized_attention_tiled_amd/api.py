@@ -350,22 +350,37 @@ def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scal
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
              softmax_max: torch.Tensor, softmax_sum: torch.Tensor, *, scale: float = 1.0, sparse_mode: int = 0,
+             layout: str = "BNSD", cu_seqlens_q: Optional[Sequence[int]] = None,
+             cu_seqlens_kv: Optional[Sequence[int]] = None, head_num: Optional[int] = None,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None):
-    """Gradients (dq, dk, dv) of attn_fwd for BNSD bf16 q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D], given the
-    forward's out and softmax_max / softmax_sum and the output gradient dout (shaped like out).
-    ``workspace``: optional fp32 device tensor of at least 2 * B * Nq * Sq elements."""
+    """Gradients (dq, dk, dv) of attn_fwd on bf16 q, k, v in any layout attn_fwd takes (shapes as
+    there, D = Dv), given the forward's out and softmax_max / softmax_sum and the output gradient
+    dout (shaped like out). ``workspace``: optional fp32 device tensor of at least
+    attn_bwd_workspace_bytes / 4 elements (2 B Nq Sq; TND: 2 Nq T)."""
     lib = load()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _require(t, n, torch.bfloat16, dev)
     for t, n in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
         _require(t, n, torch.float32, dev)
-    lay, B, Nq, Sq, Nkv, Skv, D = _dims("BNSD", q, k, None)
+    cu_q = cu_kv = None
+    if layout == "TND":
+        Sq, Nq, D = q.shape
+        Skv, Nkv = k.shape[0], k.shape[1]
+        if k.dim() != 3 or k.shape[2] != D:
+            raise ValueError("k/v must be [Tk, Nkv, D] matching q")
+        cu_q, cu_kv = _cu(cu_seqlens_q), _cu(cu_seqlens_kv if cu_seqlens_kv is not None else cu_seqlens_q)
+        if cu_q is None or len(cu_q) != len(cu_kv):
+            raise ValueError("TND needs cu_seqlens_q (and cu_seqlens_kv of the same length)")
+        B, lay, ml_shape = len(cu_q) - 1, LAYOUT_TND, (Nq, Sq)
+    else:
+        lay, B, Nq, Sq, Nkv, Skv, D = _dims(layout, q, k, head_num)
+        ml_shape = (B, Nq, Sq)
     if v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("v must match k, out and dout must match q")
-    if tuple(softmax_max.shape) != (B, Nq, Sq) or tuple(softmax_sum.shape) != (B, Nq, Sq):
-        raise ValueError("softmax_max / softmax_sum must be [B, Nq, Sq]")
+    if tuple(softmax_max.shape) != ml_shape or tuple(softmax_sum.shape) != ml_shape:
+        raise ValueError(f"softmax_max / softmax_sum must be {ml_shape}")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -373,7 +388,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         _require(t, n, torch.bfloat16, dev)
         if t.shape != ref.shape:
             raise ValueError(f"{n} must be shaped like {tuple(ref.shape)}")
-    desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode)
+    desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
+                     cu_q=cu_q, cu_kv=cu_kv)
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(desc)) // 4
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.float32, device=dev)

@@ -72,20 +72,37 @@ struct TileLoad {
   using T = BTile<D>;
   static constexpr int kRowsPerLoad = 1024 / T::kRowBytes;
   static constexpr int kLoads = kTileRows / (4 * kRowsPerLoad);  // loads per wave per tile
-  uint32_t lane_off;
-  __device__ explicit TileLoad(int wave, int lane) {
+  uint32_t lane_off, stride;  // stride: bytes between consecutive rows in HBM
+  __device__ TileLoad(int wave, int lane, uint32_t row_stride) : stride(row_stride) {
     const int row = wave * kRowsPerLoad + lane / T::kChunks;
-    lane_off = (uint32_t)(row * T::kRowBytes) + (uint32_t)(((lane % T::kChunks) ^ T::swz(row)) << 4);
+    lane_off = (uint32_t)row * stride + (uint32_t)(((lane % T::kChunks) ^ T::swz(row)) << 4);
   }
   // tile whose first row is `row0` of the buffer, into LDS at `lds`
   __device__ void issue(const rsrc4& rsrc, uint8_t* lds, int row0, int wave) const {
-    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(row0) * (uint32_t)T::kRowBytes;
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(row0) * stride;
 #pragma unroll
     for (int n = 0; n < kLoads; n++)
       load_lds16(rsrc, lds_address(lds + (4 * n + wave) * 1024), lane_off,
-                 soff + (uint32_t)(n * 4 * kRowsPerLoad * T::kRowBytes));
+                 soff + (uint32_t)(n * 4 * kRowsPerLoad) * stride);
   }
 };
+
+// bytes of a buffer of `rows` rows `stride` bytes apart whose last row is `row_bytes` long
+__device__ __forceinline__ uint32_t extent(int rows, uint32_t stride, int row_bytes) {
+  return rows > 0 ? (uint32_t)(rows - 1) * stride + (uint32_t)row_bytes : 0u;
+}
+
+// Sequence s and block index within it of per-head block number t, for blocks of 128 rows of
+// the sequences given by cumulative lengths cu (nseq entries + 1).
+__device__ __forceinline__ void seq_block(const int* cu, int nseq, int t, int& s, int& blk) {
+  int pre = 0;
+  for (s = 0; s < nseq - 1; s++) {
+    const int nb = (cu[s + 1] - cu[s] + kBlock - 1) / kBlock;
+    if (t < pre + nb) break;
+    pre += nb;
+  }
+  blk = t - pre;
+}
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -143,13 +160,17 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[D 
 // ---- per-row preparation: lse2 = m log2(e) + log2(l) (+inf when l = 0) and D = dO . O ----
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
-  const int64_t rows = (int64_t)p.B * p.Nq * p.Sq;
+  const int64_t rows = p.rows;
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;  // 16 lanes per row, D / 16 elements each
   float acc = 0.f;
   if (row < rows) {
-    const uint16_t* o = p.o + row * D;
-    const uint16_t* g = p.dout + row * D;
+    // row = (b Nq + h) Sq + i for BNSD, h T + t for TND (one "batch" of T tokens)
+    const int64_t i = row % p.Sq, bh = row / p.Sq;
+    const int64_t h = bh % p.Nq, b = bh / p.Nq;
+    const int64_t e0 = b * p.q_sb + h * p.q_sh + i * p.q_ss;
+    const uint16_t* o = p.o + e0;
+    const uint16_t* g = p.dout + e0;
     constexpr int E = D / 16;  // 8 (D = 128) or 4 (D = 64) elements per lane
     if constexpr (E == 8) {
       const bf16x8 a = *(const bf16x8*)(o + sub * 8);
@@ -186,19 +207,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   const int l32 = lane & 31, hl = lane >> 5;
   const int item = xcd_remap(blockIdx.x, gridDim.x, p.total_items);
   if (item < 0) return;
-  const int QB = (p.Sq + kBlock - 1) / kBlock;
-  const int qb = item % QB;
-  const int bh = item / QB;  // b * Nq + h
-  const int b = bh / p.Nq, h = bh % p.Nq, g = h / p.group;
-  const int Lq = p.Sq, Lkv = p.Skv;
+  int b, h, qb, Lq, Lkv, q_tok0 = 0, kv_tok0 = 0;
+  if (p.nseq > 0) {  // TND: per-head q-blocks, sequence by sequence
+    h = item / p.q_tiles;
+    seq_block(p.cu_q, p.nseq, item % p.q_tiles, b, qb);
+    q_tok0 = p.cu_q[b];
+    kv_tok0 = p.cu_kv[b];
+    Lq = p.cu_q[b + 1] - q_tok0;
+    Lkv = p.cu_kv[b + 1] - kv_tok0;
+    b = 0;  // the tokens of every sequence sit in one buffer
+  } else {
+    const int QB = (p.Sq + kBlock - 1) / kBlock;
+    qb = item % QB;
+    b = item / QB / p.Nq;
+    h = item / QB % p.Nq;
+    Lq = p.Sq;
+    Lkv = p.Skv;
+  }
+  const int g = h / p.group;
   const int row_end = min((qb + 1) * kBlock, Lq);
   const int q = qb * kBlock + wave * 32 + l32;  // this lane's query row
   const int off = CAUSAL ? (p.causal == 3 ? Lkv - Lq : 0) : 0;
 
-  const uint16_t* qp = p.q + (int64_t)bh * Lq * D;
-  const uint16_t* gp = p.dout + (int64_t)bh * Lq * D;
-  const uint16_t* kp = p.k + ((int64_t)b * p.Nkv + g) * Lkv * D;
-  const uint16_t* vp = p.v + ((int64_t)b * p.Nkv + g) * Lkv * D;
+  const int64_t qo = b * p.q_sb + h * p.q_sh + q_tok0 * p.q_ss;
+  const int64_t ko = b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
+  const uint16_t* qp = p.q + qo;
+  const uint16_t* gp = p.dout + qo;
+  const uint16_t* kp = p.k + ko;
+  const uint16_t* vp = p.v + ko;
 
   // Q^T and dO^T as B operands: lane (hl, l32) holds row q's chunk 2 t + hl for k-step t
   bf16x8 qreg[DT], greg[DT];
@@ -206,11 +242,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     const int r = max(min(q, row_end - 1), 0);
 #pragma unroll
     for (int t = 0; t < DT; t++) {
-      qreg[t] = *(const bf16x8*)(qp + (int64_t)r * D + (2 * t + hl) * 8);
-      greg[t] = *(const bf16x8*)(gp + (int64_t)r * D + (2 * t + hl) * 8);
+      qreg[t] = *(const bf16x8*)(qp + (int64_t)r * p.q_ss + (2 * t + hl) * 8);
+      greg[t] = *(const bf16x8*)(gp + (int64_t)r * p.q_ss + (2 * t + hl) * 8);
     }
   }
-  const int64_t ml = (int64_t)bh * Lq + max(min(q, row_end - 1), 0);
+  const int64_t ml = b * p.ml_sb + h * p.ml_sh + q_tok0 + max(min(q, row_end - 1), 0);
   const float lse2 = q < row_end ? p.lse2[ml] : kPosInf;
   const float dlt = q < row_end ? p.delta[ml] : 0.f;
 
@@ -220,9 +256,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 
   const int kv_end = CAUSAL ? min(Lkv, row_end - 1 + off + 1) : Lkv;
   const int ntiles = (row_end > qb * kBlock && kv_end > 0) ? (kv_end + kTileRows - 1) / kTileRows : 0;
-  const TileLoad<D> ld(wave, lane);
-  const rsrc4 k_rsrc = make_rsrc(kp, (uint32_t)Lkv * T::kRowBytes);
-  const rsrc4 v_rsrc = make_rsrc(vp, (uint32_t)Lkv * T::kRowBytes);
+  const TileLoad<D> ld(wave, lane, (uint32_t)p.k_ss * 2);
+  const rsrc4 k_rsrc = make_rsrc(kp, extent(Lkv, ld.stride, T::kRowBytes));
+  const rsrc4 v_rsrc = make_rsrc(vp, extent(Lkv, ld.stride, T::kRowBytes));
   if (ntiles > 0) {
     ld.issue(k_rsrc, smem, 0, wave);
     ld.issue(v_rsrc, smem + 2 * T::kBytes, 0, wave);
@@ -324,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     phase(IC<3>{}, IC<-1>{}, IC<-1>{}, true);
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
-  if (q < row_end) store_rows<D>(p.dq + ((int64_t)bh * Lq + q) * D, acc, p.scale, hl);
+  if (q < row_end) store_rows<D>(p.dq + qo + (int64_t)q * p.q_ss, acc, p.scale, hl);
 }
 
 // ---- dK, dV: one 128-key kv-block of kv-head g per workgroup, 4 waves x 32 keys ----
@@ -341,26 +377,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int l32 = lane & 31, hl = lane >> 5;
   const int item = xcd_remap(blockIdx.x, gridDim.x, p.total_items);
   if (item < 0) return;
-  const int KB = (p.Skv + kBlock - 1) / kBlock;
-  const int kb = item % KB;
-  const int bg = item / KB;  // b * Nkv + g
-  const int b = bg / p.Nkv, g = bg % p.Nkv;
-  const int Lq = p.Sq, Lkv = p.Skv;
+  int b, g, kb, Lq, Lkv, q_tok0 = 0, kv_tok0 = 0;
+  if (p.nseq > 0) {  // TND: per-kv-head kv-blocks, sequence by sequence
+    g = item / p.k_tiles;
+    seq_block(p.cu_kv, p.nseq, item % p.k_tiles, b, kb);
+    q_tok0 = p.cu_q[b];
+    kv_tok0 = p.cu_kv[b];
+    Lq = p.cu_q[b + 1] - q_tok0;
+    Lkv = p.cu_kv[b + 1] - kv_tok0;
+    b = 0;  // the tokens of every sequence sit in one buffer
+  } else {
+    const int KB = (p.Skv + kBlock - 1) / kBlock;
+    kb = item % KB;
+    b = item / KB / p.Nkv;
+    g = item / KB % p.Nkv;
+    Lq = p.Sq;
+    Lkv = p.Skv;
+  }
   const int key_end = min((kb + 1) * kBlock, Lkv);
   const int wkey0 = kb * kBlock + wave * 32;
   const int key = wkey0 + l32;  // this lane's key
   const int off = CAUSAL ? (p.causal == 3 ? Lkv - Lq : 0) : 0;
 
-  const uint16_t* kp = p.k + (int64_t)bg * Lkv * D;
-  const uint16_t* vp = p.v + (int64_t)bg * Lkv * D;
+  const int64_t ko = b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
+  const uint16_t* kp = p.k + ko;
+  const uint16_t* vp = p.v + ko;
   // K^T and V^T as B operands: lane (hl, l32) holds key's chunk 2 t + hl for k-step t
   bf16x8 kreg[DT], vreg[DT];
   {
     const int r = max(min(key, key_end - 1), 0);
 #pragma unroll
     for (int t = 0; t < DT; t++) {
-      kreg[t] = *(const bf16x8*)(kp + (int64_t)r * D + (2 * t + hl) * 8);
-      vreg[t] = *(const bf16x8*)(vp + (int64_t)r * D + (2 * t + hl) * 8);
+      kreg[t] = *(const bf16x8*)(kp + (int64_t)r * p.k_ss + (2 * t + hl) * 8);
+      vreg[t] = *(const bf16x8*)(vp + (int64_t)r * p.k_ss + (2 * t + hl) * 8);
     }
   }
   f32x16 dk[DB], dv[DB];
@@ -375,20 +424,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int t_first = q_first / kTileRows;
   const int ntiles = key_end > kb * kBlock ? max(0, (Lq + kTileRows - 1) / kTileRows - t_first) : 0;
   const int total = ntiles * p.group;  // tiles u = hh * ntiles + it over the group's q-heads
-  const TileLoad<D> ld(wave, lane);
-  const int64_t rows_all = (int64_t)p.B * p.Nq * Lq;
+  const TileLoad<D> ld(wave, lane, (uint32_t)p.q_ss * 2);
+  const int64_t rows_all = p.rows;
   // lse2 and rowsum(dO * O) sit back to back in the workspace (delta = lse2 + rows_all)
   const rsrc4 ml_rsrc = make_rsrc(p.lse2, (uint32_t)(rows_all * 8));
+  const uint32_t q_bytes = extent(Lq, ld.stride, T::kRowBytes);
   auto issue = [&](int u) __attribute__((always_inline)) {
     const int hh = u / ntiles, row0 = (t_first + u % ntiles) * kTileRows;
-    const int64_t bh = (int64_t)b * p.Nq + g * p.group + hh;
-    const uint32_t bytes = (uint32_t)Lq * T::kRowBytes;
-    ld.issue(make_rsrc(p.q + bh * Lq * D, bytes), smem + (u & 1) * T::kBytes, row0, wave);
-    ld.issue(make_rsrc(p.dout + bh * Lq * D, bytes), smem + (2 + (u & 1)) * T::kBytes, row0, wave);
+    const int h = g * p.group + hh;
+    const int64_t qo = b * p.q_sb + h * p.q_sh + q_tok0 * p.q_ss;
+    ld.issue(make_rsrc(p.q + qo, q_bytes), smem + (u & 1) * T::kBytes, row0, wave);
+    ld.issue(make_rsrc(p.dout + qo, q_bytes), smem + (2 + (u & 1)) * T::kBytes, row0, wave);
     if (wave == 0) {
       // lanes 0..15: 4 lse2 values each, lanes 16..31: 4 rowsum values, lanes 32..63 read past
       // the extent (zeros into the unused half of the 1 KiB)
-      const int64_t e = lane < 16 ? bh * Lq + row0 + 4 * lane : rows_all + bh * Lq + row0 + 4 * (lane - 16);
+      const int64_t mb = b * p.ml_sb + h * p.ml_sh + q_tok0 + row0;
+      const int64_t e = lane < 16 ? mb + 4 * lane : rows_all + mb + 4 * (lane - 16);
       const uint32_t voff = lane < 32 ? (uint32_t)(e * 4) : (uint32_t)(rows_all * 8);
       load_lds16(ml_rsrc, lds_address(smem + 4 * T::kBytes + (u & 1) * 1024), voff, 0u);
     }
@@ -516,19 +567,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
   if (key < key_end) {
-    store_rows<D>(p.dk + ((int64_t)bg * Lkv + key) * D, dk, p.scale, hl);
-    store_rows<D>(p.dv + ((int64_t)bg * Lkv + key) * D, dv, 1.f, hl);
+    store_rows<D>(p.dk + ko + (int64_t)key * p.k_ss, dk, p.scale, hl);
+    store_rows<D>(p.dv + ko + (int64_t)key * p.k_ss, dv, 1.f, hl);
   }
 }
 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.Nq * p.Sq;
-  if (rows > 0) hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
+  if (p.rows > 0)
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((p.rows + 15) / 16)), dim3(256), 0, stream, p);
   BwdParams pq = p;
-  pq.total_items = p.B * p.Nq * ((p.Sq + kBlock - 1) / kBlock);
+  pq.total_items = p.nseq > 0 ? p.Nq * p.q_tiles : p.B * p.Nq * ((p.Sq + kBlock - 1) / kBlock);
   BwdParams pk = p;
-  pk.total_items = p.B * p.Nkv * ((p.Skv + kBlock - 1) / kBlock);
+  pk.total_items = p.nseq > 0 ? p.Nkv * p.k_tiles : p.B * p.Nkv * ((p.Skv + kBlock - 1) / kBlock);
   const bool causal = p.causal == 2 || p.causal == 3;
   if (pq.total_items > 0) {
     if (causal)

@@ -379,7 +379,8 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
 
 size_t attn_bwd_workspace_bytes(const qattn_desc* desc) {
   if (!desc || desc->struct_size != sizeof(qattn_desc) || desc->B < 0 || desc->Nq < 0 || desc->Sq < 0) return 0;
-  return (size_t)2 * sizeof(float) * (size_t)desc->B * (size_t)desc->Nq * (size_t)desc->Sq;
+  const size_t rows = (size_t)(desc->layout == QATTN_LAYOUT_TND ? 1 : desc->B) * (size_t)desc->Nq * (size_t)desc->Sq;
+  return 2 * sizeof(float) * rows;
 }
 
 int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
@@ -387,9 +388,8 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
              qattn_bf16* dq, qattn_bf16* dk, qattn_bf16* dv, float* workspace, void* stream) {
   qattn::FwdParams f{};
   int total_qb = 0;
-  int rc = setup_common(desc, f, false, true, &total_qb);
+  int rc = setup_common(desc, f, true, true, &total_qb);
   if (rc) return rc;
-  if (desc->layout != QATTN_LAYOUT_BNSD) return fail(QATTN_UNSUPPORTED, "attn_bwd needs the BNSD layout");
   if (desc->dtype != QATTN_DTYPE_BF16) return fail(QATTN_UNSUPPORTED, "attn_bwd takes bf16 tensors");
   if (f.Dv != f.D) return fail(QATTN_UNSUPPORTED, "attn_bwd needs Dv == D");
   if (desc->atten_mask || desc->pre_tokens != INT32_MAX || desc->next_tokens != INT32_MAX || f.actual)
@@ -412,7 +412,8 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.dout = dout;
   p.m_in = softmax_max;
   p.l_in = softmax_sum;
-  const int64_t rows = (int64_t)desc->B * desc->Nq * desc->Sq;
+  const bool tnd = desc->layout == QATTN_LAYOUT_TND;
+  const int64_t rows = (int64_t)(tnd ? 1 : desc->B) * desc->Nq * desc->Sq;
   p.lse2 = workspace;
   p.delta = workspace + rows;
   p.dq = dq;
@@ -428,10 +429,37 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.causal = desc->sparse_mode;
   p.scale = f.scale;
   p.c = f.c;
-  const int64_t items_q = (int64_t)desc->B * desc->Nq * ((desc->Sq + qattn::kBlock - 1) / qattn::kBlock);
-  const int64_t items_k = (int64_t)desc->B * desc->Nkv * ((desc->Skv + qattn::kBlock - 1) / qattn::kBlock);
-  // the kernels address the workspace (8 bytes per row) through 32-bit byte offsets
-  if (items_q > (int64_t)0x7fffff00 || items_k > (int64_t)0x7fffff00 || rows * 8 >= ((int64_t)1 << 32))
+  p.q_sb = f.q_sb;
+  p.q_sh = f.q_sh;
+  p.q_ss = f.q_ss;
+  p.k_sb = f.k_sb;
+  p.k_sh = f.k_sh;
+  p.k_ss = f.k_ss;
+  p.ml_sb = f.ml_sb;
+  p.ml_sh = f.ml_sh;
+  p.rows = rows;
+  p.nseq = tnd ? desc->B : 0;
+  int64_t items_q, items_k;
+  if (tnd) {
+    p.q_tiles = p.k_tiles = 0;
+    for (int i = 0; i <= desc->B; i++) {
+      p.cu_q[i] = f.cu_q[i];
+      p.cu_kv[i] = f.cu_kv[i];
+    }
+    for (int i = 0; i < desc->B; i++) {
+      p.q_tiles += (f.cu_q[i + 1] - f.cu_q[i] + qattn::kBlock - 1) / qattn::kBlock;
+      p.k_tiles += (f.cu_kv[i + 1] - f.cu_kv[i] + qattn::kBlock - 1) / qattn::kBlock;
+    }
+    items_q = (int64_t)desc->Nq * p.q_tiles;
+    items_k = (int64_t)desc->Nkv * p.k_tiles;
+  } else {
+    items_q = (int64_t)desc->B * desc->Nq * ((desc->Sq + qattn::kBlock - 1) / qattn::kBlock);
+    items_k = (int64_t)desc->B * desc->Nkv * ((desc->Skv + qattn::kBlock - 1) / qattn::kBlock);
+  }
+  // the kernels address the workspace (8 bytes per row) and the query rows of one head through
+  // 32-bit byte offsets
+  if (items_q > (int64_t)0x7fffff00 || items_k > (int64_t)0x7fffff00 || rows * 8 >= ((int64_t)1 << 32) ||
+      ((int64_t)std::max(desc->Sq, 1) - 1) * f.q_ss * 2 + 2 * desc->D > (int64_t)INT32_MAX)
     return fail(QATTN_UNSUPPORTED, "problem too large for one launch");
   return hip_status(qattn::launch_attn_bwd(p, (hipStream_t)stream), "attn_bwd launch");
 }

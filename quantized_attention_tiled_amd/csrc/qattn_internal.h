@@ -67,7 +67,7 @@ struct FwdParams {
   int cu_kv[kMaxSeqs + 1];
 };
 
-// Everything a backward launch needs (BNSD, bf16, D = Dv), passed by value.
+// Everything a backward launch needs (BNSD or TND, bf16, D = Dv), passed by value.
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -81,11 +81,21 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  // element strides of batch, head and token: q_* for q, o, dout and dq; k_* for k, v, dk and dv;
+  // ml_* for softmax max / sum and the workspace rows (token stride 1)
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t ml_sb, ml_sh;
+  int64_t rows;       // rows of softmax max / sum: B Nq Sq (BNSD) or Nq T (TND)
   int B, Nq, Nkv, group, Sq, Skv, D;
   int causal;         // 0, 2 top-left, 3 bottom-right
   int total_items;
+  int q_tiles, k_tiles;  // TND: q-blocks / kv-blocks per head, summed over the sequences
   float scale;
   float c;            // scale * log2(e)
+  int nseq;           // TND: sequences; 0 for BNSD
+  int cu_q[kMaxSeqs + 1];
+  int cu_kv[kMaxSeqs + 1];
 };
 
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream);

@@ -84,3 +84,50 @@ def test_backward_deterministic(qa):
         torch.cuda.synchronize()
         for a, b in zip(g1, g2):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode,Nq,Nkv,D", [(3, 4, 2, 128), (0, 2, 2, 64), (2, 8, 2, 128)])
+def test_backward_tnd(qa, mode, Nq, Nkv, D):
+    """Varlen TND: sequences of unequal query and key lengths, including an empty and a one-token
+    sequence; each sequence is its own problem."""
+    lq, lk = [300, 0, 1, 130, 64], [280, 5, 40, 130, 200]
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    what = f"bwd TND mode={mode} Nq={Nq} Nkv={Nkv} D={D}"
+    banner(what)
+    qb = random_bf16(41, (cq[-1], Nq, D))
+    kb = random_bf16(42, (ck[-1], Nkv, D))
+    vb = random_bf16(43, (ck[-1], Nkv, D))
+    gb = random_bf16(44, (cq[-1], Nq, D))
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(gb)
+    kw = dict(scale=scale, sparse_mode=mode, layout="TND", cu_seqlens_q=cq.tolist(), cu_seqlens_kv=ck.tolist())
+    o, m, l = qa.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = qa.attn_bwd(q, k, v, o, do, m, l, **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(f64(qb), f64(kb), f64(vb), f64(gb), scale, layout="TND", sparse_mode=mode,
+                                           cu_seqlens_q=cq, cu_seqlens_kv=ck)
+    _check(dq, rq, what + " dQ")
+    _check(dk, rk, what + " dK")
+    _check(dv, rv, what + " dV")
+
+
+@pytest.mark.parametrize("layout", ["BSND", "BSH", "SBH"])
+def test_backward_layouts_match_bnsd(qa, layout):
+    """The batched layouts differ from BNSD only in the strides: the gradients must be the same bits."""
+    B, Nq, Nkv, S, D = 2, 4, 2, 300, 128
+    banner(f"bwd layout {layout}")
+    fwd, grads, _ = _run(qa, B, Nq, Nkv, S, S, D, 3, 55)
+    q, k, v, o, do, m, l, scale = fwd
+
+    def to(x):  # BNSD -> layout
+        if layout == "BSND":
+            return x.transpose(1, 2).contiguous()
+        y = x.permute(0, 2, 1, 3) if layout == "BSH" else x.permute(2, 0, 1, 3)
+        return y.reshape(y.shape[0], y.shape[1], -1).contiguous()
+
+    kw = dict(scale=scale, sparse_mode=3, layout=layout, head_num=Nq)
+    g2 = qa.attn_bwd(to(q), to(k), to(v), to(o), to(do), m, l, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(grads, g2):
+        assert torch.equal(to(a).view(torch.int16), b.view(torch.int16))

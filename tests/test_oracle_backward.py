@@ -108,3 +108,18 @@ def test_constant_values_closed_form():
     p = np.exp(s - s.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
     np.testing.assert_allclose(dv[0, 0], p.T @ do[0, 0], rtol=1e-12, atol=1e-14)
+
+
+def test_tnd_finite_differences():
+    """TND: two sequences of different lengths, bottom-right causal, GQA; finite differences of the
+    TND forward oracle (each sequence anchored inside itself)."""
+    lq, lk, Nq, Nkv, D = [3, 2], [2, 4], 2, 1, 2
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    q, k, v = RNG.normal(size=(cq[-1], Nq, D)), RNG.normal(size=(ck[-1], Nkv, D)), RNG.normal(size=(ck[-1], Nkv, D))
+    do = RNG.normal(size=(cq[-1], Nq, D))
+    kw = dict(layout="TND", sparse_mode=3, cu_seqlens_q=cq, cu_seqlens_kv=ck)
+    dq, dk, dv = attention_backward(q, k, v, do, 0.9, **kw)
+    fq, fk, fv = _finite_diff(q, k, v, do, 0.9, **kw)
+    for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+        np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-8)
