@@ -446,11 +446,14 @@ def backward_bench(a):
     dev = torch.device("cuda:0")
 
     def up(bits):
+        if a.dtype == "fp16":  # the same values as float16 (bf16 -> fp16 is exact in this range)
+            from workloads import bf16_bits_to_f32
+            return torch.from_numpy(bf16_bits_to_f32(bits).astype(np.float16)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v = up(w.q), up(w.k), up(w.v)
     gen = torch.Generator(device=dev).manual_seed(77)
-    do = torch.randn(q.shape, generator=gen, device=dev).to(torch.bfloat16)
+    do = torch.randn(q.shape, generator=gen, device=dev).to(q.dtype)
     tnd = w.layout == "TND"
     mode = w.sparse_mode if tnd else a.bwd_mode
     kw = dict(scale=w.scale, sparse_mode=mode)
@@ -483,7 +486,7 @@ def backward_bench(a):
     std, exe = 10 * w.D * pairs, 14 * w.D * pairs
     line = {"metric": "attention bwd TFLOP/s (dQ, dK, dV; 10 D flops per pair), % bf16 MFMA peak",
             "value": round(std / ms / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
-            "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16",
+            "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": a.dtype,
             "data": "synthetic (seeded forward inputs; dO N(0,1) drawn on the GPU)",
             "config": {"workload": f"{a.config}: {w.description}" + (f" (S {w.Sq})" if a.seq else ""),
                        "sparse_mode": mode},

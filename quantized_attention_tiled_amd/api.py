@@ -354,14 +354,15 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
              cu_seqlens_kv: Optional[Sequence[int]] = None, head_num: Optional[int] = None,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None):
-    """Gradients (dq, dk, dv) of attn_fwd on bf16 q, k, v in any layout attn_fwd takes (shapes as
-    there, D = Dv), given the forward's out and softmax_max / softmax_sum and the output gradient
-    dout (shaped like out). ``workspace``: optional fp32 device tensor of at least
+    """Gradients (dq, dk, dv) of attn_fwd on bfloat16 or float16 q, k, v (one type) in any layout
+    attn_fwd takes (shapes as there, D = Dv), given the forward's out and softmax_max / softmax_sum
+    and the output gradient dout (shaped like out). ``workspace``: optional fp32 device tensor of at least
     attn_bwd_workspace_bytes / 4 elements (2 B Nq Sq; TND: 2 Nq T)."""
     lib = load()
     dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
-        _require(t, n, torch.bfloat16, dev)
+    dtype = _check_dtypes(q, k, v, dev)
+    for t, n in ((out, "out"), (dout, "dout")):
+        _require(t, n, q.dtype, dev)
     for t, n in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
         _require(t, n, torch.float32, dev)
     cu_q = cu_kv = None
@@ -385,11 +386,11 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
-        _require(t, n, torch.bfloat16, dev)
+        _require(t, n, q.dtype, dev)
         if t.shape != ref.shape:
             raise ValueError(f"{n} must be shaped like {tuple(ref.shape)}")
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
-                     cu_q=cu_q, cu_kv=cu_kv)
+                     cu_q=cu_q, cu_kv=cu_kv, dtype=dtype)
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(desc)) // 4
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.float32, device=dev)

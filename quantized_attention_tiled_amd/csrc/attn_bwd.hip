@@ -1,5 +1,5 @@
-// Backward of the fused, tiled bf16 attention for gfx950: dQ, dK, dV from Q, K, V, O, dO and the
-// forward's per-row softmax max and sum.
+// Backward of the fused, tiled 16-bit attention for gfx950 (bf16 or fp16): dQ, dK, dV from Q, K,
+// V, O, dO and the forward's per-row softmax max and sum.
 //
 // What it computes: the derivative of the fused attention guide's definition ("Ascend NPU fused
 // attention operator", section 2: O = Softmax(Mask(Q K^T scale)) V), which the guide presents as a
@@ -8,7 +8,7 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = sum_d dO_id O_id,
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernels, all on v_mfma_f32_32x32x16_bf16 where the work is a contraction:
+// Three kernels, all on v_mfma_f32_32x32x16_{bf16,f16} where the work is a contraction:
 //   * bwd_prep_kernel: per query row, lse2 = log2(sum) + max log2(e) (+inf for a row with no
 //     key, so its P is 0) and D = dO . O, into the caller's workspace (HBM-bound);
 //   * bwd_dq_kernel: one 128-row q-block of one head per workgroup, 32 rows per wave, looping
@@ -27,7 +27,6 @@
 namespace qattn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -37,17 +36,34 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kPosInf = __builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 packed 16-bit elements
 
-// two floats rounded to bf16 (nearest even) in one dword, low half first
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+// The 16-bit element type E of Q, K, V, O, dO and the gradients (bf16 or fp16): its MFMA on
+// 8-element operands held as raw dwords, and rounding of fp32 values to E (nearest even).
+template <typename E>
+struct BElem;
+template <>
+struct BElem<__bf16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  __device__ static f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct BElem<_Float16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  __device__ static f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+};
+
+// two floats rounded to E in one dword, low half first
+template <typename E>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, typename BElem<E>::v2));
 }
 
 // Row-major 64 x D bf16 tile in LDS with 16-byte chunks XOR-swizzled by row. The swizzle repeats
@@ -109,7 +125,7 @@ __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70
 // A operand of a product whose contraction runs over tile rows: rows 16 kc .. 16 kc + 15 of the
 // tile, columns 32 db .. 32 db + 31 as the 32 output rows (transposed reads).
 template <int D>
-__device__ __forceinline__ bf16x8 read_tr(const uint8_t* lds, int kc, int db, int lane) {
+__device__ __forceinline__ u32x4 read_tr(const uint8_t* lds, int kc, int db, int lane) {
   using T = BTile<D>;
   const int grp = lane >> 4, sl = lane & 15;
   const int r0 = 16 * kc + 4 * (grp >> 1) + (sl >> 2);
@@ -117,13 +133,13 @@ __device__ __forceinline__ bf16x8 read_tr(const uint8_t* lds, int kc, int db, in
   const uint8_t* base = lds + T::at(r0, chunk) + 8 * (sl & 1);
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base);
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * T::kRowBytes));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // A operand of a product contracting over D: tile row `row` (the output row), k-step t.
 template <int D>
-__device__ __forceinline__ bf16x8 read_row(const uint8_t* lds, int row, int t, int hl) {
-  return *(const bf16x8*)(lds + BTile<D>::at(row, 2 * t + hl));
+__device__ __forceinline__ u32x4 read_row(const uint8_t* lds, int row, int t, int hl) {
+  return *(const u32x4*)(lds + BTile<D>::at(row, 2 * t + hl));
 }
 
 template <int V>
@@ -142,23 +158,23 @@ __device__ __forceinline__ void pin_use(const T& x) {
 // register r of a C-layout accumulator holds row 8 (r / 4) + 4 hl + r % 4 of its 32-row block
 __device__ __forceinline__ int c_row(int r, int hl) { return 8 * (r >> 2) + 4 * hl + (r & 3); }
 
-// Store the 32 x D^T accumulators of one wave (lane = output row l32, registers = columns) as bf16
+// Store the 32 x D^T accumulators of one wave (lane = output row l32, registers = columns) as E
 // rows of a row-major [rows, D] matrix, times `mul`.
-template <int D>
+template <typename E, int D>
 __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul, int hl) {
 #pragma unroll
   for (int db = 0; db < D / 32; db++)
 #pragma unroll
     for (int g4 = 0; g4 < 4; g4++) {
-      __bf16 v4[4];
+      E v4[4];
 #pragma unroll
-      for (int e = 0; e < 4; e++) v4[e] = (__bf16)(acc[db][4 * g4 + e] * mul);
+      for (int e = 0; e < 4; e++) v4[e] = (E)(acc[db][4 * g4 + e] * mul);
       *(uint2*)(dst + db * 32 + 8 * g4 + 4 * hl) = __builtin_bit_cast(uint2, v4);
     }
 }
 
 // ---- per-row preparation: lse2 = m log2(e) + log2(l) (+inf when l = 0) and D = dO . O ----
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
   const int64_t rows = p.rows;
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -171,19 +187,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
     const int64_t e0 = b * p.q_sb + h * p.q_sh + i * p.q_ss;
     const uint16_t* o = p.o + e0;
     const uint16_t* g = p.dout + e0;
-    constexpr int E = D / 16;  // 8 (D = 128) or 4 (D = 64) elements per lane
-    if constexpr (E == 8) {
-      const bf16x8 a = *(const bf16x8*)(o + sub * 8);
-      const bf16x8 b = *(const bf16x8*)(g + sub * 8);
+    constexpr int NE = D / 16;  // 8 (D = 128) or 4 (D = 64) elements per lane
+    typedef E ev __attribute__((ext_vector_type(NE)));
+    const ev ov = *(const ev*)(o + sub * NE);
+    const ev gv = *(const ev*)(g + sub * NE);
 #pragma unroll
-      for (int e = 0; e < 8; e++) acc += (float)a[e] * (float)b[e];
-    } else {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      const bf16x4 a = *(const bf16x4*)(o + sub * 4);
-      const bf16x4 b = *(const bf16x4*)(g + sub * 4);
-#pragma unroll
-      for (int e = 0; e < 4; e++) acc += (float)a[e] * (float)b[e];
-    }
+    for (int e = 0; e < NE; e++) acc += (float)ov[e] * (float)gv[e];
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
@@ -195,9 +204,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 }
 
 // ---- dQ: one 128-row q-block of head h per workgroup, 4 waves x 32 rows ----
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   using T = BTile<D>;
+  using EL = BElem<E>;
   constexpr int DT = D / 16, DB = D / 32;
   // K slots 0, 1, then V slots 0, 1: tile it + 1 loads while tile it is read
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * T::kBytes];
@@ -237,13 +247,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   const uint16_t* vp = p.v + ko;
 
   // Q^T and dO^T as B operands: lane (hl, l32) holds row q's chunk 2 t + hl for k-step t
-  bf16x8 qreg[DT], greg[DT];
+  u32x4 qreg[DT], greg[DT];
   {
     const int r = max(min(q, row_end - 1), 0);
 #pragma unroll
     for (int t = 0; t < DT; t++) {
-      qreg[t] = *(const bf16x8*)(qp + (int64_t)r * p.q_ss + (2 * t + hl) * 8);
-      greg[t] = *(const bf16x8*)(gp + (int64_t)r * p.q_ss + (2 * t + hl) * 8);
+      qreg[t] = *(const u32x4*)(qp + (int64_t)r * p.q_ss + (2 * t + hl) * 8);
+      greg[t] = *(const u32x4*)(gp + (int64_t)r * p.q_ss + (2 * t + hl) * 8);
     }
   }
   const int64_t ml = b * p.ml_sb + h * p.ml_sh + q_tok0 + max(min(q, row_end - 1), 0);
@@ -285,24 +295,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     //   D: the same products of h1.
     constexpr int MS = D / 8, MQ = D / 16;
     f32x16 s[2], dp[2];
-    u32x4 dsc[2][2];  // dS^T as bf16 B operands, two registers per dword
-    auto operand = [&](auto G, int k) __attribute__((always_inline)) -> bf16x8 {
+    u32x4 dsc[2][2];  // dS^T as E-typed B operands, two registers per dword
+    auto operand = [&](auto G, int k) __attribute__((always_inline)) -> u32x4 {
       constexpr int g_ = decltype(G)::value;
       if constexpr (g_ < 2)
         return read_row<D>((k & 1) ? vt : kt, 32 * g_ + l32, k >> 1, hl);
       else
         return read_tr<D>(kt, 2 * (g_ - 2) + k / DB, k % DB, lane);
     };
-    auto product = [&](auto G, int k, const bf16x8& a) __attribute__((always_inline)) {
+    auto product = [&](auto G, int k, const u32x4& a) __attribute__((always_inline)) {
       constexpr int g_ = decltype(G)::value;
       if constexpr (g_ < 2) {
         const int t = k >> 1;
         if (k & 1)
-          dp[g_] = mfma(a, greg[t], t == 0 ? f32x16{} : dp[g_]);
+          dp[g_] = EL::mfma(a, greg[t], t == 0 ? f32x16{} : dp[g_]);
         else
-          s[g_] = mfma(a, qreg[t], t == 0 ? f32x16{} : s[g_]);
+          s[g_] = EL::mfma(a, qreg[t], t == 0 ? f32x16{} : s[g_]);
       } else {
-        acc[k % DB] = mfma(a, __builtin_bit_cast(bf16x8, dsc[g_ - 2][k / DB]), acc[k % DB]);
+        acc[k % DB] = EL::mfma(a, dsc[g_ - 2][k / DB], acc[k % DB]);
       }
     };
     // dS^T of registers e0 .. e0 + n - 1 of half h (n even). Keys past the sequence are zero in K
@@ -318,16 +328,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
           if (CAUSAL && diag) pr = key0 + 32 * h + c_row(e + i, hl) <= q + off ? pr : 0.f;
           d2[i] = pr * (dp[h][e + i] - dlt);
         }
-        dsc[h][e >> 3][(e & 7) >> 1] = pack_bf16(d2[0], d2[1]);
+        dsc[h][e >> 3][(e & 7) >> 1] = pack2<E>(d2[0], d2[1]);
         pin_use(dsc[h][e >> 3][(e & 7) >> 1]);
       }
     };
-    bf16x8 carry[2];
+    u32x4 carry[2];
     auto phase = [&](auto G, auto VH, auto NG, bool pin) __attribute__((always_inline)) {
       constexpr int g_ = decltype(G)::value, vh = decltype(VH)::value, ng = decltype(NG)::value;
       constexpr int M = g_ < 2 ? MS : MQ;
       constexpr int NM = ng < 2 ? MS : MQ;
-      bf16x8 op[M];
+      u32x4 op[M];
       if (pin) {
         op[0] = carry[0];
         op[1] = carry[1];
@@ -360,13 +370,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     phase(IC<3>{}, IC<-1>{}, IC<-1>{}, true);
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
-  if (q < row_end) store_rows<D>(p.dq + qo + (int64_t)q * p.q_ss, acc, p.scale, hl);
+  if (q < row_end) store_rows<E, D>(p.dq + qo + (int64_t)q * p.q_ss, acc, p.scale, hl);
 }
 
 // ---- dK, dV: one 128-key kv-block of kv-head g per workgroup, 4 waves x 32 keys ----
-template <int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   using T = BTile<D>;
+  using EL = BElem<E>;
   constexpr int DT = D / 16, DB = D / 32;
   // Q slots 0, 1, dO slots 0, 1, then per slot 1 KiB holding the tile rows' lse2 (bytes 0..255)
   // and rowsum(dO * O) (256..511): tile u + 1 loads while tile u is read
@@ -403,13 +414,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const uint16_t* kp = p.k + ko;
   const uint16_t* vp = p.v + ko;
   // K^T and V^T as B operands: lane (hl, l32) holds key's chunk 2 t + hl for k-step t
-  bf16x8 kreg[DT], vreg[DT];
+  u32x4 kreg[DT], vreg[DT];
   {
     const int r = max(min(key, key_end - 1), 0);
 #pragma unroll
     for (int t = 0; t < DT; t++) {
-      kreg[t] = *(const bf16x8*)(kp + (int64_t)r * p.k_ss + (2 * t + hl) * 8);
-      vreg[t] = *(const bf16x8*)(vp + (int64_t)r * p.k_ss + (2 * t + hl) * 8);
+      kreg[t] = *(const u32x4*)(kp + (int64_t)r * p.k_ss + (2 * t + hl) * 8);
+      vreg[t] = *(const u32x4*)(vp + (int64_t)r * p.k_ss + (2 * t + hl) * 8);
     }
   }
   f32x16 dk[DB], dv[DB];
@@ -467,9 +478,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     //   D: the same products of h1.
     // A operands are read from LDS two slots ahead; scheduling barriers keep each slot's work.
     constexpr int M = D / 8;
-    constexpr int E = 16 / M;  // registers of one half handled per slot
+    constexpr int RPS = 16 / M;  // registers of one half handled per slot
     f32x16 s[2], dp[2];
-    u32x4 pc[2][2], dsc[2][2];  // P and dS as bf16 B operands, two registers per dword
+    u32x4 pc[2][2], dsc[2][2];  // P and dS as E-typed B operands, two registers per dword
     float lse_r[2][16], dlt_r[2][16];
     // lse2 and rowsum of group j (4 consecutive rows) of half h, read before they are needed
     auto read_ml = [&](int h, int j) __attribute__((always_inline)) {
@@ -481,7 +492,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int j = 0; j < 4; j++) read_ml(0, j);
     // A operand of product k of group G (0, 1: S / dP of half G; 2, 3: dV / dK of half G - 2)
-    auto operand = [&](auto G, int k) __attribute__((always_inline)) -> bf16x8 {
+    auto operand = [&](auto G, int k) __attribute__((always_inline)) -> u32x4 {
       constexpr int g_ = decltype(G)::value;
       if constexpr (g_ < 2) {
         return read_row<D>((k & 1) ? gt : qt, 32 * g_ + l32, k >> 1, hl);
@@ -490,28 +501,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
         return read_tr<D>((k & 1) ? qt : gt, 2 * (g_ - 2) + j / DB, j % DB, lane);
       }
     };
-    auto product = [&](auto G, int k, const bf16x8& a) __attribute__((always_inline)) {
+    auto product = [&](auto G, int k, const u32x4& a) __attribute__((always_inline)) {
       constexpr int g_ = decltype(G)::value;
       if constexpr (g_ < 2) {
         const int t = k >> 1;
         if (k & 1)
-          dp[g_] = mfma(a, vreg[t], t == 0 ? f32x16{} : dp[g_]);
+          dp[g_] = EL::mfma(a, vreg[t], t == 0 ? f32x16{} : dp[g_]);
         else
-          s[g_] = mfma(a, kreg[t], t == 0 ? f32x16{} : s[g_]);
+          s[g_] = EL::mfma(a, kreg[t], t == 0 ? f32x16{} : s[g_]);
       } else {
         const int j = k >> 1, c = j / DB, db = j % DB;
         if (k & 1)
-          dk[db] = mfma(a, __builtin_bit_cast(bf16x8, dsc[g_ - 2][c]), dk[db]);
+          dk[db] = EL::mfma(a, dsc[g_ - 2][c], dk[db]);
         else
-          dv[db] = mfma(a, __builtin_bit_cast(bf16x8, pc[g_ - 2][c]), dv[db]);
+          dv[db] = EL::mfma(a, pc[g_ - 2][c], dv[db]);
       }
     };
-    // P and dS of registers e0 .. e0 + E - 1 of half h; a register pair is packed to bf16 once
+    // P and dS of registers e0 .. e0 + RPS - 1 of half h; a register pair is packed to E once
     // both are done
     float pr_t[2], ds_t[2];
     auto softmax_grad = [&](int h, int e0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e = e0; e < e0 + E; e++) {
+      for (int e = e0; e < e0 + RPS; e++) {
         const int qr = 32 * h + c_row(e, hl);  // query row inside the tile
         // Rows past the sequence are zero in Q and dO, so their P and dS multiply zeros; their
         // lse2 slot holds another row's value, and the clamp at 0 (never binding for a real row,
@@ -521,8 +532,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
         pr_t[e & 1] = pr;
         ds_t[e & 1] = pr * (dp[h][e] - dlt_r[h][e]);
         if (e & 1) {
-          pc[h][e >> 3][(e & 7) >> 1] = pack_bf16(pr_t[0], pr_t[1]);
-          dsc[h][e >> 3][(e & 7) >> 1] = pack_bf16(ds_t[0], ds_t[1]);
+          pc[h][e >> 3][(e & 7) >> 1] = pack2<E>(pr_t[0], pr_t[1]);
+          dsc[h][e >> 3][(e & 7) >> 1] = pack2<E>(ds_t[0], ds_t[1]);
           pin_use(pc[h][e >> 3][(e & 7) >> 1]);
           pin_use(dsc[h][e >> 3][(e & 7) >> 1]);
         } else {
@@ -531,12 +542,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
         }
       }
     };
-    bf16x8 carry[2];
+    u32x4 carry[2];
     // one phase: the M products of group G, half VH's vector work (VH < 0: none), and the first two
     // operands of group NG (NG < 0: none) read at its end
     auto phase = [&](auto G, auto VH, auto NG, bool pin) __attribute__((always_inline)) {
       constexpr int vh = decltype(VH)::value, ng = decltype(NG)::value;
-      bf16x8 op[M];
+      u32x4 op[M];
       if (pin) {
         op[0] = carry[0];
         op[1] = carry[1];
@@ -553,7 +564,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
           carry[k + 2 - M] = operand(IC<(ng < 0 ? 0 : ng)>{}, k + 2 - M);
         }
         product(G, k, op[k]);
-        if constexpr (vh >= 0) softmax_grad(vh, k * E);
+        if constexpr (vh >= 0) softmax_grad(vh, k * RPS);
         if constexpr (vh == 0) {
           if (k >= M - 4) read_ml(1, k - (M - 4));  // half 1's rows, for the next phase
         }
@@ -567,15 +578,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
   if (key < key_end) {
-    store_rows<D>(p.dk + ko + (int64_t)key * p.k_ss, dk, p.scale, hl);
-    store_rows<D>(p.dv + ko + (int64_t)key * p.k_ss, dv, 1.f, hl);
+    store_rows<E, D>(p.dk + ko + (int64_t)key * p.k_ss, dk, p.scale, hl);
+    store_rows<E, D>(p.dv + ko + (int64_t)key * p.k_ss, dv, 1.f, hl);
   }
 }
 
-template <int D>
+template <typename E, int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   if (p.rows > 0)
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((p.rows + 15) / 16)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((p.rows + 15) / 16)), dim3(256), 0, stream, p);
   BwdParams pq = p;
   pq.total_items = p.nseq > 0 ? p.Nq * p.q_tiles : p.B * p.Nq * ((p.Sq + kBlock - 1) / kBlock);
   BwdParams pk = p;
@@ -583,15 +594,16 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   const bool causal = p.causal == 2 || p.causal == 3;
   if (pq.total_items > 0) {
     if (causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid_for_items(pq.total_items)), dim3(256), 0, stream, pq);
+      hipLaunchKernelGGL((bwd_dq_kernel<E, D, true>), dim3(grid_for_items(pq.total_items)), dim3(256), 0, stream, pq);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(grid_for_items(pq.total_items)), dim3(256), 0, stream, pq);
+      hipLaunchKernelGGL((bwd_dq_kernel<E, D, false>), dim3(grid_for_items(pq.total_items)), dim3(256), 0, stream, pq);
   }
   if (pk.total_items > 0) {
     if (causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid_for_items(pk.total_items)), dim3(256), 0, stream, pk);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true>), dim3(grid_for_items(pk.total_items)), dim3(256), 0, stream, pk);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid_for_items(pk.total_items)), dim3(256), 0, stream, pk);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), dim3(grid_for_items(pk.total_items)), dim3(256), 0, stream,
+                         pk);
   }
   return hipGetLastError();
 }
@@ -599,8 +611,13 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
-  if (p.D == 64) return launch_bwd_d<64>(p, stream);
-  if (p.D == 128) return launch_bwd_d<128>(p, stream);
+  if (p.f16) {
+    if (p.D == 64) return launch_bwd_d<_Float16, 64>(p, stream);
+    if (p.D == 128) return launch_bwd_d<_Float16, 128>(p, stream);
+  } else {
+    if (p.D == 64) return launch_bwd_d<__bf16, 64>(p, stream);
+    if (p.D == 128) return launch_bwd_d<__bf16, 128>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -390,7 +390,6 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   int total_qb = 0;
   int rc = setup_common(desc, f, true, true, &total_qb);
   if (rc) return rc;
-  if (desc->dtype != QATTN_DTYPE_BF16) return fail(QATTN_UNSUPPORTED, "attn_bwd takes bf16 tensors");
   if (f.Dv != f.D) return fail(QATTN_UNSUPPORTED, "attn_bwd needs Dv == D");
   if (desc->atten_mask || desc->pre_tokens != INT32_MAX || desc->next_tokens != INT32_MAX || f.actual)
     return fail(QATTN_UNSUPPORTED, "attn_bwd takes sparse_mode 0, 2 or 3 only (no atten_mask, band or actual lengths)");
@@ -427,6 +426,7 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.Skv = desc->Skv;
   p.D = desc->D;
   p.causal = desc->sparse_mode;
+  p.f16 = desc->dtype == QATTN_DTYPE_FP16;
   p.scale = f.scale;
   p.c = f.c;
   p.q_sb = f.q_sb;

@@ -67,7 +67,7 @@ struct FwdParams {
   int cu_kv[kMaxSeqs + 1];
 };
 
-// Everything a backward launch needs (BNSD or TND, bf16, D = Dv), passed by value.
+// Everything a backward launch needs (any layout, bf16 or fp16, D = Dv), passed by value.
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -89,6 +89,7 @@ struct BwdParams {
   int64_t rows;       // rows of softmax max / sum: B Nq Sq (BNSD) or Nq T (TND)
   int B, Nq, Nkv, group, Sq, Skv, D;
   int causal;         // 0, 2 top-left, 3 bottom-right
+  int f16;            // 1: fp16 tensors, 0: bf16
   int total_items;
   int q_tiles, k_tiles;  // TND: q-blocks / kv-blocks per head, summed over the sequences
   float scale;

@@ -131,3 +131,25 @@ def test_backward_layouts_match_bnsd(qa, layout):
     torch.cuda.synchronize()
     for a, b in zip(grads, g2):
         assert torch.equal(to(a).view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode,D", [(0, 128), (3, 128), (2, 64)])
+def test_backward_fp16(qa, mode, D):
+    """float16 tensors: P and dS are rounded to fp16 (2^-11) and the gradients are written in fp16;
+    the same relative bound holds with room to spare."""
+    from workloads import random_f16
+    B, Nq, Nkv, S = 1, 4, 2, 300
+    what = f"bwd fp16 mode={mode} D={D}"
+    banner(what)
+    x = [random_f16(60 + i, shape) for i, shape in enumerate([(B, Nq, S, D), (B, Nkv, S, D), (B, Nkv, S, D),
+                                                               (B, Nq, S, D)])]
+    q, k, v, do = (torch.from_numpy(a).cuda() for a in x)
+    scale = 1.0 / np.sqrt(D)
+    o, m, l = qa.attn_fwd(q, k, v, scale=scale, sparse_mode=mode)
+    dq, dk, dv = qa.attn_bwd(q, k, v, o, do, m, l, scale=scale, sparse_mode=mode)
+    torch.cuda.synchronize()
+    assert dq.dtype == torch.float16
+    rq, rk, rv = oracle.attention_backward(*(a.astype(np.float64) for a in x), scale, sparse_mode=mode)
+    _check(dq.float(), rq, what + " dQ")
+    _check(dk.float(), rk, what + " dK")
+    _check(dv.float(), rv, what + " dV")

@@ -120,7 +120,7 @@ def test_bwd_kernels_use_no_scratch_and_fit():
     (two waves per SIMD, 64 KiB of LDS each), the dK/dV kernel one (its accumulators take 512
     registers per lane)."""
     ks = _resources("attn_bwd.hip")
-    assert len(ks) == 10, list(ks)  # preparation, dQ and dK/dV (two modes each), for D = 64 and 128
+    assert len(ks) == 20, list(ks)  # preparation, dQ and dK/dV (two modes each), D = 64 / 128, bf16 / fp16
     for name, res in ks.items():
         assert res.get("ScratchSize", 0) == 0, (name, res)
         assert res.get("VGPRs Spill", 0) == 0, (name, res)
