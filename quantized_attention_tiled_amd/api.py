@@ -352,11 +352,13 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
              softmax_max: torch.Tensor, softmax_sum: torch.Tensor, *, scale: float = 1.0, sparse_mode: int = 0,
              layout: str = "BNSD", cu_seqlens_q: Optional[Sequence[int]] = None,
              cu_seqlens_kv: Optional[Sequence[int]] = None, head_num: Optional[int] = None,
+             atten_mask: Optional[torch.Tensor] = None, pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT,
              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of attn_fwd on bfloat16 or float16 q, k, v (one type) in any layout
     attn_fwd takes (shapes as there, D = Dv), given the forward's out and softmax_max / softmax_sum
-    and the output gradient dout (shaped like out). ``workspace``: optional fp32 device tensor of at least
+    and the output gradient dout (shaped like out). The masks are the forward's: sparse_mode,
+    ``atten_mask`` (not with TND) and the ``pre_tokens`` / ``next_tokens`` band. ``workspace``: optional fp32 device tensor of at least
     attn_bwd_workspace_bytes / 4 elements (2 B Nq Sq; TND: 2 Nq T)."""
     lib = load()
     dev = q.device
@@ -382,6 +384,14 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         raise ValueError("v must match k, out and dout must match q")
     if tuple(softmax_max.shape) != ml_shape or tuple(softmax_sum.shape) != ml_shape:
         raise ValueError(f"softmax_max / softmax_sum must be {ml_shape}")
+    kind = MASK_SS
+    if atten_mask is not None:
+        if atten_mask.dtype == torch.bool:
+            atten_mask = atten_mask.view(torch.uint8)
+        _require(atten_mask, "atten_mask", torch.uint8, dev)
+        if layout == "TND":
+            raise ValueError("atten_mask is not available with TND")
+        kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -390,7 +400,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         if t.shape != ref.shape:
             raise ValueError(f"{n} must be shaped like {tuple(ref.shape)}")
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
-                     cu_q=cu_q, cu_kv=cu_kv, dtype=dtype)
+                     cu_q=cu_q, cu_kv=cu_kv, dtype=dtype, atten_mask=atten_mask, mask_kind=kind,
+                     pre_tokens=pre_tokens, next_tokens=next_tokens)
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(desc)) // 4
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.float32, device=dev)

@@ -204,10 +204,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 }
 
 // ---- dQ: one 128-row q-block of head h per workgroup, 4 waves x 32 rows ----
-template <typename E, int D, bool CAUSAL>
+// MODE bits as the forward's: kCausal (the key range i - pre <= j <= i + off: causal modes and
+// the sparse_mode 0 band) and kMask (boolean atten_mask, read per element).
+template <typename E, int D, int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   using T = BTile<D>;
   using EL = BElem<E>;
+  constexpr bool CAUSAL = (MODE & kCausal) != 0, MASKED = (MODE & kMask) != 0;
   constexpr int DT = D / 16, DB = D / 32;
   // K slots 0, 1, then V slots 0, 1: tile it + 1 loads while tile it is read
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * T::kBytes];
@@ -237,7 +240,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   const int g = h / p.group;
   const int row_end = min((qb + 1) * kBlock, Lq);
   const int q = qb * kBlock + wave * 32 + l32;  // this lane's query row
-  const int off = CAUSAL ? (p.causal == 3 ? Lkv - Lq : 0) : 0;
+  const int off = CAUSAL ? (p.causal == 3 ? Lkv - Lq : p.band_next) : 0;
+  const int pre = CAUSAL ? p.band_pre : 0;
+  const int wr0 = qb * kBlock + wave * 32, wr1 = min(wr0 + 31, row_end - 1);  // this wave's rows
+  const uint8_t* mrow = nullptr;  // this lane's atten_mask row
+  if constexpr (MASKED) mrow = p.mask + b * p.mask_sb + h * p.mask_sh + (int64_t)max(min(q, row_end - 1), 0) * p.mask_ss;
 
   const int64_t qo = b * p.q_sb + h * p.q_sh + q_tok0 * p.q_ss;
   const int64_t ko = b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
@@ -264,17 +271,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
   for (int db = 0; db < DB; db++) acc[db] = f32x16{};
 
+  // keys the workgroup's rows may keep: up to row_end - 1 + off, from its first row - pre
   const int kv_end = CAUSAL ? min(Lkv, row_end - 1 + off + 1) : Lkv;
-  const int ntiles = (row_end > qb * kBlock && kv_end > 0) ? (kv_end + kTileRows - 1) / kTileRows : 0;
+  const int t0 = CAUSAL ? max(qb * kBlock - pre, 0) / kTileRows : 0;
+  const int ntiles =
+      (row_end > qb * kBlock && kv_end > t0 * kTileRows) ? (kv_end - t0 * kTileRows + kTileRows - 1) / kTileRows : 0;
   const TileLoad<D> ld(wave, lane, (uint32_t)p.k_ss * 2);
   const rsrc4 k_rsrc = make_rsrc(kp, extent(Lkv, ld.stride, T::kRowBytes));
   const rsrc4 v_rsrc = make_rsrc(vp, extent(Lkv, ld.stride, T::kRowBytes));
   if (ntiles > 0) {
-    ld.issue(k_rsrc, smem, 0, wave);
-    ld.issue(v_rsrc, smem + 2 * T::kBytes, 0, wave);
+    ld.issue(k_rsrc, smem, t0 * kTileRows, wave);
+    ld.issue(v_rsrc, smem + 2 * T::kBytes, t0 * kTileRows, wave);
   }
   for (int it = 0; it < ntiles; it++) {
-    const int key0 = it * kTileRows;
+    const int key0 = (t0 + it) * kTileRows;
     // tile it has landed everywhere, and every wave is done with tile it - 1, whose slots the
     // loads of tile it + 1 now take
     wait_loads();
@@ -285,9 +295,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     }
     const uint8_t* kt = smem + (it & 1) * T::kBytes;
     const uint8_t* vt = smem + (2 + (it & 1)) * T::kBytes;
-    if (CAUSAL && key0 > qb * kBlock + wave * 32 + 31 + off) continue;  // above this wave's diagonal
-    // a tile that crosses this wave's causal diagonal needs the per-element causal mask
-    const bool diag = CAUSAL && key0 + kTileRows - 1 > qb * kBlock + wave * 32 + off;
+    // a tile outside every row's key range of this wave contributes nothing; one that crosses a
+    // limit needs the per-element range mask
+    if (CAUSAL && (key0 > wr1 + off || key0 + kTileRows - 1 < wr0 - pre)) continue;
+    const bool diag = CAUSAL && (key0 + kTileRows - 1 > wr0 + off || key0 < wr1 - pre);
+    // atten_mask bytes of this lane's row for the 32 keys of its registers (both halves), read
+    // before the products that hide their latency
+    uint8_t mk[2][16];
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) mk[h][e] = mrow[min(key0 + 32 * h + c_row(e, hl), Lkv - 1)];
+    }
     // Four phases, one matrix product per slot (as in the dK / dV kernel):
     //   A: S^T = K Q^T and dP^T = V dO^T of keys 0..31 (h0), alternating (D / 8 products);
     //   B: the same for keys 32..63 (h1), while the vector units turn h0 into dS^T (bf16);
@@ -325,7 +345,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 2; i++) {
           float pr = __builtin_amdgcn_exp2f(fminf(s[h][e + i] * p.c - lse2, 0.f));
-          if (CAUSAL && diag) pr = key0 + 32 * h + c_row(e + i, hl) <= q + off ? pr : 0.f;
+          if (CAUSAL && diag) {
+            const int key = key0 + 32 * h + c_row(e + i, hl);
+            pr = (key <= q + off && key >= q - pre) ? pr : 0.f;
+          }
+          if constexpr (MASKED) pr = mk[h][e + i] ? 0.f : pr;
           d2[i] = pr * (dp[h][e + i] - dlt);
         }
         dsc[h][e >> 3][(e & 7) >> 1] = pack2<E>(d2[0], d2[1]);
@@ -374,10 +398,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---- dK, dV: one 128-key kv-block of kv-head g per workgroup, 4 waves x 32 keys ----
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, int MODE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   using T = BTile<D>;
   using EL = BElem<E>;
+  constexpr bool CAUSAL = (MODE & kCausal) != 0, MASKED = (MODE & kMask) != 0;
   constexpr int DT = D / 16, DB = D / 32;
   // Q slots 0, 1, dO slots 0, 1, then per slot 1 KiB holding the tile rows' lse2 (bytes 0..255)
   // and rowsum(dO * O) (256..511): tile u + 1 loads while tile u is read
@@ -408,7 +433,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int key_end = min((kb + 1) * kBlock, Lkv);
   const int wkey0 = kb * kBlock + wave * 32;
   const int key = wkey0 + l32;  // this lane's key
-  const int off = CAUSAL ? (p.causal == 3 ? Lkv - Lq : 0) : 0;
+  const int off = CAUSAL ? (p.causal == 3 ? Lkv - Lq : p.band_next) : 0;
+  const int pre = CAUSAL ? p.band_pre : 0;
 
   const int64_t ko = b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
   const uint16_t* kp = p.k + ko;
@@ -430,10 +456,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     dv[db] = f32x16{};
   }
 
-  // queries that see a key of this block: causal keeps key j for row i when j <= i + off
+  // queries that may keep a key of this block: i - pre <= j <= i + off, i.e. j - off <= i <= j + pre
   const int q_first = CAUSAL ? max(0, kb * kBlock - off) : 0;
+  const int q_last = CAUSAL ? min(Lq - 1, key_end - 1 + pre) : Lq - 1;
   const int t_first = q_first / kTileRows;
-  const int ntiles = key_end > kb * kBlock ? max(0, (Lq + kTileRows - 1) / kTileRows - t_first) : 0;
+  const int ntiles = (key_end > kb * kBlock && q_last >= q_first) ? q_last / kTileRows - t_first + 1 : 0;
   const int total = ntiles * p.group;  // tiles u = hh * ntiles + it over the group's q-heads
   const TileLoad<D> ld(wave, lane, (uint32_t)p.q_ss * 2);
   const int64_t rows_all = p.rows;
@@ -467,9 +494,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const uint8_t* gt = smem + (2 + (u & 1)) * T::kBytes;
     const float* s_lse = (const float*)(smem + 4 * T::kBytes + (u & 1) * 1024);
     const float* s_dlt = s_lse + 64;
-    if (CAUSAL && row0 + kTileRows - 1 + off < wkey0) continue;  // every row is above these keys
-    // a tile that crosses this wave's causal diagonal needs the per-element causal mask
-    const bool diag = CAUSAL && row0 + off < wkey0 + 31;
+    // a tile whose rows keep none of this wave's keys contributes nothing; one that crosses a
+    // limit needs the per-element range mask
+    if (CAUSAL && (row0 + kTileRows - 1 + off < wkey0 || row0 - pre > wkey0 + 31)) continue;
+    const bool diag = CAUSAL && (row0 + off < wkey0 + 31 || row0 + kTileRows - 1 - pre > wkey0);
+    // atten_mask bytes of this lane's key for the 32 rows of its registers (both halves), read
+    // before the products that hide their latency
+    uint8_t mk[2][16];
+    if constexpr (MASKED) {
+      const int hh = u / ntiles;
+      const uint8_t* mcol = p.mask + b * p.mask_sb + (g * p.group + hh) * p.mask_sh + min(key, Lkv - 1);
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) mk[h][e] = mcol[(int64_t)min(row0 + 32 * h + c_row(e, hl), Lq - 1) * p.mask_ss];
+    }
     // Four phases of M = D / 8 matrix products each, one product per slot:
     //   A: S = Q K^T and dP = dO V^T of rows 0..31 (h0), alternating;
     //   B: the same for rows 32..63 (h1), while the vector units turn h0's S and dP into P and
@@ -528,7 +567,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
         // lse2 slot holds another row's value, and the clamp at 0 (never binding for a real row,
         // whose scores lie below its log-sum) keeps their P finite.
         float pr = __builtin_amdgcn_exp2f(fminf(s[h][e] * p.c - lse_r[h][e], 0.f));
-        if (CAUSAL && diag) pr = key <= row0 + qr + off ? pr : 0.f;
+        if (CAUSAL && diag) pr = (key <= row0 + qr + off && key >= row0 + qr - pre) ? pr : 0.f;
+        if constexpr (MASKED) pr = mk[h][e] ? 0.f : pr;
         pr_t[e & 1] = pr;
         ds_t[e & 1] = pr * (dp[h][e] - dlt_r[h][e]);
         if (e & 1) {
@@ -583,40 +623,42 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   }
 }
 
+template <typename E, int D, int MODE>
+void launch_bwd_mode(const BwdParams& pq, const BwdParams& pk, hipStream_t stream) {
+  if (pq.total_items > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, MODE>), dim3(grid_for_items(pq.total_items)), dim3(256), 0, stream, pq);
+  if (pk.total_items > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MODE>), dim3(grid_for_items(pk.total_items)), dim3(256), 0, stream,
+                       pk);
+}
+
 template <typename E, int D>
-hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_d(const BwdParams& p, int mode, hipStream_t stream) {
   if (p.rows > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((p.rows + 15) / 16)), dim3(256), 0, stream, p);
   BwdParams pq = p;
   pq.total_items = p.nseq > 0 ? p.Nq * p.q_tiles : p.B * p.Nq * ((p.Sq + kBlock - 1) / kBlock);
   BwdParams pk = p;
   pk.total_items = p.nseq > 0 ? p.Nkv * p.k_tiles : p.B * p.Nkv * ((p.Skv + kBlock - 1) / kBlock);
-  const bool causal = p.causal == 2 || p.causal == 3;
-  if (pq.total_items > 0) {
-    if (causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<E, D, true>), dim3(grid_for_items(pq.total_items)), dim3(256), 0, stream, pq);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<E, D, false>), dim3(grid_for_items(pq.total_items)), dim3(256), 0, stream, pq);
-  }
-  if (pk.total_items > 0) {
-    if (causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true>), dim3(grid_for_items(pk.total_items)), dim3(256), 0, stream, pk);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), dim3(grid_for_items(pk.total_items)), dim3(256), 0, stream,
-                         pk);
+  switch (mode) {
+    case 0: launch_bwd_mode<E, D, 0>(pq, pk, stream); break;
+    case kCausal: launch_bwd_mode<E, D, kCausal>(pq, pk, stream); break;
+    case kMask: launch_bwd_mode<E, D, kMask>(pq, pk, stream); break;
+    case kCausal | kMask: launch_bwd_mode<E, D, kCausal | kMask>(pq, pk, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_attn_bwd(const BwdParams& p, int mode, hipStream_t stream) {
   if (p.f16) {
-    if (p.D == 64) return launch_bwd_d<_Float16, 64>(p, stream);
-    if (p.D == 128) return launch_bwd_d<_Float16, 128>(p, stream);
+    if (p.D == 64) return launch_bwd_d<_Float16, 64>(p, mode, stream);
+    if (p.D == 128) return launch_bwd_d<_Float16, 128>(p, mode, stream);
   } else {
-    if (p.D == 64) return launch_bwd_d<__bf16, 64>(p, stream);
-    if (p.D == 128) return launch_bwd_d<__bf16, 128>(p, stream);
+    if (p.D == 64) return launch_bwd_d<__bf16, 64>(p, mode, stream);
+    if (p.D == 128) return launch_bwd_d<__bf16, 128>(p, mode, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -391,8 +391,7 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   int rc = setup_common(desc, f, true, true, &total_qb);
   if (rc) return rc;
   if (f.Dv != f.D) return fail(QATTN_UNSUPPORTED, "attn_bwd needs Dv == D");
-  if (desc->atten_mask || desc->pre_tokens != INT32_MAX || desc->next_tokens != INT32_MAX || f.actual)
-    return fail(QATTN_UNSUPPORTED, "attn_bwd takes sparse_mode 0, 2 or 3 only (no atten_mask, band or actual lengths)");
+  if (f.actual) return fail(QATTN_UNSUPPORTED, "attn_bwd takes no actual sequence lengths");
   if (!(desc->head_begin == -1 && desc->head_end == -1 && desc->qblock_begin == -1 && desc->qblock_end == -1))
     return fail(QATTN_UNSUPPORTED, "attn_bwd covers the whole problem (no head or q-block subrange)");
   const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
@@ -426,6 +425,12 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.Skv = desc->Skv;
   p.D = desc->D;
   p.causal = desc->sparse_mode;
+  p.band_pre = f.band_pre;
+  p.band_next = f.band_next;
+  p.mask = desc->atten_mask;
+  p.mask_sb = f.mask_sb;
+  p.mask_sh = f.mask_sh;
+  p.mask_ss = f.mask_ss;
   p.f16 = desc->dtype == QATTN_DTYPE_FP16;
   p.scale = f.scale;
   p.c = f.c;
@@ -461,7 +466,12 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   if (items_q > (int64_t)0x7fffff00 || items_k > (int64_t)0x7fffff00 || rows * 8 >= ((int64_t)1 << 32) ||
       ((int64_t)std::max(desc->Sq, 1) - 1) * f.q_ss * 2 + 2 * desc->D > (int64_t)INT32_MAX)
     return fail(QATTN_UNSUPPORTED, "problem too large for one launch");
-  return hip_status(qattn::launch_attn_bwd(p, (hipStream_t)stream), "attn_bwd launch");
+  int mode = 0;
+  if (desc->sparse_mode == 2 || desc->sparse_mode == 3 || desc->pre_tokens != INT32_MAX ||
+      desc->next_tokens != INT32_MAX)
+    mode |= qattn::kCausal;  // the causal family: both causal modes and the band
+  if (desc->atten_mask) mode |= qattn::kMask;
+  return hip_status(qattn::launch_attn_bwd(p, mode, (hipStream_t)stream), "attn_bwd launch");
 }
 
 }  // extern "C"

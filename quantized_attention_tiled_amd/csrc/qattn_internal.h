@@ -88,7 +88,10 @@ struct BwdParams {
   int64_t ml_sb, ml_sh;
   int64_t rows;       // rows of softmax max / sum: B Nq Sq (BNSD) or Nq T (TND)
   int B, Nq, Nkv, group, Sq, Skv, D;
-  int causal;         // 0, 2 top-left, 3 bottom-right
+  int causal;         // 0 (none or the band), 2 top-left, 3 bottom-right
+  int band_pre, band_next;  // causal-family key range i - band_pre <= j <= i + band_next (as forward)
+  const uint8_t* mask;      // boolean atten_mask (1 = masked) or NULL, with its element strides
+  int64_t mask_sb, mask_sh, mask_ss;
   int f16;            // 1: fp16 tensors, 0: bf16
   int total_items;
   int q_tiles, k_tiles;  // TND: q-blocks / kv-blocks per head, summed over the sequences
@@ -99,7 +102,7 @@ struct BwdParams {
   int cu_kv[kMaxSeqs + 1];
 };
 
-hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdParams& p, int mode, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, int mode, hipStream_t stream);
 hipError_t launch_attn_fwd_f16(const FwdParams& p, int mode, hipStream_t stream);
 // q-blocks per workgroup of the 16-bit kernels in `mode` (the host sets qblocks_per_tile to

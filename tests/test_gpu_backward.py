@@ -153,3 +153,51 @@ def test_backward_fp16(qa, mode, D):
     _check(dq.float(), rq, what + " dQ")
     _check(dk.float(), rk, what + " dK")
     _check(dv.float(), rv, what + " dV")
+
+
+@pytest.mark.parametrize("kw,D", [
+    (dict(pre_tokens=100, next_tokens=20), 128),
+    (dict(pre_tokens=0, next_tokens=0), 64),       # the diagonal only
+    (dict(pre_tokens=-5, next_tokens=40), 128),    # a band off the diagonal
+    (dict(pre_tokens=2147483647, next_tokens=-3), 128),  # one-sided
+])
+def test_backward_band(qa, kw, D):
+    B, Nq, Nkv, Sq, Skv = 1, 4, 2, 330, 300
+    what = f"bwd band {kw} D={D}"
+    banner(what)
+    qb, kb, vb, gb = (random_bf16(90 + i, s) for i, s in enumerate([(B, Nq, Sq, D), (B, Nkv, Skv, D), (B, Nkv, Skv, D),
+                                                                    (B, Nq, Sq, D)]))
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(gb)
+    o, m, l = qa.attn_fwd(q, k, v, scale=scale, **kw)
+    dq, dk, dv = qa.attn_bwd(q, k, v, o, do, m, l, scale=scale, **kw)
+    torch.cuda.synchronize()
+    band = {k2: (None if v2 == 2147483647 else v2) for k2, v2 in kw.items()}
+    rq, rk, rv = oracle.attention_backward(f64(qb), f64(kb), f64(vb), f64(gb), scale, **band)
+    _check(dq, rq, what + " dQ")
+    _check(dk, rk, what + " dK")
+    _check(dv, rv, what + " dV")
+
+
+@pytest.mark.parametrize("kind,mode", [("SS", 0), ("B1SS", 2), ("BNSS", 3)])
+def test_backward_boolean_mask(qa, kind, mode):
+    B, Nq, Nkv, Sq, Skv, D = 2, 4, 2, 200, 260, 128
+    what = f"bwd mask {kind} mode={mode}"
+    banner(what)
+    qb, kb, vb, gb = (random_bf16(95 + i, s) for i, s in enumerate([(B, Nq, Sq, D), (B, Nkv, Skv, D), (B, Nkv, Skv, D),
+                                                                    (B, Nq, Sq, D)]))
+    shape = {"SS": (Sq, Skv), "B1SS": (B, 1, Sq, Skv), "BNSS": (B, Nq, Sq, Skv)}[kind]
+    mask = (np.random.default_rng(96).random(shape) < 0.3).astype(np.uint8)
+    mask[..., 11, :] = 1  # a row with no kept key
+    scale = 0.088
+    q, k, v, do = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(gb)
+    mt = torch.from_numpy(mask).cuda()
+    o, m, l = qa.attn_fwd(q, k, v, scale=scale, sparse_mode=mode, atten_mask=mt)
+    dq, dk, dv = qa.attn_bwd(q, k, v, o, do, m, l, scale=scale, sparse_mode=mode, atten_mask=mt)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(f64(qb), f64(kb), f64(vb), f64(gb), scale, sparse_mode=mode,
+                                           atten_mask=mask)
+    _check(dq, rq, what + " dQ")
+    _check(dk, rk, what + " dK")
+    _check(dv, rv, what + " dV")
+    assert torch.all(dq[:, :, 11] == 0)
