@@ -232,8 +232,9 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
  *   dQ = scale dS K, dK = scale dS^T Q,
  * with P recomputed from softmax_max / softmax_sum, never stored.
  *   desc: any layout (BNSD, BSND/BSH, SBH, TND), bf16 or fp16, Dv = D; the
- *   masks of attn_fwd (sparse_mode 0, 2 or 3, the band, atten_mask), GQA; no
- *   actual lengths or subrange (else QATTN_UNSUPPORTED).
+ *   masks of attn_fwd (sparse_mode 0, 2 or 3, the band, atten_mask), GQA,
+ *   actual lengths (padded rows and keys get zero gradients); no subrange
+ *   (else QATTN_UNSUPPORTED).
  *   q, k, v, o, dout: inputs of desc->dtype (o and the softmax outputs from
  *   attn_fwd on the same description); dq, dk, dv: outputs of that type shaped
  *   like q, k, v (a kv-head's gradients sum over the q-heads that read it).

@@ -52,12 +52,15 @@ def softmax_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float, *,
                        layout: str = "BNSD", sparse_mode: int = 0, atten_mask: Optional[np.ndarray] = None,
                        pre_tokens: Optional[int] = None, next_tokens: Optional[int] = None,
-                       cu_seqlens_q: Optional[np.ndarray] = None, cu_seqlens_kv: Optional[np.ndarray] = None):
+                       cu_seqlens_q: Optional[np.ndarray] = None, cu_seqlens_kv: Optional[np.ndarray] = None,
+                       actual_seq_q=None, actual_seq_kv=None):
     """Gradients (dq, dk, dv) shaped like q, k, v.
 
     BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D(v)], do [B, Nq, Sq, Dv].
     TND:  q [T, Nq, D], k/v [Tk, Nkv, D(v)], do [T, Nq, Dv], with cumulative lengths; each
-          sequence is its own problem (causal anchors counted inside it)."""
+          sequence is its own problem (causal anchors counted inside it).
+    ``actual_seq_q`` / ``actual_seq_kv`` (BNSD): batch b is its first aq_b rows and akv_b keys,
+    as in ``attention``; padded rows and keys get zero gradients."""
     if layout == "TND":
         if atten_mask is not None:
             raise ValueError("TND takes no boolean mask")
@@ -80,18 +83,23 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
     if Nq % Nkv:
         raise ValueError("Nq must be a multiple of Nkv")
     g = Nq // Nkv
+    aq = [Sq] * B if actual_seq_q is None else [int(x) for x in actual_seq_q]
+    akv = [Skv] * B if actual_seq_kv is None else [int(x) for x in actual_seq_kv]
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
-    rows = np.arange(Sq)
     for b in range(B):
+        lq, lk = aq[b], akv[b]
+        rows = np.arange(lq)
         for h in range(Nq):
             mask = _mask_for_head(atten_mask, b, h)
-            a = _allowed(rows, Sq, Skv, sparse_mode, mask, None, pre_tokens, next_tokens)
-            gq, gk, gv = softmax_attention_backward(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, a)
-            dq[b, h] = gq
-            dk[b, h // g] += gk
-            dv[b, h // g] += gv
+            mask = None if mask is None else mask[:lq, :lk]
+            a = _allowed(rows, lq, lk, sparse_mode, mask, None, pre_tokens, next_tokens)
+            gq, gk, gv = softmax_attention_backward(q[b, h, :lq], k[b, h // g, :lk], v[b, h // g, :lk], do[b, h, :lq],
+                                                    scale, a)
+            dq[b, h, :lq] = gq
+            dk[b, h // g, :lk] += gk
+            dv[b, h // g, :lk] += gv
     return dq, dk, dv
 
 

@@ -353,12 +353,14 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
              layout: str = "BNSD", cu_seqlens_q: Optional[Sequence[int]] = None,
              cu_seqlens_kv: Optional[Sequence[int]] = None, head_num: Optional[int] = None,
              atten_mask: Optional[torch.Tensor] = None, pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT,
-             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             actual_seq_lengths: Optional[Sequence[int]] = None,
+             actual_seq_lengths_kv: Optional[Sequence[int]] = None, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of attn_fwd on bfloat16 or float16 q, k, v (one type) in any layout
     attn_fwd takes (shapes as there, D = Dv), given the forward's out and softmax_max / softmax_sum
     and the output gradient dout (shaped like out). The masks are the forward's: sparse_mode,
-    ``atten_mask`` (not with TND) and the ``pre_tokens`` / ``next_tokens`` band. ``workspace``: optional fp32 device tensor of at least
+    ``atten_mask`` (not with TND), the ``pre_tokens`` / ``next_tokens`` band and per-batch
+    ``actual_seq_lengths`` / ``actual_seq_lengths_kv`` (padded rows and keys get zero gradients). ``workspace``: optional fp32 device tensor of at least
     attn_bwd_workspace_bytes / 4 elements (2 B Nq Sq; TND: 2 Nq T)."""
     lib = load()
     dev = q.device
@@ -399,9 +401,11 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         _require(t, n, q.dtype, dev)
         if t.shape != ref.shape:
             raise ValueError(f"{n} must be shaped like {tuple(ref.shape)}")
+    # host arrays, alive until the call returns
+    aq_arr, akv_arr = _cu(actual_seq_lengths), _cu(actual_seq_lengths_kv)
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, dtype=dtype, atten_mask=atten_mask, mask_kind=kind,
-                     pre_tokens=pre_tokens, next_tokens=next_tokens)
+                     pre_tokens=pre_tokens, next_tokens=next_tokens, actual_q=aq_arr, actual_kv=akv_arr)
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(desc)) // 4
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.float32, device=dev)

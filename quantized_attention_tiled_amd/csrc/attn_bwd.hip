@@ -198,8 +198,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
   if (row < rows && sub == 0) {
     const float m = p.m_in[row], l = p.l_in[row];
-    p.lse2[row] = (l > 0.f && m != kNegInf) ? m * kLog2e + __builtin_log2f(l) : kPosInf;
-    p.delta[row] = acc;
+    // a row with no key (l = 0, also the padding past an actual length) gets P = 0 and rowsum 0,
+    // whatever its O and dO rows hold
+    const bool live = l > 0.f && m != kNegInf;
+    p.lse2[row] = live ? m * kLog2e + __builtin_log2f(l) : kPosInf;
+    p.delta[row] = live ? acc : 0.f;
   }
 }
 
@@ -234,11 +237,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     qb = item % QB;
     b = item / QB / p.Nq;
     h = item / QB % p.Nq;
-    Lq = p.Sq;
-    Lkv = p.Skv;
+    Lq = p.actual ? p.cu_q[b] : p.Sq;  // per-batch actual lengths of a padded batch
+    Lkv = p.actual ? p.cu_kv[b] : p.Skv;
   }
   const int g = h / p.group;
   const int row_end = min((qb + 1) * kBlock, Lq);
+  // rows written: the q-block's rows of the (padded) tensor; rows from row_end on are padding
+  // past the batch's actual length, whose dQ is 0 (their P is 0: lse2 = +inf, rowsum 0)
+  const int row_limit = p.nseq > 0 ? row_end : min((qb + 1) * kBlock, p.Sq);
   const int q = qb * kBlock + wave * 32 + l32;  // this lane's query row
   const int off = CAUSAL ? (p.causal == 3 ? Lkv - Lq : p.band_next) : 0;
   const int pre = CAUSAL ? p.band_pre : 0;
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     phase(IC<3>{}, IC<-1>{}, IC<-1>{}, true);
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
-  if (q < row_end) store_rows<E, D>(p.dq + qo + (int64_t)q * p.q_ss, acc, p.scale, hl);
+  if (q < row_limit) store_rows<E, D>(p.dq + qo + (int64_t)q * p.q_ss, acc, p.scale, hl);
 }
 
 // ---- dK, dV: one 128-key kv-block of kv-head g per workgroup, 4 waves x 32 keys ----
@@ -427,10 +433,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     kb = item % KB;
     b = item / KB / p.Nkv;
     g = item / KB % p.Nkv;
-    Lq = p.Sq;
-    Lkv = p.Skv;
+    Lq = p.actual ? p.cu_q[b] : p.Sq;  // per-batch actual lengths of a padded batch
+    Lkv = p.actual ? p.cu_kv[b] : p.Skv;
   }
   const int key_end = min((kb + 1) * kBlock, Lkv);
+  // keys written: the kv-block's keys of the (padded) tensor; keys from key_end on are padding
+  // past the batch's actual length, whose dK and dV are 0
+  const int key_limit = p.nseq > 0 ? key_end : min((kb + 1) * kBlock, p.Skv);
   const int wkey0 = kb * kBlock + wave * 32;
   const int key = wkey0 + l32;  // this lane's key
   const int off = CAUSAL ? (p.causal == 3 ? Lkv - Lq : p.band_next) : 0;
@@ -617,9 +626,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     phase(IC<3>{}, IC<-1>{}, IC<-1>{}, true);
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
-  if (key < key_end) {
-    store_rows<E, D>(p.dk + ko + (int64_t)key * p.k_ss, dk, p.scale, hl);
-    store_rows<E, D>(p.dv + ko + (int64_t)key * p.k_ss, dv, 1.f, hl);
+  if (key < key_limit) {
+    const bool pad = key >= key_end;  // (its lane computed a copy of the last valid key)
+    store_rows<E, D>(p.dk + ko + (int64_t)key * p.k_ss, dk, pad ? 0.f : p.scale, hl);
+    store_rows<E, D>(p.dv + ko + (int64_t)key * p.k_ss, dv, pad ? 0.f : 1.f, hl);
   }
 }
 

@@ -391,7 +391,6 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   int rc = setup_common(desc, f, true, true, &total_qb);
   if (rc) return rc;
   if (f.Dv != f.D) return fail(QATTN_UNSUPPORTED, "attn_bwd needs Dv == D");
-  if (f.actual) return fail(QATTN_UNSUPPORTED, "attn_bwd takes no actual sequence lengths");
   if (!(desc->head_begin == -1 && desc->head_end == -1 && desc->qblock_begin == -1 && desc->qblock_end == -1))
     return fail(QATTN_UNSUPPORTED, "attn_bwd covers the whole problem (no head or q-block subrange)");
   const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
@@ -444,6 +443,12 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.ml_sh = f.ml_sh;
   p.rows = rows;
   p.nseq = tnd ? desc->B : 0;
+  p.actual = f.actual;
+  if (f.actual)
+    for (int i = 0; i < desc->B; i++) {
+      p.cu_q[i] = f.cu_q[i];
+      p.cu_kv[i] = f.cu_kv[i];
+    }
   int64_t items_q, items_k;
   if (tnd) {
     p.q_tiles = p.k_tiles = 0;

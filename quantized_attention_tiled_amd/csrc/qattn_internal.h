@@ -98,6 +98,7 @@ struct BwdParams {
   float scale;
   float c;            // scale * log2(e)
   int nseq;           // TND: sequences; 0 for BNSD
+  int actual;         // batched layouts: cu_q / cu_kv hold per-batch actual lengths
   int cu_q[kMaxSeqs + 1];
   int cu_kv[kMaxSeqs + 1];
 };

@@ -201,3 +201,39 @@ def test_backward_boolean_mask(qa, kind, mode):
     _check(dk, rk, what + " dK")
     _check(dv, rv, what + " dV")
     assert torch.all(dq[:, :, 11] == 0)
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_backward_actual_lengths(qa, mode):
+    """Padded BNSD with per-batch actual lengths: the padding of Q, K, V and dO is NaN and must never
+    be read; padded rows of dQ and padded keys of dK / dV come out as zeros, whatever the output
+    buffers held; the rest matches the oracle."""
+    B, Nq, Nkv, Sq, Skv, D = 3, 4, 2, 330, 300, 128
+    aq, akv = [330, 129, 0], [300, 77, 40]
+    what = f"bwd actual lengths mode={mode}"
+    banner(what)
+    nan = np.uint16(0x7FC0)
+
+    def padded(seed, shape, lens):
+        x = random_bf16(seed, shape)
+        for b, L in enumerate(lens):
+            x[b, :, L:] = nan
+        return x
+
+    qb, kb, vb = padded(70, (B, Nq, Sq, D), aq), padded(71, (B, Nkv, Skv, D), akv), padded(72, (B, Nkv, Skv, D), akv)
+    gb = padded(73, (B, Nq, Sq, D), aq)
+    scale = 1.0 / np.sqrt(D)
+    q, k, v, do = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(gb)
+    kw = dict(scale=scale, sparse_mode=mode, actual_seq_lengths=aq, actual_seq_lengths_kv=akv)
+    o, m, l = qa.attn_fwd(q, k, v, **kw)
+    bufs = tuple(torch.full_like(x, 5.0) for x in (q, k, v))
+    dq, dk, dv = qa.attn_bwd(q, k, v, o, do, m, l, dq=bufs[0], dk=bufs[1], dv=bufs[2], **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(np.nan_to_num(f64(qb)), np.nan_to_num(f64(kb)), np.nan_to_num(f64(vb)),
+                                           np.nan_to_num(f64(gb)), scale, sparse_mode=mode, actual_seq_q=aq,
+                                           actual_seq_kv=akv)
+    _check(dq, rq, what + " dQ")
+    _check(dk, rk, what + " dK")
+    _check(dv, rv, what + " dV")
+    for b in range(B):
+        assert torch.all(dq[b, :, aq[b]:] == 0) and torch.all(dk[b, :, akv[b]:] == 0) and torch.all(dv[b, :, akv[b]:] == 0)

@@ -123,3 +123,17 @@ def test_tnd_finite_differences():
     fq, fk, fv = _finite_diff(q, k, v, do, 0.9, **kw)
     for a, b in ((dq, fq), (dk, fk), (dv, fv)):
         np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-8)
+
+
+def test_actual_lengths_finite_differences():
+    """Per-batch actual lengths on padded BNSD: the gradients are those of the actual-length forward
+    (finite differences through it), and padded rows and keys get exactly zero."""
+    B, Nq, Sq, Skv, D = 2, 1, 4, 5, 2
+    q, k, v = RNG.normal(size=(B, Nq, Sq, D)), RNG.normal(size=(B, Nq, Skv, D)), RNG.normal(size=(B, Nq, Skv, D))
+    do = RNG.normal(size=(B, Nq, Sq, D))
+    kw = dict(sparse_mode=3, actual_seq_q=[3, 4], actual_seq_kv=[5, 2])
+    dq, dk, dv = attention_backward(q, k, v, do, 0.6, **kw)
+    fq, fk, fv = _finite_diff(q, k, v, do, 0.6, sparse_mode=3, actual_seq_q=[3, 4], actual_seq_kv=[5, 2])
+    for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+        np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-8)
+    assert np.all(dq[0, :, 3:] == 0) and np.all(dk[1, :, 2:] == 0) and np.all(dv[1, :, 2:] == 0)
