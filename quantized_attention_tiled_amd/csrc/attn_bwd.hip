@@ -19,7 +19,7 @@
 //     K^T and V^T in registers, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
 //     transposed. Each kv-head's gradients are summed over its q-heads inside one workgroup, so
 //     no atomics are needed and the result does not depend on the launch order.
-// A C-layout accumulator (one lane per column, 16 rows per lane) converted to bf16 register by
+// A C-layout accumulator (one lane per column, 16 rows per lane) converted to E register by
 // register is directly the B operand of the next product, against an A operand read transposed
 // from the row-major tile of the same rows (the permutation of rows matches on both sides).
 #include "qattn_internal.h"
@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, typename BElem<E>::v2));
 }
 
-// Row-major 64 x D bf16 tile in LDS with 16-byte chunks XOR-swizzled by row. The swizzle repeats
+// Row-major 64 x D 16-bit tile in LDS with 16-byte chunks XOR-swizzled by row. The swizzle repeats
 // every 8 rows, which the transposed reads below need (their two halves are 8 rows apart).
 template <int D>
 struct BTile {
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     }
     // Four phases, one matrix product per slot (as in the dK / dV kernel):
     //   A: S^T = K Q^T and dP^T = V dO^T of keys 0..31 (h0), alternating (D / 8 products);
-    //   B: the same for keys 32..63 (h1), while the vector units turn h0 into dS^T (bf16);
+    //   B: the same for keys 32..63 (h1), while the vector units turn h0 into dS^T (in E);
     //   C: dQ^T += K^T dS^T of h0 (D / 16 products), while the vector units do h1;
     //   D: the same products of h1.
     constexpr int MS = D / 8, MQ = D / 16;
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // Four phases of M = D / 8 matrix products each, one product per slot:
     //   A: S = Q K^T and dP = dO V^T of rows 0..31 (h0), alternating;
     //   B: the same for rows 32..63 (h1), while the vector units turn h0's S and dP into P and
-    //      dS (bf16), 16 / M rows' worth of registers per slot;
+    //      dS (in E), 16 / M rows' worth of registers per slot;
     //   C: dV^T += dO^T P and dK^T += Q^T dS of h0, while the vector units do h1;
     //   D: the same products of h1.
     // A operands are read from LDS two slots ahead; scheduling barriers keep each slot's work.

@@ -202,7 +202,7 @@ int check_optional(const void* ptr, const char* name) {
   return QATTN_OK;
 }
 
-// Work items for the bf16 / quantised kernels: q-tiles of `per_tile` q-blocks.
+// Work items for the 16-bit / quantised forward kernels: q-tiles of `per_tile` q-blocks.
 int finish_items(qattn::FwdParams& p, int per_tile) {
   p.qblocks_per_tile = per_tile;
   const int nqb = p.qb1 - p.qb0;
