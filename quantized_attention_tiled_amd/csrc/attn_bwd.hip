@@ -7,6 +7,9 @@
 // With P the softmax probabilities (recomputed here from the saved max and sum, never stored):
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = sum_d dO_id O_id,
 //   dQ = scale dS K,  dK = scale dS^T Q.
+// The forward's options carry over: every layout (batch/head/token strides; TND as per-sequence
+// work items), GQA, the causal modes and the sparse_mode 0 band (one key-range mask with tile
+// skipping), boolean masks (read per element) and per-batch actual lengths.
 //
 // Three kernels, all on v_mfma_f32_32x32x16_{bf16,f16} where the work is a contraction:
 //   * bwd_prep_kernel: per query row, lse2 = log2(sum) + max log2(e) (+inf for a row with no
