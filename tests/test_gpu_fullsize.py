@@ -1,7 +1,9 @@
 """Parity at the five workloads' full sizes, in the launch configuration the
 benchmark times (one call over all heads and q-blocks). The oracle computes
 sampled rows one by one: whole q-blocks of a few heads, chosen to include the
-first, last and interior blocks.
+first, last and interior blocks. The backward at C2 and C3 size is checked on
+whole heads (C2) or a whole GQA group (C3), whose gradients do not depend on
+the other heads.
 
 Tolerances as in the other GPU tests: bf16 O max-abs 1e-2; quantised O max-abs
 3e-2 in units of each V channel's RMS; softmax max/sum relative 1e-3;
@@ -15,7 +17,7 @@ import torch
 import oracle
 from gpu_util import (O_TOL_BF16, O_TOL_QUANT, banner, check_ml, check_o, check_o_channel_scaled, dev_bf16, f64,
                       to_np)
-from workloads import make_workload
+from workloads import f32_to_bf16_bits, make_workload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -128,3 +130,53 @@ def test_c5_qbsa_60k_full(qa):
             check_o_channel_scaled(to_np(o[0, h, rows])[None, None], oo[None, None], f64(w.v[:, h:h + 1]),
                                    O_TOL_QUANT, f"c5 h{h} qb{qb}")
             check_ml(to_np(m[0, h, rows]), to_np(l[0, h, rows]), mm, ll, what=f"c5 h{h} qb{qb}")
+
+
+def _grad_check(g, ref, what, rtol=2e-2):
+    """The backward tests' bound: max-abs error <= rtol * max(1, max |reference|)."""
+    g = to_np(g).astype(np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    bound = rtol * max(1.0, float(np.abs(ref).max()))
+    err = float(np.abs(g - ref).max())
+    banner(f"{what}: max-abs err {err:.3e} (bound {bound:.3e})")
+    assert err <= bound, f"{what}: {err:.3e} > {bound:.3e}"
+
+
+def test_c2_backward_full(qa):
+    """The backward at C2's full size in the launch the backward benchmark times (all 40 heads in
+    one call), against the oracle's full gradients of two heads (each head is its own problem)."""
+    w = make_workload("c2_dense_8k")
+    banner(f"c2 backward full {w.q.shape}")
+    gb = f32_to_bf16_bits(np.random.default_rng(2024).standard_normal(w.q.shape, dtype=np.float32))
+    q, k, v, do = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), dev_bf16(gb)
+    o, m, l = qa.attn_fwd(q, k, v, scale=w.scale)
+    dq, dk, dv = qa.attn_bwd(q, k, v, o, do, m, l, scale=w.scale)
+    torch.cuda.synchronize()
+    for h in (0, 39):
+        sl = slice(h, h + 1)
+        rq, rk, rv = oracle.attention_backward(f64(w.q[:, sl]), f64(w.k[:, sl]), f64(w.v[:, sl]), f64(gb[:, sl]),
+                                               w.scale)
+        _grad_check(dq[:, sl], rq, f"c2 bwd h{h} dQ")
+        _grad_check(dk[:, sl], rk, f"c2 bwd h{h} dK")
+        _grad_check(dv[:, sl], rv, f"c2 bwd h{h} dV")
+
+
+def test_c3_backward_full(qa):
+    """The backward at C3's full size (TND varlen, GQA 32/8, bottom-right causal) in one call;
+    the oracle computes the gradients of kv-head 0's group (q-heads 0..3) over every sequence."""
+    w = make_workload("c3_varlen_gqa_causal")
+    banner(f"c3 backward full {w.q.shape}")
+    gb = f32_to_bf16_bits(np.random.default_rng(2025).standard_normal(w.q.shape, dtype=np.float32))
+    cu = w.cu_seqlens_q.tolist()
+    kw = dict(scale=w.scale, layout="TND", sparse_mode=w.sparse_mode, cu_seqlens_q=cu, cu_seqlens_kv=cu)
+    q, k, v, do = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), dev_bf16(gb)
+    o, m, l = qa.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = qa.attn_bwd(q, k, v, o, do, m, l, **kw)
+    torch.cuda.synchronize()
+    g = w.Nq // w.Nkv
+    rq, rk, rv = oracle.attention_backward(f64(w.q[:, :g]), f64(w.k[:, :1]), f64(w.v[:, :1]), f64(gb[:, :g]), w.scale,
+                                           layout="TND", sparse_mode=w.sparse_mode, cu_seqlens_q=w.cu_seqlens_q,
+                                           cu_seqlens_kv=w.cu_seqlens_kv)
+    _grad_check(dq[:, :g], rq, "c3 bwd dQ (q-heads 0..3)")
+    _grad_check(dk[:, :1], rk, "c3 bwd dK (kv-head 0)")
+    _grad_check(dv[:, :1], rv, "c3 bwd dV (kv-head 0)")
