@@ -166,3 +166,45 @@ def test_subranges_bitexact(qa, dtype, Dv, mode):
         assert torch.equal(full[0].view(torch.int16), out[0].view(torch.int16))
         assert torch.equal(full[1].view(torch.int32), out[1].view(torch.int32))
         assert torch.equal(full[2].view(torch.int32), out[2].view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype,mode,Dv", [("bf16", 0, 128), ("bf16", 2, 128), ("fp16", 0, 128), ("fp16", 3, 64),
+                                           ("fp16", 2, 128)])
+def test_reference_max_outgrown(qa, dtype, mode, Dv):
+    """Rows whose scores grow, after their first 32 keys, far beyond the reference maximum the
+    kernel fixes there (by more than 2^64 for bf16 and 2^15 for fp16 in p): those waves take the
+    kernel's second pass from their true maxima. A spike in a few query rows and keys drives it."""
+    B, Nq, Nkv, S, D = 1, 2, 1, 400, 128
+    what = f"outgrown {dtype} mode={mode} Dv={Dv}"
+    banner(what)
+    rng = np.random.default_rng(123)
+    q = rng.standard_normal((B, Nq, S, D)) * 0.2
+    k = rng.standard_normal((B, Nkv, S, D)) * 0.2
+    v = rng.standard_normal((B, Nkv, S, Dv))
+    k[:, :, :, :2] = 0.0             # channels 0 and 1 carry only the spikes below
+    q[:, :, 300:340, 0] = 12.0       # rows 300..339 (every mask lets them see keys 200..209) ...
+    k[:, :, 200:210, 0] = 11.0       # ... score about 132 there (190 in log2), near 0 on their first keys
+    q[:, 1, 250:255, 1] = -6.0       # head 1: a milder growth, about 2^35 in p (beyond the fp16 slack only)
+    k[:, :, 100:110, 1] = -4.0
+    if dtype == "fp16":
+        x = [a.astype(np.float16) for a in (q, k, v)]
+        tq, tk, tv = (torch.from_numpy(a).cuda() for a in x)
+        r = [a.astype(np.float64) for a in x]
+    else:
+        from workloads import f32_to_bf16_bits
+        bits = [f32_to_bf16_bits(a.astype(np.float32)) for a in (q, k, v)]
+        tq, tk, tv = (dev_bf16(b_) for b_ in bits)
+        r = [f64(b_) for b_ in bits]
+    o, m, l = qa.attn_fwd(tq, tk, tv, scale=1.0, sparse_mode=mode)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(r[0], r[1], r[2], 1.0, sparse_mode=mode)
+    _check(dtype, o, m, l, ro, rm, rl, what)
+    # the second pass is taken per wave: q-block and head subranges still reproduce the full call
+    out = tuple(torch.zeros_like(x) for x in (o, m, l))
+    for hr, br in (((0, 1), (0, 4)), ((1, 2), (0, 2)), ((1, 2), (2, 4))):
+        qa.attn_fwd(tq, tk, tv, scale=1.0, sparse_mode=mode, head_range=hr, qblock_range=br, out=out[0],
+                    softmax_max=out[1], softmax_sum=out[2])
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), out[0].view(torch.int16))
+    assert torch.equal(m.view(torch.int32), out[1].view(torch.int32))
+    assert torch.equal(l.view(torch.int32), out[2].view(torch.int32))
