@@ -33,10 +33,12 @@
 // Softmax in the base-2 domain: p = exp2(s c - m_ref), c = scale log2(e), one FMA and one
 // v_exp_f32 per score. m_ref of a row is fixed at its first finite half-tile max and O is never
 // rescaled: p may exceed 1, up to 2^slack, which fp32 and the 16-bit type carry with unchanged
-// relative precision (slack 64 for bf16; 15 for fp16, whose largest finite value is 65504). A
-// wave whose true row max outgrows m_ref by more than the slack flags itself, and
-// the workgroup runs the key loop a second time in which only flagged waves recompute, from
-// their now-known true maxima. softmax_sum is rescaled to the true max at the end.
+// relative precision (slack 64 for bf16; 15 for fp16, whose largest finite value is 65504). Each
+// lane keeps only a running max of its raw scores (one v_maximum3 per two scores); after the key
+// loop the pair of lanes holding a row gives its true max. A wave whose true row max outgrows
+// m_ref by more than the slack flags itself, and the workgroup runs the key loop a second time in
+// which only flagged waves recompute, from their now-known true maxima. softmax_sum is rescaled
+// to the true max at the end.
 // Every query row's arithmetic depends only on its own 32-row wave slice and the key order,
 // never on the launch shape, so any head / q-block subrange launch reproduces the full call bit
 // for bit.
@@ -363,8 +365,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
   // 8 (r / 4) + 4 hl + r % 4].
   f32x16 o[DB];
   float mref = kNegInf, mtrue = kNegInf, lsum = 0.f;
+  float lmax = kNegInf;  // this lane's running max of the raw scores of the halves that reach the wave
   bool overflow = false;
-  bool over = false;
   bool compute = true;
   bool ref_all = false;  // every row of this wave has its reference max (wave-uniform)
 
@@ -380,8 +382,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
   // One pipeline step over MFMA slots 0 .. M - 1: slots 0 .. DT - 1 compute the scores of the next
   // half (K slot KS, half KH, into sn); slots DT .. M - 1 compute P(prev) V (pp, V slot VS, 16-key
   // chunks 2 VH and 2 VH + 1). Between the MFMAs the VALU runs the softmax of the current half (sc,
-  // exponent offset mu, P into pc) and its row max, which only feeds the true max and the overflow
-  // check (run: the half reaches this wave). NEXT / CUR / PREV switch the three parts on. Operands
+  // exponent offset mu, P into pc) and takes its scores into the lane's running max when the half
+  // reaches this wave (run). NEXT / CUR / PREV switch the three parts on. Operands
   // are read from LDS kPF slots ahead; PIN says the first two arrive in carry, POUT that the last
   // slots read the first two of the following step (K slot KS2, half KH2) into carry. DMA = 1 +
   // KD + 2 VD spreads the loads of the next K tile (into K slot KD, from byte offset dk) and V
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
 #pragma unroll
       for (int k = 0; k < kPF; k++) fetch(k);
     }
-    float ps = 0.f, m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f, m4 = 0.f, m5 = 0.f;
+    float ps = 0.f, rm = 0.f;
     float x[16], t[2];  // softmax pipeline registers
     pin_def(mu);
     __builtin_amdgcn_sched_barrier(0);
@@ -475,40 +477,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
           }
         }
       }
-      if (cur_) {
-        // row max of the current half (max3 tree, then the partner lane), true max, overflow check
-        if (k == 0) {
-          m0 = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
-          m1 = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
-          pin_use(m0);
-          pin_use(m1);
-        }
-        if (k == 1) {
-          m2 = fmaxf(fmaxf(sc[6], sc[7]), sc[8]);
-          m3 = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
-          pin_use(m2);
-          pin_use(m3);
-        }
-        if (k == 2) {
-          m4 = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
-          m5 = fmaxf(fmaxf(m0, m1), m2);
-          pin_use(m4);
-          pin_use(m5);
-        }
-        if (k == 3) {
-          m0 = fmaxf(m5, fmaxf(fmaxf(m3, m4), sc[15]));
-          pin_use(m0);
-        }
-        if (k == 4) {
-          m1 = pair_max(m0);
-          pin_use(m1);
-        }
-        if (k == 5) {
-          m2 = run ? m1 * p.c : kNegInf;
-          mtrue = fmaxf(mtrue, m2);
-          pin_use(mtrue);
-        }
-        if (k == 6) over = over | ((mref != kNegInf) & (m2 > mref + kRefSlack));
+      if (cur_ && k < 8) {
+        // the lane's running max takes in two scores per slot (v_maximum3: the IEEE maximum needs
+        // no canonicalisation of the carried value); a half that does not reach the wave leaves it
+        rm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(k == 0 ? lmax : rm, sc[2 * k]), sc[2 * k + 1]);
+        pin_use(rm);
+        if (k == 7) lmax = run ? rm : lmax;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -565,7 +539,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
       for (int db = 0; db < DB; db++) o[db] = f32x16{};
     }
     if (pass == 1 && overflow) mref = mtrue;
-    over = false;
     ref_all = false;
 
     if (ntiles > 0) {
@@ -641,7 +614,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     int* const wave_flags = (int*)(smem + kOffK);
-    if (pass == 0) overflow = __any(over);
+    if (pass == 0) {
+      // the true max (c > 0 keeps the order) and whether it outgrew the reference by the slack
+      mtrue = pair_max(lmax) * p.c;
+      overflow = __any((mref != kNegInf) & (mtrue > mref + kRefSlack));
+    }
     if (lane == 0) wave_flags[wave] = pass == 0 ? (int)overflow : 0;
     __syncthreads();
     int any_flag = 0;
