@@ -540,8 +540,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       lse_r[h][4 * j] = a4.x, lse_r[h][4 * j + 1] = a4.y, lse_r[h][4 * j + 2] = a4.z, lse_r[h][4 * j + 3] = a4.w;
       dlt_r[h][4 * j] = d4.x, dlt_r[h][4 * j + 1] = d4.y, dlt_r[h][4 * j + 2] = d4.z, dlt_r[h][4 * j + 3] = d4.w;
     };
-#pragma unroll
-    for (int j = 0; j < 4; j++) read_ml(0, j);
     // A operand of product k of group G (0, 1: S / dP of half G; 2, 3: dV / dK of half G - 2)
     auto operand = [&](auto G, int k) __attribute__((always_inline)) -> u32x4 {
       constexpr int g_ = decltype(G)::value;
@@ -599,6 +597,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // operands of group NG (NG < 0: none) read at its end
     auto phase = [&](auto G, auto VH, auto NG, bool pin) __attribute__((always_inline)) {
       constexpr int vh = decltype(VH)::value, ng = decltype(NG)::value;
+      constexpr int nvh = decltype(G)::value == 0 ? 0 : (vh == 0 ? 1 : -1);  // next phase's half
       u32x4 op[M];
       if (pin) {
         op[0] = carry[0];
@@ -617,9 +616,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
         }
         product(G, k, op[k]);
         if constexpr (vh >= 0) softmax_grad(vh, k * RPS);
-        if constexpr (vh == 0) {
-          if (k >= M - 4) read_ml(1, k - (M - 4));  // half 1's rows, for the next phase
-        }
+        // each group of 4 rows' lse2 and rowsum is read two slots before its first use: groups
+        // 1..3 of this phase's half here, group 0 of the next phase's half at this phase's end
+#pragma unroll
+        for (int j = 1; j < 4; j++)
+          if (vh >= 0 && k == 4 * j / RPS - 2) read_ml(vh < 0 ? 0 : vh, j);
+        if (nvh >= 0 && k == M - 2) read_ml(nvh < 0 ? 0 : nvh, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
