@@ -226,7 +226,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
   // key0 of tile i, or -1 when a kept-list entry is out of range (the tile contributes nothing)
   auto tile_key0 = [&](int i) __attribute__((always_inline)) -> int {
     if constexpr ((MODE & kSparse) != 0) {
-      const int blk = list[i >> 1];
+      // a scalar load (the list is uniform and read-only here): consecutive entries share a line
+      // of the scalar cache, where a vector load waits a full memory round trip after each barrier
+      const int blk = ((const __attribute__((address_space(4))) int32_t*)list)[i >> 1];
       return (blk >= 0 && blk < p.KB) ? blk * kBlock + (i & 1) * kKT : -1;
     } else {
       return (t0 + i) * kKT;
