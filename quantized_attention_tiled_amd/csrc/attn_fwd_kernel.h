@@ -140,10 +140,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
   static_assert(M >= 8, "the row-max stages take slots 0 .. 6");
   static_assert(T::kLoadsPerWave >= 1 && TV::kLoadsPerWave >= 1, "tile load split");
 
-  // K slots 0, 1, then V slots 0, 1
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::kBytes + 2 * TV::kBytes];
+  // K slots 0, 1, then V slots 0, 1; with kMaskTile, mask slots 0, 1 (the atten_mask bytes of the
+  // workgroup's rows for the keys of the K tile in the same slot, 64 bytes per row)
+  constexpr bool kMT = (MODE & kMaskTile) != 0;
+  static_assert(!kMT || (MODE & kMask) != 0, "mask tiles belong to masked launches");
+  constexpr int kMaskSlot = kBlock * NQB * kKT;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::kBytes + 2 * TV::kBytes + (kMT ? 2 * kMaskSlot : 0)];
   constexpr int kOffK = 0;
   constexpr int kOffV = 2 * T::kBytes;
+  constexpr int kOffM = 2 * T::kBytes + 2 * TV::kBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -278,6 +283,29 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
 #pragma unroll
     for (int n = 0; n < TV::kLoadsPerWave; n++) issue_one_v(kOffV + slot * TV::kBytes, soff, n);
   };
+  // Mask tiles: each wave loads its own 32 rows (two 1 KiB slabs of 16 rows x 64 bytes) of the
+  // tile's 64 keys; rows past the sequence read as zeros. A row's bytes start at a 16-byte
+  // aligned offset (the launcher checks the strides), so each lane moves one 16-byte chunk.
+  constexpr int kLoadsM = kMT ? 2 : 0;
+  rsrc4 m_rsrc{};
+  uint32_t m_voff = 0, m_slab = 0;
+  if constexpr (kMT) {
+    const int64_t rows_left = max(Lq - row_begin, 0);
+    const int64_t bytes = min(rows_left * p.mask_ss, (int64_t)0x7FFFFFFF);
+    m_rsrc = make_rsrc(p.mask + b * p.mask_sb + h * p.mask_sh + (int64_t)row_begin * p.mask_ss, (uint32_t)bytes);
+    m_voff = (uint32_t)((wave * 32 + lane / 4) * p.mask_ss + (lane % 4) * 16);
+    m_slab = (uint32_t)(16 * p.mask_ss);
+  }
+  auto issue_one_m = [&](int slot, uint32_t key0, int n) __attribute__((always_inline)) {
+    load_lds16(m_rsrc, lds_address(smem + kOffM + slot * kMaskSlot + (2 * wave + n) * 1024), m_voff,
+               key0 + (uint32_t)n * m_slab);
+  };
+  uint32_t dm = 0;  // key offset of the mask tile the next loading step fetches (kept beside dk)
+  auto issue_m = [&](int i, int slot) __attribute__((always_inline)) {
+    const uint32_t key0 = tile_soff(i, 1);
+#pragma unroll
+    for (int n = 0; n < kLoadsM; n++) issue_one_m(slot, key0, n);
+  };
 
   // ---- this wave's query rows as the Q^T B operand: lane (hl, l32) holds row l32, 16-byte chunk
   // 2 t + hl for k-step t ----
@@ -327,7 +355,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
 
   // mask one 32-key half tile in place (keys k0 .. k0 + 31): keys past the sequence, above the
   // causal diagonal, or set in atten_mask
-  auto apply_mask = [&](f32x16& s, int k0, bool valid) __attribute__((always_inline)) {
+  auto apply_mask = [&](f32x16& s, int k0, bool valid, int hidx) __attribute__((always_inline)) {
     const int q = wrow0 + l32;
     // first and last allowed key of this row, relative to k0 and to this lane's 4 hl offset
     int lim = Lkv - 1, lo = 0;
@@ -340,7 +368,20 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
 #pragma unroll
     for (int r = 0; r < 16; r++)
       if (key_off(r) > lim || ((MODE & kCausal) != 0 && key_off(r) < lo)) s[r] = kNegInf;
-    if constexpr ((MODE & kMask) != 0) {
+    if constexpr (kMT) {
+      // this row's bytes for the half's keys from the mask tile in the K tile's slot: register r
+      // is key 8 (r / 4) + r % 4 + 4 hl of the half, so four aligned words hold all sixteen
+      const int qc = min(q, row_end - 1) - row_begin;
+      const uint8_t* mrow = smem + kOffM + ((hidx >> 1) & 1) * kMaskSlot + qc * kKT + 32 * (hidx & 1) + 4 * hl;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) w[j] = *(const uint32_t*)(mrow + 8 * j);
+      if (__builtin_expect(__any((w[0] | w[1] | w[2] | w[3]) != 0u), 1)) {
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if ((w[r >> 2] >> (8 * (r & 3))) & 0xFFu) s[r] = kNegInf;
+      }
+    } else if constexpr ((MODE & kMask) != 0) {
       const int qc = min(q, row_end - 1);
       const uint8_t* mrowp = p.mask + b * p.mask_sb + h * p.mask_sh + (int64_t)qc * p.mask_ss;
 #pragma unroll
@@ -432,14 +473,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
         carry[k + kPF - M] = read_k(ks2_, kh2_, k + kPF - M);
       }
       if constexpr (dma_ != 0) {
-        constexpr int LK = T::kLoadsPerWave, LV = TV::kLoadsPerWave;
+        constexpr int LK = T::kLoadsPerWave, LV = TV::kLoadsPerWave, LA = LK + LV + kLoadsM;
 #pragma unroll
-        for (int j = 0; j < LK + LV; j++) {
-          if ((j * M) / (LK + LV) != k) continue;
+        for (int j = 0; j < LA; j++) {
+          if ((j * M) / LA != k) continue;
           if (j < LK)
             issue_one_k(kOffK + ((dma_ - 1) & 1) * T::kBytes, dk, j);
-          else
+          else if (j < LK + LV)
             issue_one_v(kOffV + ((dma_ - 1) >> 1) * TV::kBytes, dv, j - LK);
+          else
+            issue_one_m((dma_ - 1) & 1, dm, j - LK - LV);  // the mask tile beside its K tile
         }
       }
       if (k < DT) {
@@ -503,7 +546,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
     const int k0 = max(key0, 0) + 32 * (hidx & 1);
     run = compute && half_runs(k0);
     if (!run) return kPosInf;
-    if (half_needs_mask(k0, valid)) apply_mask(s, k0, valid);
+    if (half_needs_mask(k0, valid)) apply_mask(s, k0, valid, hidx);
     if (!ref_all) {
       const float mx = half_max(s) * p.c;
       mref = (mref == kNegInf) ? mx : mref;
@@ -553,6 +596,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
       issue_k(0, 0);
       if (ntiles > 1) issue_k(1, 1);
       issue_v(0, 0);
+      if constexpr (kMT) {
+        issue_m(0, 0);
+        if (ntiles > 1) issue_m(1, 1);
+      }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
       sy = f32x16{};
@@ -565,6 +612,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
       // barrier of tile 0: every wave is done with K(0); K(2) and V(1) are loaded during step 1
       __syncthreads();
       uint32_t dk = tile_soff(2, key_bytes), dv = tile_soff(1, vkey_bytes);
+      dm = kMT ? tile_soff(2, 1) : 0u;
       mu = finish(1, sx, run);
 
       // Tile it (parity PAR = it % 2) runs steps 2 it + 1 and 2 it + 2:
@@ -590,6 +638,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
           __syncthreads();
           dk = tile_soff(it + 3, key_bytes);
           dv = tile_soff(it + 2, vkey_bytes);
+          if constexpr (kMT) dm = tile_soff(it + 3, 1);
           mu = bookkeep(fast, 2 * it + 3, sx, run);
         } else {
           step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
@@ -668,11 +717,18 @@ hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
 
 template <typename E, int D, int DV>
 hipError_t launch_d(const FwdParams& p, int mode, hipStream_t stream) {
+  // masks whose rows start 16-byte aligned go through LDS with the K tiles; others are read per
+  // element from global memory
+  if ((mode & kMask) != 0 && (reinterpret_cast<uintptr_t>(p.mask) & 15) == 0 && p.mask_ss % 16 == 0 &&
+      p.mask_sb % 16 == 0 && p.mask_sh % 16 == 0 && p.mask_ss <= (1 << 20))
+    mode |= kMaskTile;
   switch (mode) {
     case 0: return launch_t<E, D, DV, 0, 2>(p, stream);
     case kCausal: return launch_t<E, D, DV, kCausal, 1>(p, stream);
     case kMask: return launch_t<E, D, DV, kMask, 2>(p, stream);
     case kCausal | kMask: return launch_t<E, D, DV, kCausal | kMask, 1>(p, stream);
+    case kMask | kMaskTile: return launch_t<E, D, DV, kMask | kMaskTile, 2>(p, stream);
+    case kCausal | kMask | kMaskTile: return launch_t<E, D, DV, kCausal | kMask | kMaskTile, 1>(p, stream);
     case kSparse: return launch_t<E, D, DV, kSparse, 1>(p, stream);
     case kVarlen: return launch_t<E, D, DV, kVarlen, 2>(p, stream);
     case kVarlen | kCausal: return launch_t<E, D, DV, kVarlen | kCausal, 1>(p, stream);

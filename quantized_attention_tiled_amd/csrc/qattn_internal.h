@@ -18,6 +18,7 @@ enum ModeBits : int {
   kMask = 2,    // explicit atten_mask (BNSD)
   kSparse = 4,  // kept-block list
   kVarlen = 8,  // TND with cumulative lengths
+  kMaskTile = 16,  // with kMask: mask tiles staged in LDS beside K (16-byte aligned mask rows)
 };
 
 // Everything an attention launch needs, passed by value as the kernel argument.

@@ -64,10 +64,14 @@ def test_dense_and_causal(qa, B, Nq, Nkv, Sq, Skv, D, mode):
     check_ml(to_np(m), to_np(l), rm, rl)
 
 
-@pytest.mark.parametrize("kind,mode", [("SS", 0), ("B1SS", 0), ("BNSS", 0), ("SS", 2), ("BNSS", 3)])
-def test_boolean_masks(qa, kind, mode):
-    B, Nq, Nkv, Sq, Skv, D = 2, 4, 2, 200, 260, 128
-    banner(f"mask {kind} mode={mode}")
+# Skv = 260: mask rows not 16-byte aligned, read per element from global memory; Skv = 272 (and
+# 1024): aligned rows, staged in LDS beside the K tiles
+@pytest.mark.parametrize("kind,mode,Skv", [("SS", 0, 260), ("B1SS", 0, 260), ("BNSS", 0, 260), ("SS", 2, 260),
+                                           ("BNSS", 3, 260), ("SS", 0, 272), ("B1SS", 0, 272), ("BNSS", 0, 272),
+                                           ("SS", 2, 272), ("BNSS", 3, 272), ("B1SS", 3, 1024)])
+def test_boolean_masks(qa, kind, mode, Skv):
+    B, Nq, Nkv, Sq, D = 2, 4, 2, 200, 128
+    banner(f"mask {kind} mode={mode} Skv={Skv}")
     q, k, v = _bnsd(7 + mode, B, Nq, Nkv, Sq, Skv, D)
     rng = np.random.default_rng(5)
     shape = {"SS": (Sq, Skv), "B1SS": (B, 1, Sq, Skv), "BNSS": (B, Nq, Sq, Skv)}[kind]

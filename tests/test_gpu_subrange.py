@@ -48,11 +48,14 @@ def _pieces(n_heads, n_qb):
     return splits
 
 
-@pytest.mark.parametrize("mode,masked,band", [(0, False, None), (2, False, None), (3, False, None), (0, True, None),
-                                             (3, True, None), (0, False, (200, 30)), (0, True, (64, 300))])
-def test_dense_subranges(qa, mode, masked, band):
-    B, Nq, Nkv, S, D = 1, 8, 4, 1100, 128
-    banner(f"subrange dense mode={mode} masked={masked}")
+# S = 1100: mask rows read per element; S = 1104: 16-byte aligned mask rows, staged in LDS
+@pytest.mark.parametrize("mode,masked,band,S", [(0, False, None, 1100), (2, False, None, 1100), (3, False, None, 1100),
+                                               (0, True, None, 1100), (3, True, None, 1100), (0, False, (200, 30), 1100),
+                                               (0, True, (64, 300), 1100), (0, True, None, 1104), (3, True, None, 1104),
+                                               (0, True, (64, 300), 1104)])
+def test_dense_subranges(qa, mode, masked, band, S):
+    B, Nq, Nkv, D = 1, 8, 4, 128
+    banner(f"subrange dense mode={mode} masked={masked} S={S}")
     q = dev_bf16(random_bf16(1, (B, Nq, S, D)))
     k = dev_bf16(random_bf16(2, (B, Nkv, S, D)))
     v = dev_bf16(random_bf16(3, (B, Nkv, S, D)))
