@@ -365,9 +365,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
     }
     lim = valid ? lim - k0 - 4 * hl : -1000000;
     lo -= k0 + 4 * hl;
+    // the range tests can bite only in a half that crosses the sequence end or the causal band
+    // (a masked launch brings every half here)
+    bool range = !valid || k0 + 32 > Lkv;
+    if constexpr ((MODE & kCausal) != 0) range = range || (k0 + 31 > wrow0 + off) || (k0 < wrow_last - pre);
+    if (range) {
 #pragma unroll
-    for (int r = 0; r < 16; r++)
-      if (key_off(r) > lim || ((MODE & kCausal) != 0 && key_off(r) < lo)) s[r] = kNegInf;
+      for (int r = 0; r < 16; r++)
+        if (key_off(r) > lim || ((MODE & kCausal) != 0 && key_off(r) < lo)) s[r] = kNegInf;
+    }
     if constexpr (kMT) {
       // this row's bytes for the half's keys from the mask tile in the K tile's slot: register r
       // is key 8 (r / 4) + r % 4 + 4 hl of the half, so four aligned words hold all sixteen
