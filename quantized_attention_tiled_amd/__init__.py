@@ -1,4 +1,4 @@
-"""Fused, tiled attention for AMD MI355X (gfx950): forward, plus the bf16 backward.
+"""Fused, tiled attention for AMD MI355X (gfx950): forward and backward.
 
 Python binding of the qattn C ABI (include/qattn.h). The kernels live in
 ``csrc/`` and are built into ``libqattn.so`` in this directory by
@@ -11,7 +11,8 @@ Python binding of the qattn C ABI (include/qattn.h). The kernels live in
 * ``quantize_qk_perblock_int8``  Q/K INT8 per 128-token block
 * ``quantize_v_perchannel_fp8``  V FP8 E4M3 per channel
 * ``attn_fwd_qbsa``              INT8 Q.K / FP8 P.V quantised block-sparse attention
-* ``attn_bwd``                   dQ, dK, dV of the dense bf16 forward (BNSD, causal, GQA)
+* ``attn_bwd``                   dQ, dK, dV of the dense forward (bf16 / fp16, every layout, GQA,
+                                 causal, band, boolean masks, actual lengths; Dv = D)
 
 Each returns the attention output plus the per-row softmax max and sum where
 the operation has them. Head and q-block subrange launches write only their
