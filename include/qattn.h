@@ -150,7 +150,11 @@ typedef struct qattn_desc {
  *   q with head dimension Dv. P is rounded to that type before P.V.
  *   softmax_max, softmax_sum: fp32 outputs (layouts above), each nullable.
  *   Causal modes and an explicit atten_mask may be combined (a pair is kept
- *   only when both keep it). atten_mask is not available with TND.
+ *   only when both keep it). atten_mask is not available with TND. A mask
+ *   whose address is 16-byte aligned and whose row length Skv is a multiple
+ *   of 16 bytes is staged through LDS with the K tiles; any other mask is read
+ *   element by element from global memory, with the same results but several
+ *   times slower.
  *   Only rows of the requested head and q-block subrange are written.
  */
 int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
