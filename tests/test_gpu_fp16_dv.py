@@ -208,3 +208,19 @@ def test_reference_max_outgrown(qa, dtype, mode, Dv):
     assert torch.equal(o.view(torch.int16), out[0].view(torch.int16))
     assert torch.equal(m.view(torch.int32), out[1].view(torch.int32))
     assert torch.equal(l.view(torch.int32), out[2].view(torch.int32))
+
+
+# Skv = 256: mask rows 16-byte aligned, staged in LDS with the K tiles; Skv = 250: read per element
+@pytest.mark.parametrize("dtype,mode,Skv,Dv", [("fp16", 0, 256, 128), ("fp16", 3, 256, 64), ("fp16", 2, 250, 128),
+                                               ("bf16", 3, 256, 64)])
+def test_boolean_mask_fp16_and_dv(qa, dtype, mode, Skv, Dv):
+    B, Nq, Nkv, Sq, D = 1, 4, 2, 300, 128
+    what = f"mask {dtype} mode={mode} Skv={Skv} Dv={Dv}"
+    banner(what)
+    (q, qr), (k, kr), (v, vr) = _inputs(dtype, 640 + Skv + mode, (B, Nq, Sq, D), (B, Nkv, Skv, D), (B, Nkv, Skv, Dv))
+    mask = (np.random.default_rng(641).random((B, Nq, Sq, Skv)) < 0.35).astype(np.uint8)
+    mask[:, :, 5, :] = 1  # a fully masked row
+    o, m, l = qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, atten_mask=torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attention(qr, kr, vr, 0.1, sparse_mode=mode, atten_mask=mask)
+    _check(dtype, o, m, l, ro, rm, rl, what)
