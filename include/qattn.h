@@ -139,8 +139,9 @@ typedef struct qattn_desc {
                                    quantised entry point takes BF16 only */
   int32_t Dv;                   /* value / output head dimension; 0 means D. Supported: Dv = D, or
                                    D = 128 with Dv = 64; the quantised entry point needs Dv = D */
-  const int32_t* actual_seq_lengths;    /* not TND: host [B] valid query rows per batch, or NULL (= Sq) */
-  const int32_t* actual_seq_lengths_kv; /* not TND: host [B] valid keys per batch, or NULL (= Skv) */
+  const int32_t* actual_seq_lengths;    /* not TND: host [B] valid query rows per batch, or NULL (= Sq);
+                                           the library reads exactly B entries */
+  const int32_t* actual_seq_lengths_kv; /* not TND: host [B] valid keys per batch, or NULL (= Skv); B entries */
 } qattn_desc;
 
 /*
@@ -226,7 +227,6 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
                   const float* q_scale, const float* k_scale, const float* v_scale, const int32_t* counts,
                   const int32_t* idx, qattn_bf16* o, float* softmax_max, float* softmax_sum, void* stream);
 
-/* Message for the calling thread's most recent failed call ("" if none). */
 /*
  * attn_bwd -- gradients of attn_fwd (fused attention guide, section 2: the
  * fused operator is a training operator whose section 5 outputs, softmax max
@@ -254,6 +254,7 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
 /* Bytes of workspace attn_bwd needs for `desc` (0 for a NULL or malformed description). */
 size_t attn_bwd_workspace_bytes(const qattn_desc* desc);
 
+/* Message for the calling thread's most recent failed call ("" if none). */
 const char* qattn_last_error(void);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

@@ -29,17 +29,29 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _require(t: torch.Tensor, name: str, dtype, device=None) -> None:
+def _require(t: torch.Tensor, name: str, dtype, shape=None) -> None:
+    """Type, dtype, shape and contiguity of a buffer the library reads or writes. The C ABI sees
+    only pointers, so a wrong shape would mean out-of-bounds device accesses. Each entry point
+    checks every buffer here first and all their devices (``_placed``) just before the call."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on a GPU device")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _placed(device: torch.device, **bufs) -> None:
+    """Every named buffer (None = absent) lives on the GPU `device`."""
+    for name, t in bufs.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU device")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _cu(x) -> Optional[ctypes.Array]:
@@ -49,6 +61,14 @@ def _cu(x) -> Optional[ctypes.Array]:
         x = x.detach().cpu().tolist()
     vals = [int(v) for v in x]
     return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _lengths(x, B: int, name: str) -> Optional[ctypes.Array]:
+    """Per-batch actual lengths as a host int32 array of exactly B entries (the library reads B)."""
+    arr = _cu(x)
+    if arr is not None and len(arr) != B:
+        raise ValueError(f"{name} must hold one length per batch ({B}), got {len(arr)}")
+    return arr
 
 
 def _ranges(head_range, qblock_range):
@@ -121,11 +141,11 @@ def _value_dim(layout: str, k: torch.Tensor, v: torch.Tensor, Nkv: int) -> int:
     return v.shape[-1]
 
 
-def _check_dtypes(q, k, v, dev) -> int:
-    if q.dtype not in _DTYPES:
-        raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
+def _check_dtypes(q, k, v) -> int:
+    if not isinstance(q, torch.Tensor) or q.dtype not in _DTYPES:
+        raise TypeError(f"q must be a bfloat16 or float16 tensor, got {getattr(q, 'dtype', type(q))}")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, n, q.dtype, dev)
+        _require(t, n, q.dtype)
     return _DTYPES[q.dtype]
 
 
@@ -174,14 +194,16 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     """
     lib = load()
     dev = q.device
-    dtype = _check_dtypes(q, k, v, dev)
+    dtype = _check_dtypes(q, k, v)
     if layout != "TND":
         lay, B, Nq, Sq, Nkv, Skv, D = _dims(layout, q, k, head_num)
         cu_q, cu_kv, ml_shape = None, None, (B, Nq, Sq)
     else:
+        if q.dim() != 3 or k.dim() != 3:
+            raise ValueError("TND tensors must be 3-D [T, N, D]")
         Sq, Nq, D = q.shape
         Skv, Nkv = k.shape[0], k.shape[1]
-        if k.dim() != 3 or k.shape[2] != D:
+        if k.shape[2] != D:
             raise ValueError("k/v must be [Tk, Nkv, D] matching q")
         cu_q, cu_kv = _cu(cu_seqlens_q), _cu(cu_seqlens_kv if cu_seqlens_kv is not None else cu_seqlens_q)
         if cu_q is None:
@@ -196,18 +218,18 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     if atten_mask is not None:
         if atten_mask.dtype == torch.bool:
             atten_mask = atten_mask.view(torch.uint8)
-        _require(atten_mask, "atten_mask", torch.uint8, dev)
+        _require(atten_mask, "atten_mask", torch.uint8)
         if layout == "TND":
             raise ValueError("atten_mask is not available with TND")
         kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)
     out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, ml_shape, o_shape)
-    for t, n, dt in ((out, "out", q.dtype), (softmax_max, "softmax_max", torch.float32),
-                     (softmax_sum, "softmax_sum", torch.float32)):
-        _require(t, n, dt, dev)
-    if out.shape != o_shape or tuple(softmax_max.shape) != ml_shape or tuple(softmax_sum.shape) != ml_shape:
-        raise ValueError("output shapes do not match")
+    _require(out, "out", q.dtype, o_shape)
+    _require(softmax_max, "softmax_max", torch.float32, ml_shape)
+    _require(softmax_sum, "softmax_sum", torch.float32, ml_shape)
     # host arrays, alive until the call returns
-    aq_arr, akv_arr = _cu(actual_seq_lengths), _cu(actual_seq_lengths_kv)
+    aq_arr = _lengths(actual_seq_lengths, B, "actual_seq_lengths")
+    akv_arr = _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv")
+    _placed(dev, q=q, k=k, v=v, atten_mask=atten_mask, out=out, softmax_max=softmax_max, softmax_sum=softmax_sum)
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, atten_mask=atten_mask, mask_kind=kind, head_range=head_range,
                      qblock_range=qblock_range, pre_tokens=pre_tokens, next_tokens=next_tokens, dtype=dtype, Dv=Dv,
@@ -227,13 +249,16 @@ def build_kv_block_list(keep: torch.Tensor, counts: Optional[torch.Tensor] = Non
     if keep.dtype == torch.bool:
         keep = keep.view(torch.uint8)
     _require(keep, "keep", torch.uint8)
+    if keep.dim() != 4:
+        raise ValueError(f"keep must be 4-D [B, N, QB, KB], got shape {tuple(keep.shape)}")
     B, N, QB, KB = keep.shape
     if counts is None:
         counts = torch.empty((B, N, QB), dtype=torch.int32, device=keep.device)
     if idx is None:
         idx = torch.empty((B, N, QB, KB), dtype=torch.int32, device=keep.device)
-    _require(counts, "counts", torch.int32, keep.device)
-    _require(idx, "idx", torch.int32, keep.device)
+    _require(counts, "counts", torch.int32, (B, N, QB))
+    _require(idx, "idx", torch.int32, (B, N, QB, KB))
+    _placed(keep.device, keep=keep, counts=counts, idx=idx)
     with torch.cuda.device(keep.device):
         check(lib.build_kv_block_list(_vp(keep), B, N, QB, KB, _vp(counts), _vp(idx), _stream(keep.device)))
     return counts, idx
@@ -246,23 +271,21 @@ def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range
     BSH or SBH, shapes and Dv as for attn_fwd); returns (out, m [B, Nq, Sq], l)."""
     lib = load()
     dev = q.device
-    dtype = _check_dtypes(q, k, v, dev)
-    _require(counts, "counts", torch.int32, dev)
-    _require(idx, "idx", torch.int32, dev)
+    dtype = _check_dtypes(q, k, v)
     lay, B, Nq, Sq, Nkv, Skv, D = _dims(layout, q, k, head_num)
     Dv = _value_dim(layout, k, v, Nkv)
     o_shape = q.shape[:-1] + (q.shape[-1] // D * Dv,)
     QB, KB = (Sq + BLOCK - 1) // BLOCK, (Skv + BLOCK - 1) // BLOCK
-    if tuple(counts.shape) != (B, Nq, QB) or tuple(idx.shape) != (B, Nq, QB, KB):
-        raise ValueError("counts/idx must be [B, Nq, QB] and [B, Nq, QB, KB]")
+    _require(counts, "counts", torch.int32, (B, Nq, QB))
+    _require(idx, "idx", torch.int32, (B, Nq, QB, KB))
     out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, (B, Nq, Sq), o_shape)
-    for t, n, dt in ((out, "out", q.dtype), (softmax_max, "softmax_max", torch.float32),
-                     (softmax_sum, "softmax_sum", torch.float32)):
-        _require(t, n, dt, dev)
-    if out.shape != o_shape:
-        raise ValueError("output shape does not match")
+    _require(out, "out", q.dtype, o_shape)
+    _require(softmax_max, "softmax_max", torch.float32, (B, Nq, Sq))
+    _require(softmax_sum, "softmax_sum", torch.float32, (B, Nq, Sq))
     # host arrays, alive until the call returns
-    aq_arr, akv_arr = _cu(actual_seq_lengths), _cu(actual_seq_lengths_kv)
+    aq_arr = _lengths(actual_seq_lengths, B, "actual_seq_lengths")
+    akv_arr = _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv")
+    _placed(dev, q=q, k=k, v=v, counts=counts, idx=idx, out=out, softmax_max=softmax_max, softmax_sum=softmax_sum)
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
                      head_range=head_range, qblock_range=qblock_range, dtype=dtype, Dv=Dv,
                      actual_q=aq_arr, actual_kv=akv_arr)
@@ -277,13 +300,16 @@ def quantize_qk_perblock_int8(x: torch.Tensor, x_q: Optional[torch.Tensor] = Non
     """INT8 per (batch, head, 128-token block); returns (codes int8, scale fp32 [B, N, ceil(S/128)])."""
     lib = load()
     _require(x, "x", torch.bfloat16)
+    if x.dim() != 4:
+        raise ValueError(f"x must be 4-D BNSD [B, N, S, D], got shape {tuple(x.shape)}")
     B, N, S, D = x.shape
     if x_q is None:
         x_q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
     if scale is None:
         scale = torch.empty((B, N, (S + BLOCK - 1) // BLOCK), dtype=torch.float32, device=x.device)
-    _require(x_q, "x_q", torch.int8, x.device)
-    _require(scale, "scale", torch.float32, x.device)
+    _require(x_q, "x_q", torch.int8, x.shape)
+    _require(scale, "scale", torch.float32, (B, N, (S + BLOCK - 1) // BLOCK))
+    _placed(x.device, x=x, x_q=x_q, scale=scale)
     with torch.cuda.device(x.device):
         check(lib.quantize_qk_perblock_int8(_vp(x), B, N, S, D, _vp(x_q), _vp(scale), _stream(x.device)))
     return x_q, scale
@@ -294,13 +320,18 @@ def quantize_v_perchannel_fp8(v: torch.Tensor, v_q: Optional[torch.Tensor] = Non
     """E4M3FN per (batch, head, channel); returns (codes uint8, scale fp32 [B, N, D])."""
     lib = load()
     _require(v, "v", torch.bfloat16)
+    if v.dim() != 4:
+        raise ValueError(f"v must be 4-D BNSD [B, N, S, D], got shape {tuple(v.shape)}")
     B, N, S, D = v.shape
     if v_q is None:
         v_q = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    if v_q.dtype == torch.float8_e4m3fn:
+        v_q = v_q.view(torch.uint8)
     if scale is None:
         scale = torch.empty((B, N, D), dtype=torch.float32, device=v.device)
-    _require(v_q, "v_q", torch.uint8, v.device)
-    _require(scale, "scale", torch.float32, v.device)
+    _require(v_q, "v_q", torch.uint8, v.shape)
+    _require(scale, "scale", torch.float32, (B, N, D))
+    _placed(v.device, v=v, v_q=v_q, scale=scale)
     with torch.cuda.device(v.device):
         check(lib.quantize_v_perchannel_fp8(_vp(v), B, N, S, D, _vp(v_q), _vp(scale), _stream(v.device)))
     return v_q, scale
@@ -313,32 +344,37 @@ def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scal
     ``actual_seq_lengths`` / ``actual_seq_lengths_kv``: per-batch valid lengths, as for attn_fwd."""
     lib = load()
     dev = q_q.device
-    _require(q_q, "q_q", torch.int8, dev)
-    _require(k_q, "k_q", torch.int8, dev)
-    if v_q.dtype == torch.float8_e4m3fn:
-        v_q = v_q.view(torch.uint8)
-    _require(v_q, "v_q", torch.uint8, dev)
-    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
-        _require(t, n, torch.float32, dev)
-    _require(counts, "counts", torch.int32, dev)
-    _require(idx, "idx", torch.int32, dev)
+    _require(q_q, "q_q", torch.int8)
+    if q_q.dim() != 4 or k_q.dim() != 4:
+        raise ValueError("q_q and k_q must be 4-D BNSD")
     B, Nq, Sq, D = q_q.shape
     Nkv, Skv = k_q.shape[1], k_q.shape[2]
+    _require(k_q, "k_q", torch.int8, (B, Nkv, Skv, D))
+    if v_q.dtype == torch.float8_e4m3fn:
+        v_q = v_q.view(torch.uint8)
+    _require(v_q, "v_q", torch.uint8, (B, Nkv, Skv, D))
     QB, KB = (Sq + BLOCK - 1) // BLOCK, (Skv + BLOCK - 1) // BLOCK
-    if tuple(q_scale.shape) != (B, Nq, QB) or tuple(k_scale.shape) != (B, Nkv, KB) or \
-            tuple(v_scale.shape) != (B, Nkv, D):
-        raise ValueError("scale shapes must be q [B, Nq, QB], k [B, Nkv, KB], v [B, Nkv, D]")
-    if tuple(counts.shape) != (B, Nq, QB) or tuple(idx.shape) != (B, Nq, QB, KB):
-        raise ValueError("counts/idx must be [B, Nq, QB] and [B, Nq, QB, KB]")
+    _require(q_scale, "q_scale", torch.float32, (B, Nq, QB))
+    _require(k_scale, "k_scale", torch.float32, (B, Nkv, KB))
+    _require(v_scale, "v_scale", torch.float32, (B, Nkv, D))
+    _require(counts, "counts", torch.int32, (B, Nq, QB))
+    _require(idx, "idx", torch.int32, (B, Nq, QB, KB))
     if out is None:
         out = torch.empty(q_q.shape, dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, (B, Nq, Sq, D))
     if return_softmax:
         if softmax_max is None:
             softmax_max = torch.empty((B, Nq, Sq), dtype=torch.float32, device=dev)
         if softmax_sum is None:
             softmax_sum = torch.empty((B, Nq, Sq), dtype=torch.float32, device=dev)
+    for t, n in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
+        if t is not None:
+            _require(t, n, torch.float32, (B, Nq, Sq))
     # host arrays, alive until the call returns
-    aq_arr, akv_arr = _cu(actual_seq_lengths), _cu(actual_seq_lengths_kv)
+    aq_arr = _lengths(actual_seq_lengths, B, "actual_seq_lengths")
+    akv_arr = _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv")
+    _placed(dev, q_q=q_q, k_q=k_q, v_q=v_q, q_scale=q_scale, k_scale=k_scale, v_scale=v_scale, counts=counts,
+            idx=idx, out=out, softmax_max=softmax_max, softmax_sum=softmax_sum)
     desc = make_desc(layout=LAYOUT_BNSD, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
                      head_range=head_range, qblock_range=qblock_range, actual_q=aq_arr, actual_kv=akv_arr)
     with torch.cuda.device(dev):
@@ -364,16 +400,18 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     attn_bwd_workspace_bytes / 4 elements (2 B Nq Sq; TND: 2 Nq T)."""
     lib = load()
     dev = q.device
-    dtype = _check_dtypes(q, k, v, dev)
+    dtype = _check_dtypes(q, k, v)
     for t, n in ((out, "out"), (dout, "dout")):
-        _require(t, n, q.dtype, dev)
+        _require(t, n, q.dtype)
     for t, n in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
-        _require(t, n, torch.float32, dev)
+        _require(t, n, torch.float32)
     cu_q = cu_kv = None
     if layout == "TND":
+        if q.dim() != 3 or k.dim() != 3:
+            raise ValueError("TND tensors must be 3-D [T, N, D]")
         Sq, Nq, D = q.shape
         Skv, Nkv = k.shape[0], k.shape[1]
-        if k.dim() != 3 or k.shape[2] != D:
+        if k.shape[2] != D:
             raise ValueError("k/v must be [Tk, Nkv, D] matching q")
         cu_q, cu_kv = _cu(cu_seqlens_q), _cu(cu_seqlens_kv if cu_seqlens_kv is not None else cu_seqlens_q)
         if cu_q is None or len(cu_q) != len(cu_kv):
@@ -390,7 +428,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     if atten_mask is not None:
         if atten_mask.dtype == torch.bool:
             atten_mask = atten_mask.view(torch.uint8)
-        _require(atten_mask, "atten_mask", torch.uint8, dev)
+        _require(atten_mask, "atten_mask", torch.uint8)
         if layout == "TND":
             raise ValueError("atten_mask is not available with TND")
         kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)
@@ -398,20 +436,21 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
-        _require(t, n, q.dtype, dev)
-        if t.shape != ref.shape:
-            raise ValueError(f"{n} must be shaped like {tuple(ref.shape)}")
+        _require(t, n, q.dtype, ref.shape)
     # host arrays, alive until the call returns
-    aq_arr, akv_arr = _cu(actual_seq_lengths), _cu(actual_seq_lengths_kv)
+    aq_arr = _lengths(actual_seq_lengths, B, "actual_seq_lengths")
+    akv_arr = _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv")
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, dtype=dtype, atten_mask=atten_mask, mask_kind=kind,
                      pre_tokens=pre_tokens, next_tokens=next_tokens, actual_q=aq_arr, actual_kv=akv_arr)
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(desc)) // 4
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.float32, device=dev)
-    _require(workspace, "workspace", torch.float32, dev)
+    _require(workspace, "workspace", torch.float32)
     if workspace.numel() < need:
         raise ValueError(f"workspace needs {need} float32 elements")
+    _placed(dev, q=q, k=k, v=v, out=out, dout=dout, softmax_max=softmax_max, softmax_sum=softmax_sum,
+            atten_mask=atten_mask, dq=dq, dk=dk, dv=dv, workspace=workspace)
     with torch.cuda.device(dev):
         check(lib.attn_bwd(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(dout), _vp(softmax_max),
                            _vp(softmax_sum), _vp(dq), _vp(dk), _vp(dv), _vp(workspace), _stream(dev)))
