@@ -28,11 +28,12 @@
 //   * a three-stage software pipeline over 64-key steps: while the VALU runs the softmax of step
 //     s, the matrix cores compute the scores of step s + 1 and P(s - 1) V(s - 1); the row max of
 //     step s + 1 is taken in the tail of step s, once its scores are complete.
-// Online softmax in the base-2 domain, as in the tiled loop of the fused attention guide: P is
-// formed against the running max m, so every p lies in [0, 1] and is rounded to FP8 at the same
-// scale as in the page's schedule whenever the max did not grow within the block. Between two
-// steps one compare tells whether any row's max grew; only then (rarely, once the first blocks
-// are done) are l and, after the step whose P V used the old max, O rescaled.
+// Online softmax in the base-2 domain, as in the tiled loop of the fused attention guide with one
+// kept 128 x 128 block per tile: the P of a block is formed against the running max through the
+// end of that block, so every p lies in [0, 1] and is rounded to FP8 at the same scale as in the
+// page's schedule. Between two steps one compare tells whether any row's max grew; only then are
+// l and O rescaled, and when the second half of a block raised it, the first half's P (not yet
+// multiplied with V) is formed again from its scores against the block's max.
 // A row's arithmetic depends only on its own q-block and the kept list, so head or q-block
 // subrange launches reproduce the full call bit for bit.
 #include "qattn_internal.h"
@@ -457,24 +458,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     auto tile_plain = [&](int blk) __attribute__((always_inline)) -> bool {
       return blk_valid(blk) && (blk + 1) * kTK <= Lkv;
     };
+    // P of one step from its scores, against the offset cc: the same operations, in the same
+    // order, as the softmax stages of `step` (P only; the row sum is not formed again).
+    auto form_p = [&](const i32x16 (&s)[2], i32x8& pc, float ct, float cc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < 16; q++) {
+        const int kb = q >> 3, r0 = 2 * (q & 7);
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[kb][r0]), ct, -cc));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[kb][r0 + 1]), ct, -cc));
+        if (q & 1)
+          pc[q >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, pc[q >> 1], true);
+        else
+          pc[q >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, pc[q >> 1], false);
+      }
+    };
     // Online-max update before a step's softmax (mm: the step's row max unless the step needs
-    // masking first). Returns the offset cc of the step's FMA. O is rescaled one step late, after
-    // the P V product that still used the old max.
-    auto bookkeep = [&](bool fast, int blk, int half, i32x16 (&s)[2], int mm, float ct) __attribute__((always_inline)) -> float {
+    // masking first). Returns the offset cc of the step's FMA. The reference max of a kept block's
+    // P is the running max over all keys up to the end of that block, as in the tiled loop with
+    // 128 x 128 tiles: the first half (HALF 0) is formed against the max through its own 64 keys;
+    // when the second half (HALF 1) raises a row's max, the first half's P is formed again from
+    // its scores s0 (untouched until the following step) into p0, before the step that issues its
+    // P V. After a first half, O is rescaled one step late (the P V issued meanwhile still belongs
+    // to the old max); after a second half at once, together with any pending factor.
+    auto bookkeep = [&](bool fast, int blk, auto HALF, i32x16 (&s)[2], int mm, float ct, const i32x16 (&s0)[2],
+                        i32x8& p0) __attribute__((always_inline)) -> float {
+      constexpr int half = decltype(HALF)::value;
       if (!__builtin_expect(fast, 1)) mm = finish(blk, half, s);
       const float mh = (__int_as_float(mm) - kMagic) * ct;  // -inf for a fully masked step
-      if (__builtin_expect(pending, 0)) {
-#pragma unroll
-        for (int db = 0; db < DB; db++) o[db] *= alpha_p;
-        pending = false;
-      }
       if (__builtin_expect(__any(mh > mrun), 0)) {
         const float mnew = fmaxf(mrun, mh);
         const float alpha = (mnew == mrun) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
         lsum *= alpha;
         mrun = mnew;
-        alpha_p = alpha;
-        pending = true;
+        if constexpr (half == 0) {
+          alpha_p = alpha;
+          pending = true;
+        } else {
+          const float f = pending ? alpha_p * alpha : alpha;
+#pragma unroll
+          for (int db = 0; db < DB; db++) o[db] *= f;
+          pending = false;
+          form_p(s0, p0, ct, kMagic * ct + mrun);
+        }
+      }
+      if constexpr (half == 1) {
+        if (__builtin_expect(pending, 0)) {
+#pragma unroll
+          for (int db = 0; db < DB; db++) o[db] *= alpha_p;
+          pending = false;
+        }
       }
       return kMagic * ct + (mrun == kNegInf ? 0.f : mrun);
     };
@@ -505,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
         sy[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(read_k(0, 0, kb, t), qreg[t], t == 0 ? magic : sy[kb], 0, 0, 0);
     ct = ct_of(k0v);
     const bool fast0 = tile_plain(b0);
-    cc = bookkeep(false, b0, 0, sy, 0, ct);
+    cc = bookkeep(false, b0, IC<0>{}, sy, 0, ct, sy, pu);
     // step 0: softmax of step 0, scores of step 1 (K(0), second half), no P V yet
     step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{},
          sx, sy, pv, pu, carry, ct, cc, mm, 0u, 0u);
@@ -514,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     uint32_t dk = block_soff(b2), dv = block_soff(b1);
     int k2v = load_ksc(b2);
     int b3v = load_blk(3);
-    cc = bookkeep(fast0, b0, 1, sx, mm, ct);
+    cc = bookkeep(fast0, b0, IC<1>{}, sx, mm, ct, sy, pu);
 
     // Tile it (parity PAR = it % 2) runs steps 2 it + 1 and 2 it + 2:
     //   step 2 it + 1: softmax of step 2 it + 1 (sx -> pv), scores of step 2 it + 2 from K(it + 1)
@@ -533,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
         step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<1>{}, IC<par ^ 1>{},
              IC<1>{}, IC<1 + par + 2 * (par ^ 1)>{}, sy, sx, pu, pv, carry, ct, cc, mm, dk, dv);
         ct = ct_of(k1v);
-        cc = bookkeep(fast, b1, 0, sy, mm, ct);
+        cc = bookkeep(fast, b1, IC<0>{}, sy, mm, ct, sy, pu);
         step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{},
              IC<0>{}, IC<0>{}, sx, sy, pv, pu, carry, ct, cc, mm, 0u, 0u);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it + 2), V(it + 1), list entry and scale
@@ -543,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
         dv = block_soff(b2);
         const int k3v = load_ksc(b3);
         b3v = load_blk(it + 4);
-        cc = bookkeep(fast, b1, 1, sx, mm, ct);
+        cc = bookkeep(fast, b1, IC<1>{}, sx, mm, ct, sy, pu);
         b1 = b2;
         b2 = b3;
         k1v = k2v;
@@ -551,11 +583,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
       } else {
         step(IC<par ^ 1>{}, IC<0>{}, IC<par>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
              IC<0>{}, IC<0>{}, sy, sx, pu, pv, carry, ct, cc, mm, 0u, 0u);
-        if (pending) {
-#pragma unroll
-          for (int db = 0; db < DB; db++) o[db] *= alpha_p;
-          pending = false;
-        }
         step(IC<par ^ 1>{}, IC<1>{}, IC<par>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{},
              IC<0>{}, IC<0>{}, sx, sy, pv, pu, carry, ct, cc, mm, 0u, 0u);
       }
