@@ -498,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
 #pragma unroll
           for (int db = 0; db < DB; db++) o[db] *= f;
           pending = false;
-          form_p(s0, p0, ct, kMagic * ct + mrun);
+          form_p(s0, p0, ct, __builtin_fmaf(kMagic, ct, mrun));
         }
       }
       if constexpr (half == 1) {
@@ -508,7 +508,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
           pending = false;
         }
       }
-      return kMagic * ct + (mrun == kNegInf ? 0.f : mrun);
+      // one rounding (an explicit FMA), the same for every P of the block
+      return __builtin_fmaf(kMagic, ct, mrun == kNegInf ? 0.f : mrun);
     };
 
     i32x16 sx[2], sy[2];  // score buffers: the pipeline alternates between them

@@ -149,3 +149,26 @@ def test_actual_lengths_skip_padded_keys_and_rows():
                                          vs[0, h], 0.3, [0, 1], qb)
             np.testing.assert_allclose(l, pl, rtol=1e-12)
             np.testing.assert_allclose(m, pm, rtol=1e-12)
+
+
+def test_kernel_model_within_the_fp8_tolerance():
+    """The float32 model of the quantised kernel's steps (a GPU-test helper) agrees with the
+    oracle to the quantised tolerance; only E4M3 rounding decisions near midpoints differ."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    import oracle
+    from qbsa_kernel_model import qbsa_qblock_model
+    rng = np.random.default_rng(5)
+    S, D = 384, 64
+    q = rng.standard_normal((S, D)) + rng.normal(0, 0.5, (3, 1, D)).repeat(128, 0)[:S, 0]
+    k = rng.standard_normal((S, D))
+    v = rng.standard_normal((1, 1, S, D))
+    qc, qs = oracle.quantize_qk_perblock_int8(q[None, None])
+    kc, ks = oracle.quantize_qk_perblock_int8(k[None, None])
+    vc, vs = oracle.quantize_v_perchannel_fp8(v)
+    for qb, kept in [(0, [0, 2]), (1, [0, 1, 2]), (2, [2])]:
+        o_ref, _, _ = oracle.qbsa_qblock(qc[0, 0], kc[0, 0], vc[0, 0], qs[0, 0, qb], ks[0, 0], vs[0, 0], 0.125,
+                                         kept, qb)
+        o_mod = qbsa_qblock_model(qc[0, 0], kc[0, 0], vc[0, 0], qs[0, 0, qb], ks[0, 0], vs[0, 0], 0.125, kept, qb)
+        assert np.abs(o_mod - o_ref).max() <= 3e-2
