@@ -254,6 +254,26 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
 /* Bytes of workspace attn_bwd needs for `desc` (0 for a NULL or malformed description). */
 size_t attn_bwd_workspace_bytes(const qattn_desc* desc);
 
+/* Size of the static workspace of attn_bwd_noalloc: 32 MiB, i.e. up to 4194304 query rows. */
+#define QATTN_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments, kernels
+ * and results as attn_bwd, without `workspace`: the per-row workspace is a static device buffer
+ * of QATTN_NOALLOC_WORKSPACE_BYTES bytes that the library holds on every GPU it runs on until
+ * the process ends. The caller still provides every input and output.
+ *   Returns QATTN_UNSUPPORTED when attn_bwd_workspace_bytes(desc) exceeds that size, and the
+ *   status codes of attn_bwd otherwise. Allocates nothing: no hipMalloc, no allocating library
+ *   call; the buffer's device address is looked up once per device, on the first call there.
+ *   Every call on one GPU uses that GPU's one buffer, so calls that overlap on one GPU (other
+ *   streams, other threads) race: the caller serialises them. The buffer needs no clearing:
+ *   each call writes every workspace row before reading it.
+ */
+int attn_bwd_noalloc(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
+                     const qattn_bf16* o, const qattn_bf16* dout, const float* softmax_max,
+                     const float* softmax_sum, qattn_bf16* dq, qattn_bf16* dk, qattn_bf16* dv, void* stream);
+
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char* qattn_last_error(void);
 

@@ -13,6 +13,8 @@ Python binding of the qattn C ABI (include/qattn.h). The kernels live in
 * ``attn_fwd_qbsa``              INT8 Q.K / FP8 P.V quantised block-sparse attention
 * ``attn_bwd``                   dQ, dK, dV of the dense forward (bf16 / fp16, every layout, GQA,
                                  causal, band, boolean masks, actual lengths; Dv = D)
+* ``attn_bwd_noalloc``           attn_bwd for callers that cannot allocate: its workspace is a
+                                 static per-GPU buffer of the library
 
 Each returns the attention output plus the per-row softmax max and sum where
 the operation has them. Head and q-block subrange launches write only their
@@ -21,6 +23,7 @@ slice and reproduce the full call bit for bit.
 
 from .api import (  # noqa: F401
     attn_bwd,
+    attn_bwd_noalloc,
     attn_fwd,
     attn_fwd_blocksparse,
     attn_fwd_qbsa,

@@ -30,8 +30,9 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "MISALIGNED
 
 # Every symbol include/qattn.h declares.
 EXPORTS = ("attn_fwd", "build_kv_block_list", "attn_fwd_blocksparse", "quantize_qk_perblock_int8",
-           "quantize_v_perchannel_fp8", "attn_fwd_qbsa", "attn_bwd", "attn_bwd_workspace_bytes", "qattn_last_error",
-           "qattn_version")
+           "quantize_v_perchannel_fp8", "attn_fwd_qbsa", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_noalloc",
+           "qattn_last_error", "qattn_version")
+NOALLOC_WORKSPACE_BYTES = 32 << 20  # QATTN_NOALLOC_WORKSPACE_BYTES
 
 
 class QattnError(RuntimeError):
@@ -92,13 +93,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.build_kv_block_list.argtypes = [vp, i32, i32, i32, i32, i32p, i32p, vp]
     lib.attn_fwd_blocksparse.argtypes = [desc_p, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp]
     lib.attn_bwd.argtypes = [desc_p, vp, vp, vp, vp, vp, f32p, f32p, vp, vp, vp, f32p, vp]
+    lib.attn_bwd_noalloc.argtypes = [desc_p, vp, vp, vp, vp, vp, f32p, f32p, vp, vp, vp, vp]
     lib.attn_bwd_workspace_bytes.argtypes = [desc_p]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.quantize_qk_perblock_int8.argtypes = [vp, i32, i32, i32, i32, vp, f32p, vp]
     lib.quantize_v_perchannel_fp8.argtypes = [vp, i32, i32, i32, i32, vp, f32p, vp]
     lib.attn_fwd_qbsa.argtypes = [desc_p, vp, vp, vp, f32p, f32p, f32p, i32p, i32p, vp, f32p, f32p, vp]
     for name in ("attn_fwd", "build_kv_block_list", "attn_fwd_blocksparse", "quantize_qk_perblock_int8",
-                 "quantize_v_perchannel_fp8", "attn_fwd_qbsa", "attn_bwd", "qattn_version"):
+                 "quantize_v_perchannel_fp8", "attn_fwd_qbsa", "attn_bwd", "attn_bwd_noalloc", "qattn_version"):
         getattr(lib, name).restype = ctypes.c_int
     lib.qattn_last_error.argtypes = []
     lib.qattn_last_error.restype = ctypes.c_char_p

@@ -384,22 +384,10 @@ def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scal
     return out, softmax_max, softmax_sum
 
 
-def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
-             softmax_max: torch.Tensor, softmax_sum: torch.Tensor, *, scale: float = 1.0, sparse_mode: int = 0,
-             layout: str = "BNSD", cu_seqlens_q: Optional[Sequence[int]] = None,
-             cu_seqlens_kv: Optional[Sequence[int]] = None, head_num: Optional[int] = None,
-             atten_mask: Optional[torch.Tensor] = None, pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT,
-             actual_seq_lengths: Optional[Sequence[int]] = None,
-             actual_seq_lengths_kv: Optional[Sequence[int]] = None, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None):
-    """Gradients (dq, dk, dv) of attn_fwd on bfloat16 or float16 q, k, v (one type) in any layout
-    attn_fwd takes (shapes as there, D = Dv), given the forward's out and softmax_max / softmax_sum
-    and the output gradient dout (shaped like out). The masks are the forward's: sparse_mode,
-    ``atten_mask`` (not with TND), the ``pre_tokens`` / ``next_tokens`` band and per-batch
-    ``actual_seq_lengths`` / ``actual_seq_lengths_kv`` (padded rows and keys get zero gradients). ``workspace``: optional fp32 device tensor of at least
-    attn_bwd_workspace_bytes / 4 elements (2 B Nq Sq; TND: 2 Nq T)."""
-    lib = load()
-    dev = q.device
+def _bwd_args(q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, layout, cu_seqlens_q,
+              cu_seqlens_kv, head_num, atten_mask, pre_tokens, next_tokens, actual_seq_lengths,
+              actual_seq_lengths_kv, dq, dk, dv, allocate_grads: bool):
+    """Checked arguments of the backward entry points: (desc, host arrays kept alive, mask, dq, dk, dv)."""
     dtype = _check_dtypes(q, k, v)
     for t, n in ((out, "out"), (dout, "dout")):
         _require(t, n, q.dtype)
@@ -432,17 +420,44 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
         if layout == "TND":
             raise ValueError("atten_mask is not available with TND")
         kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    if allocate_grads:
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
     for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        if t is None:
+            raise ValueError(f"{n} must be given (this entry point allocates nothing)")
         _require(t, n, q.dtype, ref.shape)
     # host arrays, alive until the call returns
-    aq_arr = _lengths(actual_seq_lengths, B, "actual_seq_lengths")
-    akv_arr = _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv")
+    keep = (cu_q, cu_kv, _lengths(actual_seq_lengths, B, "actual_seq_lengths"),
+            _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv"))
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, dtype=dtype, atten_mask=atten_mask, mask_kind=kind,
-                     pre_tokens=pre_tokens, next_tokens=next_tokens, actual_q=aq_arr, actual_kv=akv_arr)
+                     pre_tokens=pre_tokens, next_tokens=next_tokens, actual_q=keep[2], actual_kv=keep[3])
+    return desc, keep, atten_mask, dq, dk, dv
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+             softmax_max: torch.Tensor, softmax_sum: torch.Tensor, *, scale: float = 1.0, sparse_mode: int = 0,
+             layout: str = "BNSD", cu_seqlens_q: Optional[Sequence[int]] = None,
+             cu_seqlens_kv: Optional[Sequence[int]] = None, head_num: Optional[int] = None,
+             atten_mask: Optional[torch.Tensor] = None, pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT,
+             actual_seq_lengths: Optional[Sequence[int]] = None,
+             actual_seq_lengths_kv: Optional[Sequence[int]] = None, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of attn_fwd on bfloat16 or float16 q, k, v (one type) in any layout
+    attn_fwd takes (shapes as there, D = Dv), given the forward's out and softmax_max / softmax_sum
+    and the output gradient dout (shaped like out). The masks are the forward's: sparse_mode,
+    ``atten_mask`` (not with TND), the ``pre_tokens`` / ``next_tokens`` band and per-batch
+    ``actual_seq_lengths`` / ``actual_seq_lengths_kv`` (padded rows and keys get zero gradients).
+    ``workspace``: optional fp32 device tensor of at least attn_bwd_workspace_bytes / 4 elements
+    (2 B Nq Sq; TND: 2 Nq T)."""
+    lib = load()
+    dev = q.device
+    desc, _keep, atten_mask, dq, dk, dv = _bwd_args(
+        q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, layout, cu_seqlens_q, cu_seqlens_kv,
+        head_num, atten_mask, pre_tokens, next_tokens, actual_seq_lengths, actual_seq_lengths_kv, dq, dk, dv, True)
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(desc)) // 4
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.float32, device=dev)
@@ -457,5 +472,30 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     return dq, dk, dv
 
 
-__all__ = ["attn_bwd", "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_qbsa", "build_kv_block_list", "quantize_qk_perblock_int8",
+def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                     softmax_max: torch.Tensor, softmax_sum: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor,
+                     dv: torch.Tensor, *, scale: float = 1.0, sparse_mode: int = 0, layout: str = "BNSD",
+                     cu_seqlens_q: Optional[Sequence[int]] = None, cu_seqlens_kv: Optional[Sequence[int]] = None,
+                     head_num: Optional[int] = None, atten_mask: Optional[torch.Tensor] = None,
+                     pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT,
+                     actual_seq_lengths: Optional[Sequence[int]] = None,
+                     actual_seq_lengths_kv: Optional[Sequence[int]] = None):
+    """attn_bwd for callers that cannot allocate: the caller passes every input and the outputs
+    dq, dk, dv; the workspace is the library's static per-GPU buffer (at most
+    NOALLOC_WORKSPACE_BYTES, i.e. 4194304 query rows). Allocates no device memory. Calls that
+    overlap on one GPU share that buffer and must be serialised by the caller."""
+    lib = load()
+    dev = q.device
+    desc, _keep, atten_mask, dq, dk, dv = _bwd_args(
+        q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, layout, cu_seqlens_q, cu_seqlens_kv,
+        head_num, atten_mask, pre_tokens, next_tokens, actual_seq_lengths, actual_seq_lengths_kv, dq, dk, dv, False)
+    _placed(dev, q=q, k=k, v=v, out=out, dout=dout, softmax_max=softmax_max, softmax_sum=softmax_sum,
+            atten_mask=atten_mask, dq=dq, dk=dk, dv=dv)
+    with torch.cuda.device(dev):
+        check(lib.attn_bwd_noalloc(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(dout),
+                                   _vp(softmax_max), _vp(softmax_sum), _vp(dq), _vp(dk), _vp(dv), _stream(dev)))
+    return dq, dk, dv
+
+
+__all__ = ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_qbsa", "build_kv_block_list", "quantize_qk_perblock_int8",
            "quantize_v_perchannel_fp8", "make_desc", "_lib"]

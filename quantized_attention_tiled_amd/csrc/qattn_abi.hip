@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "qattn_internal.h"
 
@@ -383,9 +384,49 @@ size_t attn_bwd_workspace_bytes(const qattn_desc* desc) {
   return 2 * sizeof(float) * rows;
 }
 
-int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
+}  // extern "C"
+
+namespace {
+
+// The static workspace of attn_bwd_noalloc: one copy per GPU, held until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: kernels get the address
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = QATTN_NOALLOC_WORKSPACE_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's `scratch`, or NULL with a message.
+float* device_scratch(int* rc) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *rc = fail(QATTN_HIP_ERROR, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *rc = fail(QATTN_UNSUPPORTED, "device %d: attn_bwd_noalloc serves devices 0..%d", dev, kMaxDevices - 1);
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+    *rc = fail(QATTN_HIP_ERROR, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+               hipGetErrorString(g_scratch_err[dev]));
+    return nullptr;
+  }
+  return static_cast<float*>(g_scratch_ptr[dev]);
+}
+
+// attn_bwd with the caller's workspace, or (use_static, attn_bwd_noalloc) this device's `scratch`,
+// looked up once every argument has passed validation.
+int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
              const qattn_bf16* o, const qattn_bf16* dout, const float* softmax_max, const float* softmax_sum,
-             qattn_bf16* dq, qattn_bf16* dk, qattn_bf16* dv, float* workspace, void* stream) {
+             qattn_bf16* dq, qattn_bf16* dk, qattn_bf16* dv, float* workspace, bool use_static, void* stream) {
   qattn::FwdParams f{};
   int total_qb = 0;
   int rc = setup_common(desc, f, true, true, &total_qb);
@@ -396,8 +437,11 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
   const char* names[] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};
   if ((rc = check_ptrs(ptrs, names, 8))) return rc;
-  if (!softmax_max || !softmax_sum || !workspace)
+  if (!softmax_max || !softmax_sum || (!workspace && !use_static))
     return fail(QATTN_INVALID_ARGUMENT, "softmax_max, softmax_sum and workspace must be non-NULL");
+  if (use_static && attn_bwd_workspace_bytes(desc) > kScratchBytes)
+    return fail(QATTN_UNSUPPORTED, "attn_bwd_noalloc needs %zu bytes of workspace, more than its %zu-byte static buffer",
+                attn_bwd_workspace_bytes(desc), kScratchBytes);
   if ((rc = check_optional(softmax_max, "softmax_max")) || (rc = check_optional(softmax_sum, "softmax_sum")) ||
       (rc = check_optional(workspace, "workspace")))
     return rc;
@@ -412,7 +456,7 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   const bool tnd = desc->layout == QATTN_LAYOUT_TND;
   const int64_t rows = (int64_t)(tnd ? 1 : desc->B) * desc->Nq * desc->Sq;
   p.lse2 = workspace;
-  p.delta = workspace + rows;
+  p.delta = workspace ? workspace + rows : nullptr;
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
@@ -476,7 +520,29 @@ int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
       desc->next_tokens != INT32_MAX)
     mode |= qattn::kCausal;  // the causal family: both causal modes and the band
   if (desc->atten_mask) mode |= qattn::kMask;
+  if (use_static) {
+    float* ws = device_scratch(&rc);
+    if (!ws) return rc;
+    p.lse2 = ws;
+    p.delta = ws + rows;
+  }
   return hip_status(qattn::launch_attn_bwd(p, mode, (hipStream_t)stream), "attn_bwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_bwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
+             const qattn_bf16* o, const qattn_bf16* dout, const float* softmax_max, const float* softmax_sum,
+             qattn_bf16* dq, qattn_bf16* dk, qattn_bf16* dv, float* workspace, void* stream) {
+  return bwd_impl(desc, q, k, v, o, dout, softmax_max, softmax_sum, dq, dk, dv, workspace, false, stream);
+}
+
+int attn_bwd_noalloc(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,
+                     const qattn_bf16* o, const qattn_bf16* dout, const float* softmax_max, const float* softmax_sum,
+                     qattn_bf16* dq, qattn_bf16* dk, qattn_bf16* dv, void* stream) {
+  return bwd_impl(desc, q, k, v, o, dout, softmax_max, softmax_sum, dq, dk, dv, nullptr, true, stream);
 }
 
 }  // extern "C"

@@ -185,6 +185,17 @@ def test_backward_validation(q):
     assert bwd(_desc(q, sparse_mode=1)) == 1
     assert lib.attn_bwd(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                         None) == 3  # dout misaligned
+    # the no-allocation variant: the same checks, and problems beyond its static workspace are refused
+    # on the host (4194304 query rows of 8 bytes fit its 32 MiB)
+    def noalloc(d):
+        return lib.attn_bwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+
+    assert noalloc(_desc(q, Nq=64, Nkv=64, Sq=65538, Skv=128)) == 2
+    assert b"static buffer" in lib.qattn_last_error()
+    assert noalloc(_desc(q, Dv=64)) == 2
+    assert noalloc(_desc(q, sparse_mode=1)) == 1
+    assert lib.attn_bwd_noalloc(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                None) == 1
 
 
 def test_blocksparse_and_qbsa_validation(q):
