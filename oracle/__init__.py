@@ -30,6 +30,7 @@ invariants, closed forms, brute force and independent library routines.
 
 from .backward import attention_backward, softmax_attention_backward  # noqa: F401
 from .attention import (  # noqa: F401
+    atten_mask_from_bits,
     attention,
     attention_block_sparse,
     attention_rows,

@@ -5,7 +5,9 @@ Definition followed ("Ascend NPU fused attention operator" guide):
     dropout are modelled.
   * section 6.1 spells out the unfused steps: scores = Q K^T * scale, add the
     mask, softmax over keys, multiply by V. This module is exactly those steps.
-  * section 4.2: ``atten_mask`` uses 1 = masked, 0 = kept, shapes SS / B1SS / BNSS.
+  * section 4.2: ``atten_mask`` uses 1 = masked, 0 = kept, shapes SS / B1SS / BNSS;
+    section 8 recommends a compressed mask with the causal modes (``atten_mask_from_bits``
+    states the bit layout read here).
   * section 4.3: ``sparse_mode`` 2 and 3 are causal lower triangles anchored at
     the top-left and bottom-right corners; ``sparse_mode`` 0 takes its range from
     ``pre_tokens`` and ``next_tokens`` (section 3's prototype defaults both to
@@ -89,6 +91,22 @@ def _allowed(rows: np.ndarray, Sq: int, Skv: int, sparse_mode: int,
     if keep is not None:
         a &= keep[rows // BLOCK][:, np.arange(Skv) // BLOCK].astype(bool)
     return a
+
+
+def atten_mask_from_bits(words: np.ndarray, Skv: int) -> np.ndarray:
+    """The uint8 atten_mask (1 = masked) that a bit-packed mask stands for.
+
+    The guide advises a compressed atten_mask beside the causal sparse_modes (section 8, tuning
+    advice) without giving its layout; section 4.2 fixes 1 = masked. Reading: one bit per key,
+    each mask row held as ceil(Skv / 32) 32-bit words, key j in bit (j mod 32) of word
+    (j div 32); bits past Skv carry nothing. ``words``: integer array [..., Sq, ceil(Skv / 32)]
+    (SS, B1SS or BNSS). Returns uint8 [..., Sq, Skv].
+    """
+    w = np.asarray(words).astype(np.int64) & 0xFFFFFFFF
+    if w.shape[-1] != (Skv + 31) // 32:
+        raise ValueError(f"a bit-packed row of {Skv} keys has {(Skv + 31) // 32} words, got {w.shape[-1]}")
+    j = np.arange(Skv)
+    return ((w[..., j // 32] >> (j % 32)) & 1).astype(np.uint8)
 
 
 def _mask_for_head(atten_mask: Optional[np.ndarray], b: int, h: int) -> Optional[np.ndarray]:

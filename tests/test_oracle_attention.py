@@ -334,3 +334,39 @@ def test_actual_lengths_equal_tnd_and_full_lengths():
         np.testing.assert_array_equal(x, y)
     with pytest.raises(ValueError):
         attention(q, k, v, 0.5, actual_seq_q=[S + 1, 1, 1])
+
+
+def test_bit_mask_layout_hand_worked():
+    """Bit j % 32 of word j // 32 is key j, 1 = masked; bits past Skv are ignored."""
+    from oracle import atten_mask_from_bits
+    words = np.array([[0x80000005, 0x00000001], [0x00000000, 0xFFFFFFFE]], dtype=np.uint32)
+    m = atten_mask_from_bits(words, 33)
+    assert m.shape == (2, 33) and m.dtype == np.uint8
+    assert np.nonzero(m[0])[0].tolist() == [0, 2, 31, 32]
+    assert m[1].sum() == 0                       # bits 1..31 of the last word lie past key 32
+    with pytest.raises(ValueError):
+        atten_mask_from_bits(words, 65)
+
+
+@pytest.mark.parametrize("Skv", [1, 31, 32, 33, 100, 257])
+def test_bit_mask_inverts_numpy_packbits(Skv):
+    """Against an independent routine: numpy's little-endian packbits of a byte mask, padded to
+    whole 32-bit words and read as little-endian uint32, unpacks to the same byte mask (SS, B1SS
+    and BNSS shapes)."""
+    from oracle import atten_mask_from_bits
+    for shape in ((5, Skv), (2, 1, 3, Skv), (2, 3, 4, Skv)):
+        m = (RNG.random(shape) < 0.4).astype(np.uint8)
+        W = (Skv + 31) // 32
+        padded = np.zeros(shape[:-1] + (32 * W,), dtype=np.uint8)
+        padded[..., :Skv] = m
+        packed = np.packbits(padded, axis=-1, bitorder="little")          # bytes, 4 W per row
+        words = np.ascontiguousarray(packed).view("<u4")
+        assert words.shape == shape[:-1] + (W,)
+        np.testing.assert_array_equal(atten_mask_from_bits(words, Skv), m)
+        # and the attention it gives equals the byte mask's
+        if len(shape) == 2:
+            q, k, v = RNG.normal(size=(1, 1, 5, 4)), RNG.normal(size=(1, 1, Skv, 4)), RNG.normal(size=(1, 1, Skv, 4))
+            a = attention(q, k, v, 0.5, atten_mask=m)
+            b = attention(q, k, v, 0.5, atten_mask=atten_mask_from_bits(words, Skv))
+            for x, y in zip(a, b):
+                np.testing.assert_array_equal(x, y)
