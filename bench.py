@@ -520,6 +520,9 @@ def main(argv=None):
     ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16",
                     help="input / output type of the dense and block-sparse configs (fp16: the same values in float16)")
     ap.add_argument("--dv", type=int, default=None, help="value head dimension below D (dense / block-sparse configs)")
+    ap.add_argument("--mask", choices=["none", "bytes", "bits"], default="none",
+                    help="dense BNSD configs: an SS atten_mask [S, S], one byte per key or bit-packed")
+    ap.add_argument("--mask-density", type=float, default=0.0, help="fraction of masked keys of --mask (i.i.d.)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -575,6 +578,21 @@ def main(argv=None):
     l = torch.empty(ml_shape, dtype=torch.float32, device=dev)
     # every launch goes to torch's current stream of cuda:0, which the binding passes to the library
     stream = torch.cuda.current_stream(dev)
+    amask = None
+    if a.mask != "none":
+        if kind != "dense" or w.layout != "BNSD":
+            log("--mask applies to the dense BNSD configs")
+            return 2
+        # seeded i.i.d. SS mask (1 = masked); every row keeps at least its first key
+        mk = (np.random.default_rng(77).random((w.Sq, w.Skv)) < a.mask_density).astype(np.uint8)
+        mk[:, 0] = 0
+        if a.mask == "bits":
+            W = (w.Skv + 31) // 32
+            pad = np.zeros((w.Sq, 32 * W), np.uint8)
+            pad[:, :w.Skv] = mk
+            mk = np.ascontiguousarray(np.packbits(pad, axis=-1, bitorder="little")).view("<i4")
+        amask = torch.from_numpy(mk).to(dev)
+        name += f"_mask{a.mask}{a.mask_density:g}"
     if kind == "dense":
         cu = w.cu_seqlens_q.tolist() if w.layout == "TND" else None
 
@@ -582,7 +600,7 @@ def main(argv=None):
             if ka is not None:
                 ka.record(stream)
             qa.attn_fwd(q, k, v, scale=w.scale, layout=w.layout, sparse_mode=w.sparse_mode, cu_seqlens_q=cu,
-                        cu_seqlens_kv=cu, out=o, softmax_max=m, softmax_sum=l)
+                        cu_seqlens_kv=cu, out=o, softmax_max=m, softmax_sum=l, atten_mask=amask)
             if kb is not None:
                 kb.record(stream)
         dtype, peak = a.dtype, PEAK_BF16
@@ -668,6 +686,9 @@ def main(argv=None):
         conf = {"workload": wl, "layout": "BNSD", "B": w.B, "N": w.Nq, "Nkv": w.Nkv, "S": w.Sq, "D": w.D}
         if a.dv:
             conf["Dv"] = a.dv
+        if amask is not None:
+            conf["atten_mask"] = {"kind": "SS", "format": a.mask, "density": a.mask_density,
+                                  "bytes": int(amask.numel() * amask.element_size())}
         if w.keep is not None:
             conf["kept_fraction"] = round(float(w.keep.mean()), 4)
     line = {

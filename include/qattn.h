@@ -108,6 +108,12 @@ extern "C" {
 #define QATTN_MASK_SS 0   /* atten_mask [Sq, Skv] shared by all batches and heads */
 #define QATTN_MASK_B1SS 1 /* atten_mask [B, 1, Sq, Skv] shared by heads */
 #define QATTN_MASK_BNSS 2 /* atten_mask [B, Nq, Sq, Skv] */
+/* OR'ed into mask_kind: the mask is bit-packed, one bit per key (the compressed atten_mask the
+ * fused attention guide recommends beside the causal sparse_modes, section 8). Each mask row is
+ * ceil(Skv / 32) little-endian 32-bit words; key j is bit j % 32 of word j / 32 (equivalently
+ * bit j % 8 of byte j / 8), 1 = masked; bits past Skv are ignored. The shapes are those above
+ * with Skv replaced by ceil(Skv / 32) words; the mask must be 4-byte aligned. */
+#define QATTN_MASK_BITS 0x100
 
 #define QATTN_MAX_SEQS 256 /* TND: at most this many sequences per call */
 
@@ -127,8 +133,10 @@ typedef struct qattn_desc {
   int32_t sparse_mode;   /* 0: none, explicit mask and/or band; 2: causal top-left; 3: causal bottom-right */
   const int32_t* cu_seqlens_q;  /* TND: host [B + 1] cumulative query lengths; else NULL */
   const int32_t* cu_seqlens_kv; /* TND: host [B + 1] cumulative key lengths; else NULL */
-  const uint8_t* atten_mask;    /* not TND: device uint8, 1 = masked, 0 = kept; NULL = none */
-  int32_t mask_kind;            /* QATTN_MASK_SS / _B1SS / _BNSS when atten_mask != NULL */
+  const uint8_t* atten_mask;    /* not TND: device uint8, 1 = masked, 0 = kept (or bits, see
+                                   QATTN_MASK_BITS); NULL = none */
+  int32_t mask_kind;            /* QATTN_MASK_SS / _B1SS / _BNSS when atten_mask != NULL, optionally
+                                   | QATTN_MASK_BITS (one bit per key; attn_fwd only) */
   int32_t head_begin;           /* subrange of q-heads [head_begin, head_end); -1, -1 = all */
   int32_t head_end;
   int32_t qblock_begin;         /* subrange of q-blocks [qblock_begin, qblock_end); -1, -1 = all */
@@ -151,11 +159,13 @@ typedef struct qattn_desc {
  *   q with head dimension Dv. P is rounded to that type before P.V.
  *   softmax_max, softmax_sum: fp32 outputs (layouts above), each nullable.
  *   Causal modes and an explicit atten_mask may be combined (a pair is kept
- *   only when both keep it). atten_mask is not available with TND. A mask
- *   whose address is 16-byte aligned and whose row length Skv is a multiple
- *   of 16 bytes is staged through LDS with the K tiles; any other mask is read
- *   element by element from global memory, with the same results but several
- *   times slower.
+ *   only when both keep it). atten_mask is not available with TND. A byte
+ *   mask whose address is 16-byte aligned and whose row length Skv is a
+ *   multiple of 16 bytes is staged through LDS with the K tiles; any other byte
+ *   mask is read element by element from global memory, with the same results
+ *   but several times slower. A bit-packed mask (mask_kind | QATTN_MASK_BITS)
+ *   always goes through LDS and gives the same results as the byte mask it
+ *   packs, bit for bit; it needs Skv < 2^28.
  *   Only rows of the requested head and q-block subrange are written.
  */
 int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, const qattn_bf16* v,

@@ -23,6 +23,7 @@ LAYOUT_TND = 1
 LAYOUT_BSND = 2  # also BSH
 LAYOUT_SBH = 3
 MASK_SS, MASK_B1SS, MASK_BNSS = 0, 1, 2
+MASK_BITS = 0x100  # OR'ed into mask_kind: one bit per key
 DTYPE_BF16, DTYPE_FP16 = 0, 1
 MAX_SEQS = 256
 

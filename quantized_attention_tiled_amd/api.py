@@ -14,8 +14,8 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import (DTYPE_BF16, DTYPE_FP16, LAYOUT_BNSD, LAYOUT_BSND, LAYOUT_SBH, LAYOUT_TND, MASK_B1SS, MASK_BNSS,
-                   MASK_SS, NO_LIMIT, QattnDesc, check, load)
+from ._lib import (DTYPE_BF16, DTYPE_FP16, LAYOUT_BNSD, LAYOUT_BSND, LAYOUT_SBH, LAYOUT_TND, MASK_B1SS, MASK_BITS,
+                   MASK_BNSS, MASK_SS, NO_LIMIT, QattnDesc, check, load)
 
 BLOCK = 128
 _DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_FP16}
@@ -150,13 +150,30 @@ def _check_dtypes(q, k, v) -> int:
 
 
 def _mask_kind(mask: torch.Tensor, B: int, Nq: int, Sq: int, Skv: int) -> int:
-    if mask.dim() == 2 and tuple(mask.shape) == (Sq, Skv):
-        return MASK_SS
-    if mask.dim() == 4 and tuple(mask.shape) == (B, 1, Sq, Skv):
-        return MASK_B1SS
-    if mask.dim() == 4 and tuple(mask.shape) == (B, Nq, Sq, Skv):
-        return MASK_BNSS
-    raise ValueError(f"atten_mask shape {tuple(mask.shape)} is not SS, B1SS or BNSS for B={B} Nq={Nq} Sq={Sq} Skv={Skv}")
+    """mask_kind of an atten_mask: uint8 (one byte per key) or int32 (bit-packed, ceil(Skv / 32)
+    words per row, key j in bit j % 32 of word j // 32), shaped SS, B1SS or BNSS."""
+    bits = mask.dtype == torch.int32
+    W = (Skv + 31) // 32 if bits else Skv
+    flag = MASK_BITS if bits else 0
+    if mask.dim() == 2 and tuple(mask.shape) == (Sq, W):
+        return MASK_SS | flag
+    if mask.dim() == 4 and tuple(mask.shape) == (B, 1, Sq, W):
+        return MASK_B1SS | flag
+    if mask.dim() == 4 and tuple(mask.shape) == (B, Nq, Sq, W):
+        return MASK_BNSS | flag
+    raise ValueError(f"atten_mask shape {tuple(mask.shape)} is not SS, B1SS or BNSS for B={B} Nq={Nq} Sq={Sq} "
+                     f"Skv={Skv}" + (f" (bit-packed: {W} int32 words per row)" if bits else ""))
+
+
+def _atten_mask(atten_mask: torch.Tensor) -> torch.Tensor:
+    """bool / uint8 byte masks as uint8; int32 bit-packed masks as they are."""
+    if atten_mask.dtype == torch.bool:
+        atten_mask = atten_mask.view(torch.uint8)
+    if atten_mask.dtype not in (torch.uint8, torch.int32):
+        raise TypeError(f"atten_mask must be bool / uint8 (one byte per key) or int32 (bit-packed), "
+                        f"got {atten_mask.dtype}")
+    _require(atten_mask, "atten_mask", atten_mask.dtype)
+    return atten_mask
 
 
 def _outputs(q, out, softmax_max, softmax_sum, ml_shape, o_shape=None):
@@ -185,7 +202,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     BSH: q [B, Sq, Nq * D], SBH: q [Sq, B, Nq * D] (k/v alike, with head_num = Nq); m/l [B, Nq, Sq].
     TND:  q [T, Nq, D], k/v [Tk, Nkv, D] plus cumulative lengths; m/l [Nq, T].
     v may have a smaller head dimension Dv (128 / 64); out then has Dv where q has D.
-    ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (not with TND).
+    ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (not with TND); an int32
+    mask is bit-packed: ceil(Skv / 32) words per row, key j in bit j % 32 of word j // 32.
     With sparse_mode 0, ``pre_tokens`` / ``next_tokens`` keep key j for query i when
     i - pre_tokens <= j <= i + next_tokens (2147483647 = no limit).
     ``actual_seq_lengths`` / ``actual_seq_lengths_kv`` (not TND): per-batch valid query / key
@@ -216,9 +234,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     o_shape = q.shape[:-1] + (q.shape[-1] // D * Dv,)
     kind = MASK_SS
     if atten_mask is not None:
-        if atten_mask.dtype == torch.bool:
-            atten_mask = atten_mask.view(torch.uint8)
-        _require(atten_mask, "atten_mask", torch.uint8)
+        atten_mask = _atten_mask(atten_mask)
         if layout == "TND":
             raise ValueError("atten_mask is not available with TND")
         kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)
@@ -414,9 +430,7 @@ def _bwd_args(q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, 
         raise ValueError(f"softmax_max / softmax_sum must be {ml_shape}")
     kind = MASK_SS
     if atten_mask is not None:
-        if atten_mask.dtype == torch.bool:
-            atten_mask = atten_mask.view(torch.uint8)
-        _require(atten_mask, "atten_mask", torch.uint8)
+        atten_mask = _atten_mask(atten_mask)
         if layout == "TND":
             raise ValueError("atten_mask is not available with TND")
         kind = _mask_kind(atten_mask, B, Nq, Sq, Skv)

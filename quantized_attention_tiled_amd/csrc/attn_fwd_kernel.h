@@ -140,11 +140,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
   static_assert(M >= 8, "the row-max stages take slots 0 .. 6");
   static_assert(T::kLoadsPerWave >= 1 && TV::kLoadsPerWave >= 1, "tile load split");
 
-  // K slots 0, 1, then V slots 0, 1; with kMaskTile, mask slots 0, 1 (the atten_mask bytes of the
-  // workgroup's rows for the keys of the K tile in the same slot, 64 bytes per row)
+  // K slots 0, 1, then V slots 0, 1; with kMaskTile, mask slots 0, 1 (the atten_mask of the
+  // workgroup's rows for the keys of the K tile in the same slot: 64 bytes per row, or with
+  // kMaskBits 64 bits, two 32-bit words, per row)
   constexpr bool kMT = (MODE & kMaskTile) != 0;
+  constexpr bool kBits = (MODE & kMaskBits) != 0;
   static_assert(!kMT || (MODE & kMask) != 0, "mask tiles belong to masked launches");
-  constexpr int kMaskSlot = kBlock * NQB * kKT;
+  static_assert(!kBits || kMT, "bit masks go through the mask tiles");
+  constexpr int kMaskRow = kBits ? kKT / 8 : kKT;  // mask bytes per row and tile
+  constexpr int kMaskSlot = kBlock * NQB * kMaskRow;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::kBytes + 2 * TV::kBytes + (kMT ? 2 * kMaskSlot : 0)];
   constexpr int kOffK = 0;
   constexpr int kOffV = 2 * T::kBytes;
@@ -283,22 +287,31 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
 #pragma unroll
     for (int n = 0; n < TV::kLoadsPerWave; n++) issue_one_v(kOffV + slot * TV::kBytes, soff, n);
   };
-  // Mask tiles: each wave loads its own 32 rows (two 1 KiB slabs of 16 rows x 64 bytes) of the
-  // tile's 64 keys; rows past the sequence read as zeros. A row's bytes start at a 16-byte
-  // aligned offset (the launcher checks the strides), so each lane moves one 16-byte chunk.
-  constexpr int kLoadsM = kMT ? 2 : 0;
+  // Mask tiles: each wave loads its own 32 rows of the tile's 64 keys; rows past the sequence
+  // read as zeros. Bytes: two 1 KiB slabs of 16 rows x 64 bytes, each lane one 16-byte chunk of a
+  // row (rows start 16-byte aligned; the launcher checks the strides). Bits: one 256-byte slab of
+  // 32 rows x 8 bytes, each lane one 32-bit word (rows are whole words, 4-byte aligned).
+  constexpr int kLoadsM = kMT ? (kBits ? 1 : 2) : 0;
   rsrc4 m_rsrc{};
   uint32_t m_voff = 0, m_slab = 0;
   if constexpr (kMT) {
     const int64_t rows_left = max(Lq - row_begin, 0);
     const int64_t bytes = min(rows_left * p.mask_ss, (int64_t)0x7FFFFFFF);
     m_rsrc = make_rsrc(p.mask + b * p.mask_sb + h * p.mask_sh + (int64_t)row_begin * p.mask_ss, (uint32_t)bytes);
-    m_voff = (uint32_t)((wave * 32 + lane / 4) * p.mask_ss + (lane % 4) * 16);
-    m_slab = (uint32_t)(16 * p.mask_ss);
+    if constexpr (kBits) {
+      m_voff = (uint32_t)((wave * 32 + lane / 2) * p.mask_ss + (lane % 2) * 4);
+    } else {
+      m_voff = (uint32_t)((wave * 32 + lane / 4) * p.mask_ss + (lane % 4) * 16);
+      m_slab = (uint32_t)(16 * p.mask_ss);
+    }
   }
+  // load n of the mask tile whose first key is key0 (a multiple of 64)
   auto issue_one_m = [&](int slot, uint32_t key0, int n) __attribute__((always_inline)) {
-    load_lds16(m_rsrc, lds_address(smem + kOffM + slot * kMaskSlot + (2 * wave + n) * 1024), m_voff,
-               key0 + (uint32_t)n * m_slab);
+    if constexpr (kBits)
+      load_lds4(m_rsrc, lds_address(smem + kOffM + slot * kMaskSlot + wave * 256), m_voff, key0 >> 3);
+    else
+      load_lds16(m_rsrc, lds_address(smem + kOffM + slot * kMaskSlot + (2 * wave + n) * 1024), m_voff,
+                 key0 + (uint32_t)n * m_slab);
   };
   uint32_t dm = 0;  // key offset of the mask tile the next loading step fetches (kept beside dk)
   auto issue_m = [&](int i, int slot) __attribute__((always_inline)) {
@@ -374,7 +387,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
       for (int r = 0; r < 16; r++)
         if (key_off(r) > lim || ((MODE & kCausal) != 0 && key_off(r) < lo)) s[r] = kNegInf;
     }
-    if constexpr (kMT) {
+    if constexpr (kBits) {
+      // this row's 32 bits for the half's keys from the mask tile in the K tile's slot; register r
+      // is key 8 (r / 4) + r % 4 + 4 hl of the half, i.e. bit key_off(r) of the word shifted by 4 hl
+      const int qc = min(q, row_end - 1) - row_begin;
+      const uint32_t w = *(const uint32_t*)(smem + kOffM + ((hidx >> 1) & 1) * kMaskSlot + qc * kMaskRow +
+                                            4 * (hidx & 1));
+      if (__builtin_expect(__any(w != 0u), 1)) {
+        const uint32_t ws = w >> (4 * hl);
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+          if ((ws >> key_off(r)) & 1u) s[r] = kNegInf;
+      }
+    } else if constexpr (kMT) {
       // this row's bytes for the half's keys from the mask tile in the K tile's slot: register r
       // is key 8 (r / 4) + r % 4 + 4 hl of the half, so four aligned words hold all sixteen
       const int qc = min(q, row_end - 1) - row_begin;
@@ -723,8 +748,8 @@ hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
 
 template <typename E, int D, int DV>
 hipError_t launch_d(const FwdParams& p, int mode, hipStream_t stream) {
-  // masks whose rows start 16-byte aligned go through LDS with the K tiles; others are read per
-  // element from global memory
+  // byte masks whose rows start 16-byte aligned go through LDS with the K tiles; others are read
+  // per element from global memory (bit masks always come with kMaskTile)
   if ((mode & kMask) != 0 && (reinterpret_cast<uintptr_t>(p.mask) & 15) == 0 && p.mask_ss % 16 == 0 &&
       p.mask_sb % 16 == 0 && p.mask_sh % 16 == 0 && p.mask_ss <= (1 << 20))
     mode |= kMaskTile;
@@ -735,6 +760,9 @@ hipError_t launch_d(const FwdParams& p, int mode, hipStream_t stream) {
     case kCausal | kMask: return launch_t<E, D, DV, kCausal | kMask, 1>(p, stream);
     case kMask | kMaskTile: return launch_t<E, D, DV, kMask | kMaskTile, 2>(p, stream);
     case kCausal | kMask | kMaskTile: return launch_t<E, D, DV, kCausal | kMask | kMaskTile, 1>(p, stream);
+    case kMask | kMaskTile | kMaskBits: return launch_t<E, D, DV, kMask | kMaskTile | kMaskBits, 2>(p, stream);
+    case kCausal | kMask | kMaskTile | kMaskBits:
+      return launch_t<E, D, DV, kCausal | kMask | kMaskTile | kMaskBits, 1>(p, stream);
     case kSparse: return launch_t<E, D, DV, kSparse, 1>(p, stream);
     case kVarlen: return launch_t<E, D, DV, kVarlen, 2>(p, stream);
     case kVarlen | kCausal: return launch_t<E, D, DV, kVarlen | kCausal, 1>(p, stream);

@@ -50,10 +50,16 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
     return fail(QATTN_INVALID_ARGUMENT, "pre_tokens / next_tokens set the sparse_mode 0 range only");
   if (!allow_masks && (d->sparse_mode != 0 || d->atten_mask != nullptr || band))
     return fail(QATTN_UNSUPPORTED, "block-sparse entry points take no causal mode, band or atten_mask");
+  const int mask_shape = d->mask_kind & ~QATTN_MASK_BITS;
+  const bool mask_bits = (d->mask_kind & QATTN_MASK_BITS) != 0;
   if (d->atten_mask != nullptr) {
     if (d->layout == QATTN_LAYOUT_TND) return fail(QATTN_UNSUPPORTED, "atten_mask is not available with TND");
-    if (d->mask_kind < QATTN_MASK_SS || d->mask_kind > QATTN_MASK_BNSS)
+    if (mask_shape < QATTN_MASK_SS || mask_shape > QATTN_MASK_BNSS)
       return fail(QATTN_INVALID_ARGUMENT, "mask_kind %d", d->mask_kind);
+    if (mask_bits && (reinterpret_cast<uintptr_t>(d->atten_mask) & 3u))
+      return fail(QATTN_MISALIGNED, "a bit-packed atten_mask must be 4-byte aligned");
+    if (mask_bits && d->Skv >= (1 << 28))
+      return fail(QATTN_UNSUPPORTED, "bit-packed atten_mask with Skv=%d (needs Skv < 2^28)", d->Skv);
   }
   const int D = d->D;
   p.B = d->B;
@@ -121,10 +127,11 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
       }
     }
     if (d->atten_mask) {
-      p.mask_ss = d->Skv;
-      const int64_t ss = (int64_t)d->Sq * d->Skv;
-      p.mask_sh = d->mask_kind == QATTN_MASK_BNSS ? ss : 0;
-      p.mask_sb = d->mask_kind == QATTN_MASK_SS ? 0 : (d->mask_kind == QATTN_MASK_B1SS ? ss : ss * d->Nq);
+      // bytes per mask row: Skv, or ceil(Skv / 32) 32-bit words of bits
+      p.mask_ss = mask_bits ? 4 * (((int64_t)d->Skv + 31) / 32) : d->Skv;
+      const int64_t ss = (int64_t)d->Sq * p.mask_ss;
+      p.mask_sh = mask_shape == QATTN_MASK_BNSS ? ss : 0;
+      p.mask_sb = mask_shape == QATTN_MASK_SS ? 0 : (mask_shape == QATTN_MASK_B1SS ? ss : ss * d->Nq);
     }
   } else {
     if (d->actual_seq_lengths || d->actual_seq_lengths_kv)
@@ -263,6 +270,7 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   if (desc->sparse_mode == 2 || desc->sparse_mode == 3) mode |= qattn::kCausal;
   if (desc->pre_tokens != INT32_MAX || desc->next_tokens != INT32_MAX) mode |= qattn::kCausal;  // the band
   if (desc->atten_mask) mode |= qattn::kMask;
+  if (desc->atten_mask && (desc->mask_kind & QATTN_MASK_BITS)) mode |= qattn::kMaskTile | qattn::kMaskBits;
   if (desc->layout == QATTN_LAYOUT_TND) mode |= qattn::kVarlen;
   if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(mode)))) return rc;
   if (p.total_items == 0) return QATTN_OK;
@@ -432,6 +440,8 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   int rc = setup_common(desc, f, true, true, &total_qb);
   if (rc) return rc;
   if (f.Dv != f.D) return fail(QATTN_UNSUPPORTED, "attn_bwd needs Dv == D");
+  if (desc->atten_mask && (desc->mask_kind & QATTN_MASK_BITS))
+    return fail(QATTN_UNSUPPORTED, "attn_bwd takes byte masks (no QATTN_MASK_BITS)");
   if (!(desc->head_begin == -1 && desc->head_end == -1 && desc->qblock_begin == -1 && desc->qblock_end == -1))
     return fail(QATTN_UNSUPPORTED, "attn_bwd covers the whole problem (no head or q-block subrange)");
   const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};

@@ -19,6 +19,7 @@ enum ModeBits : int {
   kSparse = 4,  // kept-block list
   kVarlen = 8,  // TND with cumulative lengths
   kMaskTile = 16,  // with kMask: mask tiles staged in LDS beside K (16-byte aligned mask rows)
+  kMaskBits = 32,  // with kMask | kMaskTile: the mask holds one bit per key (QATTN_MASK_BITS)
 };
 
 // Everything an attention launch needs, passed by value as the kernel argument.
@@ -160,6 +161,12 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_lds16(const rsrc4& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+// The same with 4 bytes per lane (buffer_load_dword ... lds): lane l writes LDS bytes lds + 4 l .. + 3.
+__device__ __forceinline__ void load_lds4(const rsrc4& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory", "m0");
 }

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from gpu_util import O_TOL_BF16, banner, check_ml, check_o, dev_bf16, f64, to_np
-from workloads import make_block_keep, make_workload, random_bf16
+from workloads import bf16_bits_to_f32, make_block_keep, make_workload, random_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,52 @@ def test_boolean_masks(qa, kind, mode, Skv):
     check_o(to_np(o), ro, O_TOL_BF16)
     check_ml(to_np(m), to_np(l), rm, rl)
     assert np.all(to_np(o)[:, :, 17] == 0)
+
+
+def pack_mask_bits(mask: np.ndarray) -> np.ndarray:
+    """Bit-packed form of a uint8 mask: rows of ceil(Skv / 32) little-endian 32-bit words, key j
+    in bit j % 32 of word j // 32 (numpy's little-endian packbits, padded to whole words)."""
+    Skv = mask.shape[-1]
+    W = (Skv + 31) // 32
+    padded = np.zeros(mask.shape[:-1] + (32 * W,), dtype=np.uint8)
+    padded[..., :Skv] = mask != 0
+    return np.ascontiguousarray(np.packbits(padded, axis=-1, bitorder="little")).view("<i4")
+
+
+# bit-packed masks: every shape and causal mode, ragged rows (Skv = 260: 9 words per row; 33: two
+# words, the second one bit), checked against the oracle and bit for bit against the byte mask
+@pytest.mark.parametrize("kind,mode,Skv,dt,Dv", [("SS", 0, 260, "bf16", 128), ("B1SS", 0, 260, "bf16", 128),
+                                                ("BNSS", 0, 260, "bf16", 128), ("SS", 2, 260, "bf16", 128),
+                                                ("BNSS", 3, 260, "bf16", 128), ("SS", 0, 1024, "bf16", 128),
+                                                ("B1SS", 3, 1024, "bf16", 128), ("BNSS", 2, 272, "bf16", 128),
+                                                ("SS", 0, 33, "bf16", 128), ("B1SS", 2, 300, "fp16", 64),
+                                                ("SS", 3, 500, "bf16", 64)])
+def test_bit_packed_masks(qa, kind, mode, Skv, dt, Dv):
+    B, Nq, Nkv, Sq, D = 2, 4, 2, 200, 128
+    banner(f"bit mask {kind} mode={mode} Skv={Skv} {dt} Dv={Dv}")
+    q, k, v = _bnsd(70 + mode, B, Nq, Nkv, Sq, Skv, D)
+    v = np.ascontiguousarray(v[..., :Dv])
+    rng = np.random.default_rng(50 + Skv)
+    shape = {"SS": (Sq, Skv), "B1SS": (B, 1, Sq, Skv), "BNSS": (B, Nq, Sq, Skv)}[kind]
+    mask = (rng.random(shape) < 0.3).astype(np.uint8)
+    mask[..., 17, :] = 1                                   # a fully masked row
+    mask[..., 40, :] = 0                                   # and an unmasked one
+    words = pack_mask_bits(mask)
+    up = (lambda x: dev_bf16(x)) if dt == "bf16" else \
+        (lambda x: torch.from_numpy(bf16_bits_to_f32(x).astype(np.float16)).cuda())
+    qd, kd, vd = up(q), up(k), up(v)
+    scale = 0.09
+    o, m, l = qa.attn_fwd(qd, kd, vd, scale=scale, sparse_mode=mode, atten_mask=torch.from_numpy(words).cuda())
+    ob, mb, lb = qa.attn_fwd(qd, kd, vd, scale=scale, sparse_mode=mode, atten_mask=torch.from_numpy(mask).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ob.view(torch.int16)), "bits and bytes masks differ"
+    assert torch.equal(m, mb) and torch.equal(l, lb)
+    unpacked = oracle.atten_mask_from_bits(words, Skv)
+    assert np.array_equal(unpacked, mask)
+    ro, rm, rl = oracle.attention(f64(q), f64(k), f64(v), scale, sparse_mode=mode, atten_mask=unpacked)
+    check_o(o.float().cpu().numpy().astype(np.float64), ro, O_TOL_BF16)
+    check_ml(to_np(m), to_np(l), rm, rl)
+    assert np.all(o.float().cpu().numpy()[:, :, 17] == 0)
 
 
 @pytest.mark.parametrize("lens_q,lens_kv,mode,Nq,Nkv,D", [

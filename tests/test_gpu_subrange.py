@@ -48,11 +48,13 @@ def _pieces(n_heads, n_qb):
     return splits
 
 
-# S = 1100: mask rows read per element; S = 1104: 16-byte aligned mask rows, staged in LDS
+# S = 1100: byte-mask rows read per element; S = 1104: 16-byte aligned byte-mask rows, staged in
+# LDS; "bits": the same mask bit-packed (always staged in LDS)
 @pytest.mark.parametrize("mode,masked,band,S", [(0, False, None, 1100), (2, False, None, 1100), (3, False, None, 1100),
                                                (0, True, None, 1100), (3, True, None, 1100), (0, False, (200, 30), 1100),
                                                (0, True, (64, 300), 1100), (0, True, None, 1104), (3, True, None, 1104),
-                                               (0, True, (64, 300), 1104)])
+                                               (0, True, (64, 300), 1104), (0, "bits", None, 1100),
+                                               (3, "bits", None, 1104), (0, "bits", (64, 300), 1100)])
 def test_dense_subranges(qa, mode, masked, band, S):
     B, Nq, Nkv, D = 1, 8, 4, 128
     banner(f"subrange dense mode={mode} masked={masked} S={S}")
@@ -63,6 +65,9 @@ def test_dense_subranges(qa, mode, masked, band, S):
     if masked:  # B1SS boolean mask, about 20% of the keys masked
         g = torch.Generator(device="cuda").manual_seed(5)
         mask = (torch.rand((B, 1, S, S), generator=g, device="cuda") < 0.2).to(torch.uint8)
+        if masked == "bits":
+            from test_gpu_attention import pack_mask_bits
+            mask = torch.from_numpy(pack_mask_bits(mask.cpu().numpy())).cuda()
     bk = {} if band is None else dict(pre_tokens=band[0], next_tokens=band[1])
     full = qa.attn_fwd(q, k, v, scale=0.1, sparse_mode=mode, atten_mask=mask, **bk)
     nqb = (S + 127) // 128

@@ -61,13 +61,14 @@ def fwd(request):
 
 
 def test_fwd_instantiations(fwd):
-    """Each element type gets every (D, Dv) pair in all nine modes."""
+    """Each element type gets every (D, Dv) pair in all eleven modes."""
     shapes = set()
     for name in fwd:
         m = FWD_NAME.search(name)
         assert m, name
         shapes.add((int(m.group(2)), int(m.group(3)), int(m.group(4))))
-    modes = [0, 1, 2, 3, 4, 8, 9, 18, 19]  # 18, 19: kMask (| kCausal) | kMaskTile
+    # 18, 19: kMask (| kCausal) | kMaskTile; 50, 51: the same with kMaskBits (bit-packed masks)
+    modes = [0, 1, 2, 3, 4, 8, 9, 18, 19, 50, 51]
     assert shapes == {(d, dv, mode) for d, dv in [(64, 64), (128, 128), (128, 64)] for mode in modes}
     assert len({FWD_NAME.search(n).group(1) for n in fwd}) == 1
 
@@ -154,5 +155,5 @@ def test_m0_only_feeds_direct_lds_loads(src):
         uses += 1
         assert re.match(r"s_mov_b32 m0, s\d+$", ln), ln
         nxt = [x for x in lines[i + 1:i + 4] if not x.startswith("s_nop")]
-        assert nxt and re.match(r"buffer_load_dwordx4 .* offen lds$", nxt[0]), (ln, lines[i + 1:i + 4])
+        assert nxt and re.match(r"buffer_load_dword(x4)? .* offen lds$", nxt[0]), (ln, lines[i + 1:i + 4])
     assert uses > 0
