@@ -132,6 +132,61 @@ def test_c5_qbsa_60k_full(qa):
             check_ml(to_np(m[0, h, rows]), to_np(l[0, h, rows]), mm, ll, what=f"c5 h{h} qb{qb}")
 
 
+def test_sweep_128k_sampled(qa):
+    """The long end of the EagleQBSA article's operator sweep (Fig. 4.1: S up to 128K at N = 40,
+    D = 128): dense, block-sparse (sparsity 0.9) and quantised block-sparse (sparsity 0.63) at
+    S = 131072 on 2 heads. A row's arithmetic does not depend on how many heads a launch holds
+    (the subrange tests check it bit for bit), so 2 heads at the full length are the work items of
+    the 40-head sweep. Sampled q-blocks (first, interior, last) against the oracle."""
+    S = 131072
+    wd = make_workload("c2_dense_8k", S=S, N=2)
+    banner(f"128k dense {wd.q.shape}")
+    o, m, l = qa.attn_fwd(dev_bf16(wd.q), dev_bf16(wd.k), dev_bf16(wd.v), scale=wd.scale)
+    torch.cuda.synchronize()
+    for h, qbs in ((0, [0, 1023]), (1, [512])):
+        rows = _rows_of(qbs, S)
+        ro, rm, rl = oracle.attention_rows(f64(wd.q[0, h]), f64(wd.k[0, h]), f64(wd.v[0, h]), wd.scale, rows)
+        check_o(to_np(o[0, h, rows]), ro, O_TOL_BF16, f"dense128k h{h}")
+        check_ml(to_np(m[0, h, rows]), to_np(l[0, h, rows]), rm, rl, what=f"dense128k h{h}")
+    del wd, o, m, l
+
+    wb = make_workload("c4_blocksparse_64k", S=S, N=2)
+    banner(f"128k block-sparse {wb.q.shape} kept fraction {wb.keep.mean():.4f}")
+    counts, idx = qa.build_kv_block_list(torch.from_numpy(wb.keep).cuda())
+    o, m, l = qa.attn_fwd_blocksparse(dev_bf16(wb.q), dev_bf16(wb.k), dev_bf16(wb.v), counts, idx, scale=wb.scale)
+    torch.cuda.synchronize()
+    for h, qbs in ((0, [0, 1023]), (1, [300, 777])):
+        ro, rm, rl = oracle.attention_block_sparse(f64(wb.q[0, h]), f64(wb.k[0, h]), f64(wb.v[0, h]), wb.scale,
+                                                   wb.keep[0, h], qblocks=qbs)
+        rows = _rows_of(qbs, S)
+        check_o(to_np(o[0, h, rows]), ro, O_TOL_BF16, f"bsa128k h{h}")
+        check_ml(to_np(m[0, h, rows]), to_np(l[0, h, rows]), rm, rl, what=f"bsa128k h{h}")
+    del wb, o, m, l, counts, idx
+
+    wq = make_workload("c5_qbsa_60k", S=S, N=2)
+    banner(f"128k quantised block-sparse {wq.q.shape} kept fraction {wq.keep.mean():.4f}")
+    qq, qs = qa.quantize_qk_perblock_int8(dev_bf16(wq.q))
+    kq, ks = qa.quantize_qk_perblock_int8(dev_bf16(wq.k))
+    vq, vs = qa.quantize_v_perchannel_fp8(dev_bf16(wq.v))
+    counts, idx = qa.build_kv_block_list(torch.from_numpy(wq.keep).cuda())
+    o, m, l = qa.attn_fwd_qbsa(qq, kq, vq, qs, ks, vs, counts, idx, scale=wq.scale)
+    torch.cuda.synchronize()
+    for h in (0, 1):
+        rqc, rqs = oracle.quantize_qk_perblock_int8(f64(wq.q[:, h:h + 1]))
+        rkc, rks = oracle.quantize_qk_perblock_int8(f64(wq.k[:, h:h + 1]))
+        rvc, rvs = oracle.quantize_v_perchannel_fp8(f64(wq.v[:, h:h + 1]))
+        assert np.array_equal(to_np(qq[:, h:h + 1]), rqc) and np.array_equal(to_np(kq[:, h:h + 1]), rkc)
+        assert np.array_equal(to_np(vq[:, h:h + 1]), rvc)
+        assert np.array_equal(to_np(vs[:, h:h + 1]).view(np.uint32), rvs.view(np.uint32))
+        for qb in ((0, 1023) if h == 0 else (640,)):
+            oo, mm, ll = oracle.qbsa_qblock(rqc[0, 0], rkc[0, 0], rvc[0, 0], rqs[0, 0, qb], rks[0, 0], rvs[0, 0],
+                                            wq.scale, np.nonzero(wq.keep[0, h, qb])[0], qb)
+            rows = slice(qb * 128, qb * 128 + 128)
+            check_o_channel_scaled(to_np(o[0, h, rows])[None, None], oo[None, None], f64(wq.v[:, h:h + 1]),
+                                   O_TOL_QUANT, f"qbsa128k h{h} qb{qb}")
+            check_ml(to_np(m[0, h, rows]), to_np(l[0, h, rows]), mm, ll, what=f"qbsa128k h{h} qb{qb}")
+
+
 def _grad_check(g, ref, what, rtol=2e-2):
     """The backward tests' bound: max-abs error <= rtol * max(1, max |reference|)."""
     g = to_np(g).astype(np.float64)

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from gpu_util import O_TOL_QUANT, banner, check_ml, check_o, check_o_channel_scaled, dev_bf16, f64, to_np
-from workloads import make_block_keep, make_workload, random_bf16
+from workloads import bf16_bits_to_f32, make_block_keep, make_workload, random_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +57,61 @@ def test_quant_v_bitexact(qa, B, N, S, D):
     rc, rs = oracle.quantize_v_perchannel_fp8(f64(x))
     assert np.array_equal(to_np(scale).view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(to_np(codes), rc)
+
+
+def test_quant_qk_rounding_ties(qa):
+    """Exact ties of the INT8 rounding (half-way between two integers) go to the even code, as the
+    oracle's rint does: each block's amax is 127 * 2^e, so its scale is exactly 2^e and x / scale
+    lands on the tie itself. Every value below is exact in bf16."""
+    from workloads import f32_to_bf16_bits
+    B, N, S, D = 1, 2, 384, 64
+    rng = np.random.default_rng(11)
+    ties = np.array([0.5, 1.5, 2.5, 3.5, 62.5, 63.5, 100.5, 125.5, 126.5], dtype=np.float32)
+    x = np.zeros((B, N, S, D), dtype=np.float32)
+    for n in range(N):
+        for blk, e in enumerate((0, -3, 5)):
+            vals = rng.choice(np.concatenate([ties, -ties]), size=(128, D)).astype(np.float32)
+            vals[0, 0] = 127.0                              # the block's amax: scale = 2^e exactly
+            x[0, n, blk * 128:(blk + 1) * 128] = vals * np.float32(2.0 ** e)
+    bits = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(bits), x)
+    codes, scale = qa.quantize_qk_perblock_int8(dev_bf16(bits))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_qk_perblock_int8(f64(bits))
+    assert np.array_equal(to_np(scale).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(to_np(codes), rc)
+    t = rc[0, 0, :128][x[0, 0, :128] == 2.5]
+    assert t.size and np.all(t == 2)                      # 2.5 -> 2, not 3
+    t = rc[0, 0, :128][x[0, 0, :128] == -126.5]
+    assert t.size and np.all(t == -126)
+
+
+def test_quant_v_rounding_ties(qa):
+    """Exact E4M3 midpoints (normal and subnormal, both signs) go to the even code, as in the
+    oracle's encoder: each channel's amax is 448 * 2^e, so its scale is exactly 2^e and v / scale
+    is the midpoint itself. Every value below is exact in bf16."""
+    from workloads import f32_to_bf16_bits
+    table = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))          # non-negative finite values
+    mids = ((table[1:] + table[:-1]) / 2).astype(np.float32)             # every midpoint, 2^-10 .. 432
+    B, N, S, D = 1, 2, len(mids) * 2, 128
+    x = np.zeros((B, N, S, D), dtype=np.float32)
+    for d in range(D):
+        e = (d % 5) - 2
+        col = np.concatenate([mids, -mids]) * np.float32(2.0 ** e)
+        x[0, d % N, :, d] = np.roll(col, d)
+        x[0, (d + 1) % N, :, d] = np.roll(col, -d)
+        x[0, 0, d % S, d] = x[0, 1, (d + 7) % S, d] = np.float32(448.0 * 2.0 ** e)   # amax of the channel
+    bits = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(bits), x)
+    codes, scale = qa.quantize_v_perchannel_fp8(dev_bf16(bits))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_v_perchannel_fp8(f64(bits))
+    assert np.array_equal(to_np(scale).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(to_np(codes), rc)
+    unit = x[..., 2::5]                                                   # channels with scale 1
+    assert np.all(rc[..., 2::5][unit == np.float32(1.0625)] == 0x38)      # 1.0625 -> 1.0
+    assert np.all(rc[..., 2::5][unit == np.float32(1.1875)] == 0x3A)      # 1.1875 -> 1.25
+    assert np.all(rc[..., 2::5][unit == np.float32(-2.0 ** -10)] == 0x80)  # -2^-10 -> -0
 
 
 def _qbsa_case(qa, S, Nq, Nkv, D, p, seed):
