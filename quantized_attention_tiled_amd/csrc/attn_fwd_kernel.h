@@ -118,8 +118,10 @@ struct Tile {
   static constexpr int kLoadsPerWave = kKT / kRowsPerLoad / kWaves;
   // K: column reads of 16 consecutive rows must hit 16 distinct bank groups
   __device__ static int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-  // V: a transposed read touches 4 consecutive rows x 2 adjacent chunks; keep the 8 apart
-  __device__ static int vswz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
+  // V: a transposed read (ds_read_b64_tr_b16) covers 8 rows x 4 chunks, rows 0-3 in lanes 0-31 and
+  // rows 4-7 in lanes 32-63; at D = 128 (a row spans all 64 banks) rows r and r + 1 .. r + 3 of one
+  // half must use disjoint chunk groups, which 4 (row & 3) gives (no bank conflict)
+  __device__ static int vswz(int row) { return D == 128 ? 4 * (row & 3) : 2 * ((row >> 1) & 3); }
 };
 
 // NQB q-blocks per workgroup share every K/V tile: 4 NQB waves, two waves per SIMD either way
