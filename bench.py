@@ -204,14 +204,76 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
 
 
-def sustained_clock_power(step, step_ms, seconds=3.0, settle=1.0):
-    """GPU clock and socket power while the step runs back to back for about `seconds`, outside the
-    timed region: one thread keeps launching steps while this one reads `amd-smi metric -c -p`.
-    The tool's readings lag the load by up to a second, so samples before `settle` seconds are
-    dropped. Returns the kept samples (time, gfx clock averaged over the XCDs, socket power) and
-    their medians, or None when amd-smi is missing or prints something else."""
-    import shutil
+def _smi_clock_power(smi):
+    """One `amd-smi metric -c -p` reading: (gfx clock averaged over the XCDs in MHz, socket power in
+    W), or None when the tool is missing or prints something else."""
     import subprocess
+    try:
+        r = subprocess.run([smi, "metric", "-c", "-p", "--json"], capture_output=True, text=True, timeout=15)
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clks = [c["clk"]["value"] for key, c in g["clock"].items()
+                if key.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)
+                and isinstance(c["clk"].get("value"), (int, float))]
+        pw = g["power"]["socket_power"]["value"]
+    except Exception:  # noqa: BLE001 - a missing or changed tool only ends the sampling
+        return None
+    if not clks or not isinstance(pw, (int, float)):
+        return None
+    return float(np.mean(clks)), float(pw)
+
+
+class ClockSampler:
+    """The GPU clock and socket power while the timed steps run: a host thread reads `amd-smi metric
+    -c -p` back to back between start() and stop(). The tool's readings lag the load by up to about
+    a second, so readings taken in the first `settle` seconds are dropped; the timed region must
+    last a few seconds for several readings to remain."""
+
+    def __init__(self, settle: float = 0.8):
+        import shutil
+        self.smi = shutil.which("amd-smi")
+        self.settle = settle
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    def start(self):
+        import threading
+        if self.smi is None:
+            return self
+        self._stop = threading.Event()
+        t0 = time.perf_counter()
+
+        def loop():
+            while not self._stop.is_set():
+                r = _smi_clock_power(self.smi)
+                if r is None:
+                    break
+                if not self._stop.is_set():
+                    self.samples.append((round(time.perf_counter() - t0, 2), round(r[0]), r[1]))
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=30)
+        kept = [x for x in self.samples if x[0] >= self.settle]
+        if not kept:
+            return None
+        return {"median_mhz": int(np.median([c for _, c, _ in kept])),
+                "socket_power_w": round(float(np.median([w for _, _, w in kept]))),
+                "samples_t_s_mhz_w": kept, "source": "amd-smi metric -c -p, read while the timed steps ran"}
+
+
+def sustained_clock_power(step, step_ms, seconds=3.0, settle=1.0):
+    """GPU clock and socket power while the step runs back to back for about `seconds` (the power
+    study's schedules): one thread keeps launching steps while this one reads amd-smi. Readings
+    before `settle` seconds are dropped (the tool lags the load). Returns the kept samples (time,
+    gfx clock averaged over the XCDs, socket power) and their medians, or None without amd-smi."""
+    import shutil
     import threading
     import torch
     smi = shutil.which("amd-smi")
@@ -233,18 +295,11 @@ def sustained_clock_power(step, step_ms, seconds=3.0, settle=1.0):
     time.sleep(settle)
     samples = []
     while busy.is_set() and len(samples) < 12 and time.perf_counter() - t0 < 4 * seconds:
-        try:
-            r = subprocess.run([smi, "metric", "-c", "-p", "--json"], capture_output=True, text=True, timeout=15)
-            d = json.loads(r.stdout)
-            g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
-            clks = [c["clk"]["value"] for key, c in g["clock"].items()
-                    if key.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)
-                    and isinstance(c["clk"].get("value"), (int, float))]
-            pw = g["power"]["socket_power"]["value"]
-        except Exception:  # noqa: BLE001 - a missing or changed tool only ends the sampling
+        r = _smi_clock_power(smi)
+        if r is None:
             break
-        if clks and isinstance(pw, (int, float)) and busy.is_set():
-            samples.append((round(time.perf_counter() - t0, 2), round(float(np.mean(clks))), float(pw)))
+        if busy.is_set():
+            samples.append((round(time.perf_counter() - t0, 2), round(r[0]), r[1]))
     t.join(timeout=60)
     if not samples:
         return None
@@ -400,32 +455,31 @@ def power_study(S, gaps_ms, chunk_counts=(10,), seconds=3.0):
         if N % chunks:
             raise ValueError(f"{chunks} chunks do not divide {N} heads")
         cyc = cycles_for(gap / chunks)
-        if True:
-            for _ in range(3):
-                schedule(kind, cyc, chunks)
-            torch.cuda.synchronize()
-            reps = 5
-            evs = []
-            e_all0, e_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e_all0.record(stream)
-            for _ in range(reps):
-                schedule(kind, cyc, chunks, evs)
-            e_all1.record(stream)
-            torch.cuda.synchronize()
-            total = e_all0.elapsed_time(e_all1) / reps
-            fa_ms = sum(a.elapsed_time(b) for t, a, b in evs if t == "fa") / reps
-            gap_total = sum(a.elapsed_time(b) for t, a, b in evs if t == "gap") / reps
-            sustained = sustained_clock_power(lambda: schedule(kind, cyc, chunks), total, seconds=seconds)
-            flop = 4.0 * D * B * N * S * S
-            line = {"study": "power_cap", "schedule": kind, "chunks": chunks, "gap_ms_per_layer": gap, "S": S, "N": N,
-                    "launches": 1 if kind == "baseline" else chunks * (1 if kind == "insertcomm" else 2),
-                    "ms_per_layer": round(total, 3), "attention_ms": round(fa_ms, 3), "gap_ms": round(gap_total, 3),
-                    "attention_tflops": round(flop / fa_ms / 1e9, 1)}
-            if sustained:
-                line["sclk_mhz"] = sustained["sclk_mhz"]
-                line["socket_power_w"] = sustained["socket_power_w"]
-                line["energy_j_per_layer"] = round(sustained["socket_power_w"] * total * 1e-3, 3)
-            print(json.dumps(line), flush=True)
+        for _ in range(3):
+            schedule(kind, cyc, chunks)
+        torch.cuda.synchronize()
+        reps = 5
+        evs = []
+        e_all0, e_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_all0.record(stream)
+        for _ in range(reps):
+            schedule(kind, cyc, chunks, evs)
+        e_all1.record(stream)
+        torch.cuda.synchronize()
+        total = e_all0.elapsed_time(e_all1) / reps
+        fa_ms = sum(a.elapsed_time(b) for t, a, b in evs if t == "fa") / reps
+        gap_total = sum(a.elapsed_time(b) for t, a, b in evs if t == "gap") / reps
+        sustained = sustained_clock_power(lambda: schedule(kind, cyc, chunks), total, seconds=seconds)
+        flop = 4.0 * D * B * N * S * S
+        line = {"study": "power_cap", "schedule": kind, "chunks": chunks, "gap_ms_per_layer": gap, "S": S, "N": N,
+                "launches": 1 if kind == "baseline" else chunks * (1 if kind == "insertcomm" else 2),
+                "ms_per_layer": round(total, 3), "attention_ms": round(fa_ms, 3), "gap_ms": round(gap_total, 3),
+                "attention_tflops": round(flop / fa_ms / 1e9, 1)}
+        if sustained:
+            line["sclk_mhz"] = sustained["sclk_mhz"]
+            line["socket_power_w"] = sustained["socket_power_w"]
+            line["energy_j_per_layer"] = round(sustained["socket_power_w"] * total * 1e-3, 3)
+        print(json.dumps(line), flush=True)
     return 0
 
 
@@ -500,7 +554,7 @@ def backward_bench(a):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c2_dense_8k")
     ap.add_argument("--seq", type=int, default=None, help="override S (dense BNSD configs)")
@@ -523,6 +577,9 @@ def main(argv=None):
     ap.add_argument("--mask", choices=["none", "bytes", "bits"], default="none",
                     help="dense BNSD configs: an SS atten_mask [S, S], one byte per key or bit-packed")
     ap.add_argument("--mask-density", type=float, default=0.0, help="fraction of masked keys of --mask (i.i.d.)")
+    ap.add_argument("--q-gain", type=float, default=1.0,
+                    help="dense configs: multiply Q by this factor (a peaked softmax: rows whose max outgrows the "
+                         "16-bit kernel's reference take its second key pass)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -563,6 +620,13 @@ def main(argv=None):
         name += f"_dv{a.dv}"
     if a.dtype != "bf16":
         name += f"_{a.dtype}"
+    if a.q_gain != 1.0:
+        if kind != "dense":
+            log("--q-gain applies to the dense configs")
+            return 2
+        from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+        w.q = f32_to_bf16_bits(bf16_bits_to_f32(w.q) * np.float32(a.q_gain))
+        name += f"_qgain{a.q_gain:g}"
     dev = torch.device("cuda:0")
 
     def up(bits):
@@ -650,6 +714,7 @@ def main(argv=None):
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
     log(f"timing {a.steps} steps")
     torch.cuda.synchronize()
+    sampler = None if a.no_smi else ClockSampler().start()
     wall0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(a.steps):
@@ -657,6 +722,7 @@ def main(argv=None):
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    clock = sampler.stop() if sampler is not None else None
     per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(a.steps)])
     kper = np.array([ka.elapsed_time(kb) for ka, kb in kev])
     total_ms = ev[0].elapsed_time(ev[a.steps])
@@ -672,7 +738,12 @@ def main(argv=None):
     roof = {"bound": "mfma", "achieved": round(kvalue, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(kvalue / peak, 4), "traffic": traffic, "kernel": "attn_fwd_kernel" if kind != "qbsa"
             else "attn_qbsa_kernel", "flop_per_launch": ex, "launch_ms": round(kms, 4)}
-    sustained = None if a.no_smi else sustained_clock_power(step, ms)
+    if clock:
+        # the published peak assumes 2400 MHz; at the clock measured during the timed steps the
+        # matrix cores can deliver peak * clock / 2400
+        roof["clock_mhz_during_timed"] = clock["median_mhz"]
+        roof["clock_limited_peak"] = round(peak * clock["median_mhz"] / 2400.0, 1)
+        roof["frac_of_clock_limited_peak"] = round(kvalue / roof["clock_limited_peak"], 4)
     cpu = None
     if not a.no_cpu:
         log(f"cpu oracle baseline (~{a.cpu_seconds:.0f} s)")
@@ -686,6 +757,8 @@ def main(argv=None):
         conf = {"workload": wl, "layout": "BNSD", "B": w.B, "N": w.Nq, "Nkv": w.Nkv, "S": w.Sq, "D": w.D}
         if a.dv:
             conf["Dv"] = a.dv
+        if a.q_gain != 1.0:
+            conf["q_gain"] = a.q_gain
         if amask is not None:
             conf["atten_mask"] = {"kind": "SS", "format": a.mask, "density": a.mask_density,
                                   "bytes": int(amask.numel() * amask.element_size())}
@@ -702,7 +775,7 @@ def main(argv=None):
                    "min_ms": round(float(per.min()), 4), "cv": round(float(per.std() / per.mean()), 4),
                    "algorithmic_bytes": alg_bytes, "algorithmic_gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
                    "wall_s_timed": round(wall, 3), "kernel_source_sha": source_hash(kind),
-                   "sustained_clock_power": sustained},
+                   "clock_during_timed": clock},
     }
     print(json.dumps(line), flush=True)
     return 0

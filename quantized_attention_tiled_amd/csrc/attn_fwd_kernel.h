@@ -226,10 +226,20 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
   }
   int ntiles;
   const int32_t* list = nullptr;
+  int nkept = 0, kept0 = 0;
   if constexpr ((MODE & kSparse) != 0) {
     const int64_t row = ((int64_t)b * p.Nq + h) * p.QB + qblk;
     list = p.idx + row * p.KB;
-    ntiles = 2 * min(max(p.counts[row], 0), p.KB);
+    nkept = min(max(p.counts[row], 0), p.KB);
+    ntiles = 2 * nkept;
+    // Visit order: the kept list rotated to start near kv-block (KB / 64) * row. An XCD runs about
+    // 64 of these workgroups at once, started one after another in row order, and each crosses
+    // the whole kv range in its lifetime; with the start moving 1/64 of the range per row, the
+    // workgroups running together walk through the same kv-blocks at the same time and share
+    // them in the XCD's L2. The block-sparse result does not depend on the visit order, and the
+    // order is a function of (batch, head, q-block) alone, so subrange launches stay bit-identical.
+    const int64_t start_blk = (row * ((p.KB + 63) / 64)) % max(p.KB, 1);
+    kept0 = (int)((start_blk * nkept) / max(p.KB, 1));
   } else {
     ntiles = kv_end > t0 * kKT ? (kv_end - t0 * kKT + kKT - 1) / kKT : 0;
   }
@@ -239,7 +249,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
     if constexpr ((MODE & kSparse) != 0) {
       // a scalar load (the list is uniform and read-only here): consecutive entries share a line
       // of the scalar cache, where a vector load waits a full memory round trip after each barrier
-      const int blk = ((const __attribute__((address_space(4))) int32_t*)list)[i >> 1];
+      int j = kept0 + (i >> 1);
+      j = j >= nkept ? j - nkept : j;
+      const int blk = ((const __attribute__((address_space(4))) int32_t*)list)[j];
       return (blk >= 0 && blk < p.KB) ? blk * kBlock + (i & 1) * kKT : -1;
     } else {
       return (t0 + i) * kKT;
