@@ -145,19 +145,6 @@ __device__ __forceinline__ u32x4 read_row(const uint8_t* lds, int row, int t, in
   return *(const u32x4*)(lds + BTile<D>::at(row, 2 * t + hl));
 }
 
-template <int V>
-struct IC {
-  static constexpr int value = V;
-};
-
-// Empty volatile asm statements keep their relative order: pin_use(x) needs x at this point, so the
-// work that produces x cannot sink below it; together with the scheduling barriers this keeps each
-// slot's vector work next to its matrix product.
-template <typename T>
-__device__ __forceinline__ void pin_use(const T& x) {
-  asm volatile("" ::"v"(x));
-}
-
 // register r of a C-layout accumulator holds row 8 (r / 4) + 4 hl + r % 4 of its 32-row block
 __device__ __forceinline__ int c_row(int r, int hl) { return 8 * (r >> 2) + 4 * hl + (r & 3); }
 

@@ -82,31 +82,6 @@ struct Elem<_Float16> {
   }
 };
 
-template <int V>
-struct IC {
-  static constexpr int value = V;
-};
-
-// Empty volatile asm statements keep their relative order. pin_def(x) makes x's value opaque at this
-// point, so nothing computed from x can be moved above it; pin_use(x) needs x, so nothing that
-// feeds x can be moved below it. Together they keep each pipeline step's VALU work inside the
-// step, between its MFMAs, where the compiler's code motion would otherwise hoist or sink it.
-__device__ __forceinline__ void pin_def(float& x) { asm volatile("" : "+v"(x)); }
-template <typename T>
-__device__ __forceinline__ void pin_use(const T& x) {
-  asm volatile("" ::"v"(x));
-}
-
-// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap returns both halves)
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return __int_as_float(r[0]) + __int_as_float(r[1]);
-}
-
 // LDS tile geometry: 64 rows of D 16-bit elements (D * 2 bytes), 16-byte chunks XOR-swizzled per
 // row, loaded by kWaves waves.
 template <int D, int kWaves>

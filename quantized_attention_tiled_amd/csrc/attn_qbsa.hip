@@ -62,20 +62,6 @@ constexpr float kMagic = 12582912.0f;
 constexpr int kNegInfBits = (int)0xFF800000u;
 constexpr float kMinCt = 1e-30f;  // keeps ct > 0 (all-zero blocks have scale 0) so -inf stays -inf
 
-template <int V>
-struct IC {
-  static constexpr int value = V;
-};
-
-// Empty volatile asm statements keep their relative order. pin_def(x) makes x's value opaque at
-// this point; pin_use(x) needs x here. Together they keep each pipeline step's VALU work inside
-// the step, between its MFMAs.
-__device__ __forceinline__ void pin_def(float& x) { asm volatile("" : "+v"(x)); }
-template <typename T>
-__device__ __forceinline__ void pin_use(const T& x) {
-  asm volatile("" ::"v"(x));
-}
-
 __device__ __forceinline__ int imax3(int a, int b, int c) { return max(max(a, b), c); }
 
 // a register whose contents do not matter (an empty asm output costs no instruction)
@@ -90,11 +76,6 @@ __device__ __forceinline__ int pair_max_i(int x) {
   const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return max((int)r[0], (int)r[1]);
 }
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return __int_as_float(r[0]) + __int_as_float(r[1]);
-}
-
 // LDS tile geometry: 128 rows of D bytes, 16-byte chunks XOR-swizzled per row.
 template <int D>
 struct QTile {
