@@ -91,19 +91,28 @@ struct Tile {
   static constexpr int kBytes = kKT * kRowBytes;           // one K or V tile
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;    // rows one wave-wide 64 x 16 B load covers
   static constexpr int kLoadsPerWave = kKT / kRowsPerLoad / kWaves;
-  // K: column reads of 16 consecutive rows must hit 16 distinct bank groups
-  __device__ static int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  // K: column reads of 16 consecutive rows must hit 16 distinct bank groups (from D = 128 on every
+  // row starts at bank 0, so the low four chunk bits must differ)
+  __device__ static int kswz(int row) { return D >= 128 ? (row & 15) : ((row >> 1) & 7); }
   // V: a transposed read (ds_read_b64_tr_b16) covers 8 rows x 4 chunks, rows 0-3 in lanes 0-31 and
-  // rows 4-7 in lanes 32-63; at D = 128 (a row spans all 64 banks) rows r and r + 1 .. r + 3 of one
-  // half must use disjoint chunk groups, which 4 (row & 3) gives (no bank conflict)
-  __device__ static int vswz(int row) { return D == 128 ? 4 * (row & 3) : 2 * ((row >> 1) & 3); }
+  // rows 4-7 in lanes 32-63; from D = 128 on (every row starts at bank 0) rows r and r + 1 .. r + 3
+  // of one half must use disjoint chunk groups, which 4 (row & 3) gives (no bank conflict)
+  __device__ static int vswz(int row) { return D >= 128 ? 4 * (row & 3) : 2 * ((row >> 1) & 3); }
 };
 
-// NQB q-blocks per workgroup share every K/V tile: 4 NQB waves, two waves per SIMD either way
-// (two workgroups per CU for NQB = 1, one for NQB = 2). D is the query/key head dimension, DV
-// the value head dimension (DV <= D).
+// Workgroups per CU the kernel is built for: two waves per SIMD (two workgroups of one q-block or
+// one of two) up to D = 128; one wave per SIMD beyond, where a wave's Q^T and O^T registers alone
+// take 192 of the 256 a two-wave budget leaves.
+template <int D, int NQB>
+constexpr int fwd_blocks_per_cu() { return D > 128 ? 1 : 2 / NQB; }
+
+// NQB q-blocks per workgroup share every K/V tile (4 NQB waves). D and DV are the query/key and
+// value head dimensions the kernel is built for (DV <= D); the problem's own p.D <= D and
+// p.Dv <= DV (multiples of 8) are padded with zeros: the Q registers and the LDS tiles hold zeros
+// past them, so the padded columns add exact zeros to every score, and O is stored up to p.Dv.
 template <typename E, int D, int DV, int MODE, int NQB>
-__global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQB>())) void attn_fwd_kernel(
+    const FwdParams p) {
   typedef typename Elem<E>::v8 ev8;
   constexpr float kRefSlack = Elem<E>::kSlack;
   constexpr int kWaves = kWavesPerBlock * NQB;
@@ -235,29 +244,43 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
 
   // ---- direct HBM -> LDS tile loads (buffer_load_dwordx4 ... lds): load n of this wave fills
   // 1 KiB slab n * kWaves + wave, i.e. rows lrow + n * kWaves * kRowsPerLoad, one 16-byte chunk
-  // per lane. The swizzle of a lane's chunk does not depend on n, so one per-lane byte offset
-  // serves every load; the tile's key offset goes in the scalar offset. The buffer extent is the
-  // sequence's valid rows: rows past it (a ragged last tile) read as zeros and are masked. ----
+  // per lane. The swizzles repeat every 16 rows; where loads are 16 rows apart (or a multiple) the
+  // swizzle of a lane's chunk does not depend on n, else (8 rows apart: K at D = 256) it takes
+  // two values, for even and odd n, and so does the per-lane byte offset. The tile's key offset
+  // goes in the scalar offset. The buffer extent is the sequence's valid rows: rows past it (a
+  // ragged last tile) read as zeros and are masked. ----
   const int64_t key_bytes = p.k_ss * 2;   // bytes between consecutive keys
   const int64_t vkey_bytes = p.v_ss * 2;  // and between consecutive values
+  constexpr int kStepK = kWaves * T::kRowsPerLoad, kStepV = kWaves * TV::kRowsPerLoad;  // rows between loads
+  static_assert(kStepK % 8 == 0 && kStepV % 8 == 0, "swizzle parity of the tile loads");
   const int lrow = wave * T::kRowsPerLoad + lane / T::kChunks;
   const int lrow_v = wave * TV::kRowsPerLoad + lane / TV::kChunks;
-  const uint32_t k_lane_off = (uint32_t)(lrow * key_bytes) + (uint32_t)(((lane % T::kChunks) ^ T::kswz(lrow)) << 4);
-  const uint32_t v_lane_off =
-      (uint32_t)(lrow_v * vkey_bytes) + (uint32_t)(((lane % TV::kChunks) ^ TV::vswz(lrow_v)) << 4);
-  const int k_extent = Lkv > 0 ? (int)((Lkv - 1) * key_bytes) + T::kRowBytes : 0;
-  const int v_extent = Lkv > 0 ? (int)((Lkv - 1) * vkey_bytes) + TV::kRowBytes : 0;
+  // per-lane byte offset of the load whose first row is `row` (lrow or lrow_v plus a multiple of
+  // the step). A lane whose chunk lies past the problem's head dimension reads at an offset beyond
+  // every extent (the tile offsets stay below 2^31), so it writes zeros to its LDS chunk.
+  auto lane_off_k = [&](int row) -> uint32_t {
+    const int chunk = (lane % T::kChunks) ^ T::kswz(row);
+    return 8 * chunk >= p.D ? 0x80000000u : (uint32_t)(lrow * key_bytes) + (uint32_t)(chunk << 4);
+  };
+  auto lane_off_v = [&](int row) -> uint32_t {
+    const int chunk = (lane % TV::kChunks) ^ TV::vswz(row);
+    return 8 * chunk >= p.Dv ? 0x80000000u : (uint32_t)(lrow_v * vkey_bytes) + (uint32_t)(chunk << 4);
+  };
+  const uint32_t k_lane_off[2] = {lane_off_k(lrow), lane_off_k(lrow + kStepK)};
+  const uint32_t v_lane_off[2] = {lane_off_v(lrow_v), lane_off_v(lrow_v + kStepV)};
+  const int k_extent = Lkv > 0 ? (int)((Lkv - 1) * key_bytes) + 2 * p.D : 0;
+  const int v_extent = Lkv > 0 ? (int)((Lkv - 1) * vkey_bytes) + 2 * p.Dv : 0;
   const rsrc4 k_rsrc = make_rsrc(kp, (uint32_t)k_extent);
   const rsrc4 v_rsrc = make_rsrc(vp, (uint32_t)v_extent);
   // Load n of a K (V) tile whose first key sits soff bytes into the sequence: rows between two
   // loads of one wave are kWaves * kRowsPerLoad apart.
   auto issue_one_k = [&](int lds_off, uint32_t soff, int n) __attribute__((always_inline)) {
-    load_lds16(k_rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), k_lane_off,
-               soff + (uint32_t)(n * kWaves * T::kRowsPerLoad * key_bytes));
+    load_lds16(k_rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), k_lane_off[n & 1],
+               soff + (uint32_t)(n * kStepK * key_bytes));
   };
   auto issue_one_v = [&](int lds_off, uint32_t soff, int n) __attribute__((always_inline)) {
-    load_lds16(v_rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), v_lane_off,
-               soff + (uint32_t)(n * kWaves * TV::kRowsPerLoad * vkey_bytes));
+    load_lds16(v_rsrc, lds_address(smem + lds_off + (n * kWaves + wave) * 1024), v_lane_off[n & 1],
+               soff + (uint32_t)(n * kStepV * vkey_bytes));
   };
   // Byte offsets of tile i's first key in K and in V. The ring loads after the first ones are
   // spread over the MFMA slots of a pipeline step instead of being issued in a burst; a tile past
@@ -316,7 +339,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
     const int r = max(min(wrow0 + l32, row_end - 1), 0);
     const ev8* src = (const ev8*)(qp + (int64_t)r * p.q_ss);
 #pragma unroll
-    for (int t = 0; t < DT; t++) qreg[t] = src[2 * t + hl];
+    for (int t = 0; t < DT; t++) qreg[t] = 8 * (2 * t + hl) < p.D ? src[2 * t + hl] : ev8{};
   }
 
   // ---- per-lane LDS read offsets (fixed for the whole kernel) ----
@@ -713,6 +736,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
     for (int db = 0; db < DB; db++)
 #pragma unroll
       for (int g4 = 0; g4 < 4; g4++) {
+        if (db * 32 + 8 * g4 + 4 * hl >= p.Dv) continue;  // a padded column (p.Dv is a multiple of 8)
         E v4[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) v4[e] = (E)(pad ? 0.f : o[db][4 * g4 + e] * inv);
@@ -728,6 +752,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, 2 / NQB) void attn_fwd_k
 
 template <typename E, int D, int DV, int MODE, int NQB>
 hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
+  static_assert(NQB == 1 || D <= 128, "beyond D = 128 a workgroup holds one q-block");
   if (p.qblocks_per_tile != NQB) return hipErrorInvalidValue;
   const int grid = grid_for_items(p.total_items);
   hipLaunchKernelGGL((attn_fwd_kernel<E, D, DV, MODE, NQB>), dim3(grid), dim3(64 * kWavesPerBlock * NQB), 0, stream,
@@ -742,30 +767,43 @@ hipError_t launch_d(const FwdParams& p, int mode, hipStream_t stream) {
   if ((mode & kMask) != 0 && (reinterpret_cast<uintptr_t>(p.mask) & 15) == 0 && p.mask_ss % 16 == 0 &&
       p.mask_sb % 16 == 0 && p.mask_sh % 16 == 0 && p.mask_ss <= (1 << 20))
     mode |= kMaskTile;
+  constexpr int N2 = fwd_qblocks_per_tile(0, D);  // the q-block pairs of unmasked / masked / varlen launches
   switch (mode) {
-    case 0: return launch_t<E, D, DV, 0, 2>(p, stream);
+    case 0: return launch_t<E, D, DV, 0, N2>(p, stream);
     case kCausal: return launch_t<E, D, DV, kCausal, 1>(p, stream);
-    case kMask: return launch_t<E, D, DV, kMask, 2>(p, stream);
+    case kMask: return launch_t<E, D, DV, kMask, N2>(p, stream);
     case kCausal | kMask: return launch_t<E, D, DV, kCausal | kMask, 1>(p, stream);
-    case kMask | kMaskTile: return launch_t<E, D, DV, kMask | kMaskTile, 2>(p, stream);
+    case kMask | kMaskTile: return launch_t<E, D, DV, kMask | kMaskTile, N2>(p, stream);
     case kCausal | kMask | kMaskTile: return launch_t<E, D, DV, kCausal | kMask | kMaskTile, 1>(p, stream);
-    case kMask | kMaskTile | kMaskBits: return launch_t<E, D, DV, kMask | kMaskTile | kMaskBits, 2>(p, stream);
+    case kMask | kMaskTile | kMaskBits: return launch_t<E, D, DV, kMask | kMaskTile | kMaskBits, N2>(p, stream);
     case kCausal | kMask | kMaskTile | kMaskBits:
       return launch_t<E, D, DV, kCausal | kMask | kMaskTile | kMaskBits, 1>(p, stream);
     case kSparse: return launch_t<E, D, DV, kSparse, 1>(p, stream);
-    case kVarlen: return launch_t<E, D, DV, kVarlen, 2>(p, stream);
+    case kVarlen: return launch_t<E, D, DV, kVarlen, N2>(p, stream);
     case kVarlen | kCausal: return launch_t<E, D, DV, kVarlen | kCausal, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Every (D, DV) pair the library supports, for element type E.
+// The kernel built for the problem's head dimensions: D and Dv (multiples of 8, Dv <= D <= 256)
+// rounded up to 64, 128 or 256, with DV = 128 when D = 256. A value head dimension beyond 128
+// takes two launches of that kernel, one per column range [0, 128) and [128, Dv) of V and O (a
+// wave's O^T for all 256 columns does not fit its registers beside Q^T); both compute the same
+// scores in the same order, so the first one's softmax max and sum serve both.
 template <typename E>
 hipError_t launch_attn_fwd(const FwdParams& p, int mode, hipStream_t stream) {
-  if (p.D == 64 && p.Dv == 64) return launch_d<E, 64, 64>(p, mode, stream);
-  if (p.D == 128 && p.Dv == 128) return launch_d<E, 128, 128>(p, mode, stream);
-  if (p.D == 128 && p.Dv == 64) return launch_d<E, 128, 64>(p, mode, stream);
-  return hipErrorInvalidValue;
+  if (p.D < 8 || p.D > 256 || p.D % 8 != 0 || p.Dv < 8 || p.Dv > p.D || p.Dv % 8 != 0) return hipErrorInvalidValue;
+  if (p.D <= 64) return launch_d<E, 64, 64>(p, mode, stream);
+  if (p.D <= 128) return p.Dv <= 64 ? launch_d<E, 128, 64>(p, mode, stream) : launch_d<E, 128, 128>(p, mode, stream);
+  if (p.Dv <= 128) return launch_d<E, 256, 128>(p, mode, stream);
+  FwdParams lo = p, hi = p;
+  lo.Dv = 128;
+  hi.Dv = p.Dv - 128;
+  hi.v += 128;
+  hi.o += 128;
+  hi.m_out = hi.l_out = nullptr;
+  const hipError_t e = launch_d<E, 256, 128>(lo, mode, stream);
+  return e != hipSuccess ? e : launch_d<E, 256, 128>(hi, mode, stream);
 }
 
 }  // namespace

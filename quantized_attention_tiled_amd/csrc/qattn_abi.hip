@@ -35,13 +35,11 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   if (d->B < 1 || d->Nq < 1 || d->Nkv < 1 || d->Sq < 0 || d->Skv < 0)
     return fail(QATTN_INVALID_ARGUMENT, "bad sizes B=%d Nq=%d Nkv=%d Sq=%d Skv=%d", d->B, d->Nq, d->Nkv, d->Sq, d->Skv);
   if (d->Nq % d->Nkv != 0) return fail(QATTN_INVALID_ARGUMENT, "Nq=%d is not a multiple of Nkv=%d", d->Nq, d->Nkv);
-  if (d->D != 64 && d->D != 128) return fail(QATTN_UNSUPPORTED, "head dimension D=%d (supported: 64, 128)", d->D);
+  if (d->D < 1 || d->D > 768) return fail(QATTN_INVALID_ARGUMENT, "head dimension D=%d outside [1, 768]", d->D);
   if (d->dtype != QATTN_DTYPE_BF16 && d->dtype != QATTN_DTYPE_FP16)
     return fail(QATTN_INVALID_ARGUMENT, "dtype %d is not BF16 (0) or FP16 (1)", d->dtype);
   const int Dv = d->Dv == 0 ? d->D : d->Dv;
   if (Dv < 0 || Dv > d->D) return fail(QATTN_INVALID_ARGUMENT, "Dv=%d must lie in [1, D=%d] (0 means D)", d->Dv, d->D);
-  if (Dv != d->D && !(d->D == 128 && Dv == 64))
-    return fail(QATTN_UNSUPPORTED, "Dv=%d with D=%d (supported: Dv = D, or D = 128 with Dv = 64)", Dv, d->D);
   if (!(std::isfinite(d->scale) && d->scale > 0.f)) return fail(QATTN_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (d->sparse_mode != 0 && d->sparse_mode != 2 && d->sparse_mode != 3)
     return fail(QATTN_INVALID_ARGUMENT, "sparse_mode %d (supported: 0, 2, 3)", d->sparse_mode);
@@ -197,6 +195,22 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   return QATTN_OK;
 }
 
+// Head dimensions the 16-bit forward kernels take: D and Dv multiples of 8 (rows of 16-byte chunks)
+// with Dv <= D <= 256.
+int check_dims_16bit(const qattn::FwdParams& p) {
+  if (p.D % 8 != 0 || p.Dv % 8 != 0 || p.D > 256)
+    return fail(QATTN_UNSUPPORTED, "head dimensions D=%d, Dv=%d (supported: multiples of 8 with Dv <= D <= 256)", p.D,
+                p.Dv);
+  return QATTN_OK;
+}
+
+// Head dimensions the quantised forward and the backward take: D = Dv = 64 or 128.
+int check_dims_fixed(const qattn::FwdParams& p, const char* who) {
+  if ((p.D != 64 && p.D != 128) || p.Dv != p.D)
+    return fail(QATTN_UNSUPPORTED, "%s needs D = Dv = 64 or 128 (D=%d, Dv=%d)", who, p.D, p.Dv);
+  return QATTN_OK;
+}
+
 int check_ptrs(const void* const* ptrs, const char* const* names, int n) {
   for (int i = 0; i < n; i++) {
     if (!ptrs[i]) return fail(QATTN_INVALID_ARGUMENT, "%s is NULL", names[i]);
@@ -254,7 +268,7 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   qattn::FwdParams p{};
   int total_qb = 0;
   int rc = setup_common(desc, p, true, true, &total_qb);
-  if (rc) return rc;
+  if (rc || (rc = check_dims_16bit(p))) return rc;
   const void* ptrs[] = {q, k, v, o};
   const char* names[] = {"q", "k", "v", "o"};
   if ((rc = check_ptrs(ptrs, names, 4))) return rc;
@@ -272,7 +286,7 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   if (desc->atten_mask) mode |= qattn::kMask;
   if (desc->atten_mask && (desc->mask_kind & QATTN_MASK_BITS)) mode |= qattn::kMaskTile | qattn::kMaskBits;
   if (desc->layout == QATTN_LAYOUT_TND) mode |= qattn::kVarlen;
-  if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(mode)))) return rc;
+  if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(mode, qattn::fwd_kernel_dim(p.D))))) return rc;
   if (p.total_items == 0) return QATTN_OK;
   const hipError_t e = desc->dtype == QATTN_DTYPE_FP16 ? qattn::launch_attn_fwd_f16(p, mode, (hipStream_t)stream)
                                                        : qattn::launch_attn_fwd_bf16(p, mode, (hipStream_t)stream);
@@ -296,7 +310,7 @@ int attn_fwd_blocksparse(const qattn_desc* desc, const qattn_bf16* q, const qatt
   qattn::FwdParams p{};
   int total_qb = 0;
   int rc = setup_common(desc, p, false, false, &total_qb);
-  if (rc) return rc;
+  if (rc || (rc = check_dims_16bit(p))) return rc;
   const void* ptrs[] = {q, k, v, o};
   const char* names[] = {"q", "k", "v", "o"};
   if ((rc = check_ptrs(ptrs, names, 4))) return rc;
@@ -311,7 +325,7 @@ int attn_fwd_blocksparse(const qattn_desc* desc, const qattn_bf16* q, const qatt
   p.l_out = softmax_sum;
   p.counts = counts;
   p.idx = idx;
-  if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(qattn::kSparse)))) return rc;
+  if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(qattn::kSparse, qattn::fwd_kernel_dim(p.D))))) return rc;
   if (p.total_items == 0) return QATTN_OK;
   const hipError_t e = desc->dtype == QATTN_DTYPE_FP16
                            ? qattn::launch_attn_fwd_f16(p, qattn::kSparse, (hipStream_t)stream)
@@ -360,7 +374,7 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
   if (rc) return rc;
   if (desc->layout != QATTN_LAYOUT_BNSD) return fail(QATTN_UNSUPPORTED, "attn_fwd_qbsa needs the BNSD layout");
   if (desc->dtype != QATTN_DTYPE_BF16) return fail(QATTN_UNSUPPORTED, "attn_fwd_qbsa writes bf16 (dtype must be BF16)");
-  if (p.Dv != p.D) return fail(QATTN_UNSUPPORTED, "attn_fwd_qbsa needs Dv == D");
+  if ((rc = check_dims_fixed(p, "attn_fwd_qbsa"))) return rc;
   const void* ptrs[] = {q, k, v, o};
   const char* names[] = {"q", "k", "v", "o"};
   if ((rc = check_ptrs(ptrs, names, 4))) return rc;
@@ -439,7 +453,7 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   int total_qb = 0;
   int rc = setup_common(desc, f, true, true, &total_qb);
   if (rc) return rc;
-  if (f.Dv != f.D) return fail(QATTN_UNSUPPORTED, "attn_bwd needs Dv == D");
+  if ((rc = check_dims_fixed(f, "attn_bwd"))) return rc;
   if (desc->atten_mask && (desc->mask_kind & QATTN_MASK_BITS))
     return fail(QATTN_UNSUPPORTED, "attn_bwd takes byte masks (no QATTN_MASK_BITS)");
   if (!(desc->head_begin == -1 && desc->head_end == -1 && desc->qblock_begin == -1 && desc->qblock_end == -1))

@@ -81,14 +81,14 @@ def _fwd(q, d, qp=FAKE, kp=FAKE, vp=FAKE, op=FAKE, m=0, l=0):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=96), 2), (dict(D=0), 2), (dict(Nq=3, Nkv=2), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
+    (dict(D=100), 2), (dict(D=264), 2), (dict(D=0), 1), (dict(D=769), 1), (dict(Nq=3, Nkv=2), 1), (dict(scale=0.0), 1), (dict(scale=-1.0), 1),
     (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1), (dict(sparse_mode=1), 1), (dict(layout=4), 1),
     (dict(layout=-1), 1), (dict(sparse_mode=2, pre_tokens=5), 1), (dict(sparse_mode=3, next_tokens=0), 1), (dict(layout=3, B=64, Nq=64, Nkv=64, Skv=1 << 17, Sq=128), 2),
     (dict(layout=2, Nq=64, Nkv=64, Skv=1 << 20, Sq=128), 2),
     (dict(B=0), 1), (dict(Sq=-1), 1), (dict(Nkv=0), 1), (dict(head_begin=0, head_end=5), 1),
     (dict(head_begin=3, head_end=2), 1), (dict(qblock_begin=0, qblock_end=3), 1), (dict(qblock_begin=-2, qblock_end=1), 1),
     (dict(dtype=2), 1), (dict(dtype=-1), 1), (dict(Dv=-64), 1), (dict(Dv=256), 1), (dict(D=64, Dv=128), 1),
-    (dict(Dv=32), 2), (dict(Dv=96), 2), (dict(D=64, Dv=32), 2),
+    (dict(Dv=36), 2), (dict(Dv=100), 2), (dict(D=64, Dv=20), 2), (dict(D=96, Dv=4), 2),
 ])
 def test_invalid_descriptions(q, kw, status):
     assert _fwd(q, _desc(q, **kw)) == status
@@ -178,7 +178,7 @@ def test_backward_validation(q):
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(_desc(q, B=2, Nq=4, Sq=100))) == 8 * 2 * 4 * 100
     assert lib.attn_bwd_workspace_bytes(None) == 0
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(_desc(q, layout=1, B=3, Nq=4, Sq=100))) == 8 * 4 * 100  # TND
-    for kw in (dict(Dv=64), dict(head_begin=0, head_end=1), dict(qblock_begin=0, qblock_end=1)):
+    for kw in (dict(Dv=64), dict(D=96), dict(D=256), dict(head_begin=0, head_end=1), dict(qblock_begin=0, qblock_end=1)):
         assert bwd(_desc(q, **kw)) == 2, kw
     assert bwd(_desc(q), ws=None) == 1
     assert bwd(_desc(q), m=FAKE + 2) == 3
@@ -207,6 +207,9 @@ def test_blocksparse_and_qbsa_validation(q):
     assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 2
     d = _desc(q)
     assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None) == 1
+    for kw in (dict(D=100), dict(D=264), dict(Dv=36)):  # head dimensions as for attn_fwd
+        assert lib.attn_fwd_blocksparse(ctypes.byref(_desc(q, **kw)), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                        None) == 2, kw
     d = _desc(q, pre_tokens=10)  # the band is a dense-entry-point option
     assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 2
     assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, next_tokens=0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
@@ -216,7 +219,7 @@ def test_blocksparse_and_qbsa_validation(q):
     for lay in (2, 3):  # BSND and SBH are bf16-only layouts
         assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, layout=lay)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  FAKE, None, None, None) == 2
-    for kw in (dict(dtype=1), dict(Dv=64)):  # the quantised path writes bf16 and needs Dv = D
+    for kw in (dict(dtype=1), dict(Dv=64), dict(D=96), dict(D=256)):  # bf16 out, D = Dv = 64 or 128
         assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q, **kw)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  FAKE, None, None, None) == 2
     assert lib.attn_fwd_qbsa(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,

@@ -6,7 +6,9 @@ cross-compiles here; no GPU needed).
   meant an outlined lambda that demoted the kernel arguments and register arrays to memory.
 * Both attention kernels run two waves per SIMD (at most 256 VGPRs). A forward workgroup of one
   q-block (four waves) uses at most 80 KiB of LDS, so that two share a CU; one of two q-blocks
-  (eight waves, the CU's only workgroup) at most 160 KiB.
+  (eight waves, the CU's only workgroup) at most 160 KiB. The exception is the 16-bit forward
+  built for head dimension 256: one q-block, one wave per SIMD (its Q^T and O^T registers alone
+  take 192 VGPRs), the CU's only workgroup, its extra registers in AGPRs rather than scratch.
 """
 
 import functools
@@ -69,7 +71,7 @@ def test_fwd_instantiations(fwd):
         shapes.add((int(m.group(2)), int(m.group(3)), int(m.group(4))))
     # 18, 19: kMask (| kCausal) | kMaskTile; 50, 51: the same with kMaskBits (bit-packed masks)
     modes = [0, 1, 2, 3, 4, 8, 9, 18, 19, 50, 51]
-    assert shapes == {(d, dv, mode) for d, dv in [(64, 64), (128, 128), (128, 64)] for mode in modes}
+    assert shapes == {(d, dv, mode) for d, dv in [(64, 64), (128, 128), (128, 64), (256, 128)] for mode in modes}
     assert len({FWD_NAME.search(n).group(1) for n in fwd}) == 1
 
 
@@ -80,12 +82,18 @@ def test_fwd_kernels_use_no_scratch(fwd):
         if mode in MASK_MODES:
             continue
         assert res.get("ScratchSize", 0) == 0, (name, res)
-        assert res.get("VGPRs Spill", 0) == 0, (name, res)
+        if int(FWD_NAME.search(name).group(2)) <= 128:
+            assert res.get("VGPRs Spill", 0) == 0, (name, res)
 
 
 def test_fwd_two_waves_per_simd_and_lds(fwd):
     for name, res in fwd.items():
-        nqb = int(FWD_NAME.search(name).group(5))
+        m = FWD_NAME.search(name)
+        d, nqb = int(m.group(2)), int(m.group(5))
+        if d > 128:
+            assert nqb == 1 and res.get("Occupancy", 0) == 1, (name, res)
+            assert res.get("LDS Size", 0) <= 160 * 1024, (name, res)
+            continue
         assert res.get("Occupancy", 0) >= 2, (name, res)
         assert res.get("LDS Size", 0) <= (80 if nqb == 1 else 160) * 1024, (name, res)
 
