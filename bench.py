@@ -574,6 +574,9 @@ def main(argv=None):
     ap.add_argument("--dtype", choices=["bf16", "fp16"], default="bf16",
                     help="input / output type of the dense and block-sparse configs (fp16: the same values in float16)")
     ap.add_argument("--dv", type=int, default=None, help="value head dimension below D (dense / block-sparse configs)")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="query/key head dimension D in place of the config's (dense / block-sparse BNSD configs; "
+                         "scale 1/sqrt(D))")
     ap.add_argument("--mask", choices=["none", "bytes", "bits"], default="none",
                     help="dense BNSD configs: an SS atten_mask [S, S], one byte per key or bit-packed")
     ap.add_argument("--mask-density", type=float, default=0.0, help="fraction of masked keys of --mask (i.i.d.)")
@@ -606,15 +609,20 @@ def main(argv=None):
     qa.load()
     cfg = CONFIGS[a.config]
     kind = cfg["kind"]
-    log(f"generating {a.config} {'S=' + str(a.seq) if a.seq else ''}")
-    w = make_workload(a.config, S=a.seq) if a.seq else make_workload(a.config)
-    name = a.config if not a.seq else f"{a.config}_S{a.seq}"
-    if (a.dtype != "bf16" or a.dv) and kind == "qbsa":
-        log("--dtype / --dv apply to the dense and block-sparse configs only")
+    if (a.dtype != "bf16" or a.dv or a.head_dim) and kind == "qbsa":
+        log("--dtype / --dv / --head-dim apply to the dense and block-sparse configs only")
         return 2
+    if a.head_dim and cfg["layout"] != "BNSD":
+        log("--head-dim applies to the BNSD configs")
+        return 2
+    log(f"generating {a.config} {'S=' + str(a.seq) if a.seq else ''} {'D=' + str(a.head_dim) if a.head_dim else ''}")
+    w = make_workload(a.config, S=a.seq, D=a.head_dim)
+    name = a.config if not a.seq else f"{a.config}_S{a.seq}"
+    if a.head_dim:
+        name += f"_d{a.head_dim}"
     if a.dv:
-        if not 0 < a.dv < w.D:
-            log(f"--dv must lie below D = {w.D}")
+        if not 0 < a.dv <= w.D:
+            log(f"--dv must lie in [1, D = {w.D}]")
             return 2
         w.v = np.ascontiguousarray(w.v[..., :a.dv])  # the first Dv channels of the same draw
         name += f"_dv{a.dv}"
@@ -753,7 +761,8 @@ def main(argv=None):
         conf = {"workload": wl, "layout": "TND", "sequences": int(w.B), "lengths": np.diff(w.cu_seqlens_q).tolist(),
                 "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D, "sparse_mode": w.sparse_mode}
     else:
-        wl = f"{name}: {w.description}" + (f" (S overridden to {w.Sq})" if a.seq else "")
+        wl = f"{name}: {w.description}" + (f" (S overridden to {w.Sq})" if a.seq else "") + \
+            (f" (D overridden to {w.D})" if a.head_dim else "")
         conf = {"workload": wl, "layout": "BNSD", "B": w.B, "N": w.Nq, "Nkv": w.Nkv, "S": w.Sq, "D": w.D}
         if a.dv:
             conf["Dv"] = a.dv

@@ -128,7 +128,7 @@ typedef struct qattn_desc {
   int32_t Nkv;           /* key/value heads; Nq % Nkv == 0 */
   int32_t Sq;            /* query length; TND: total query tokens T */
   int32_t Skv;           /* key length; TND: total key tokens Tk */
-  int32_t D;             /* head dimension: 64 or 128 */
+  int32_t D;             /* query/key head dimension, in [1, 768] (see Dv for what each entry point takes) */
   float scale;           /* softmax scale, finite and > 0 */
   int32_t sparse_mode;   /* 0: none, explicit mask and/or band; 2: causal top-left; 3: causal bottom-right */
   const int32_t* cu_seqlens_q;  /* TND: host [B + 1] cumulative query lengths; else NULL */
@@ -145,8 +145,10 @@ typedef struct qattn_desc {
   int32_t next_tokens;          /* ... and this many after it; 2147483647 = no limit (both default) */
   int32_t dtype;                /* QATTN_DTYPE_BF16 (default) or _FP16: type of q, k, v and o; the
                                    quantised entry point takes BF16 only */
-  int32_t Dv;                   /* value / output head dimension; 0 means D. Supported: Dv = D, or
-                                   D = 128 with Dv = 64; the quantised entry point needs Dv = D */
+  int32_t Dv;                   /* value / output head dimension, 1 <= Dv <= D; 0 means D. The 16-bit
+                                   forward entry points take D and Dv multiples of 8 up to 256; the
+                                   quantised forward and the backward take D = Dv = 64 or 128; other
+                                   dimensions in [1, 768] return QATTN_UNSUPPORTED */
   const int32_t* actual_seq_lengths;    /* not TND: host [B] valid query rows per batch, or NULL (= Sq);
                                            the library reads exactly B entries */
   const int32_t* actual_seq_lengths_kv; /* not TND: host [B] valid keys per batch, or NULL (= Skv); B entries */
@@ -157,6 +159,12 @@ typedef struct qattn_desc {
  * 2-5 and 7; power-cap page, InsertComm/BlockAttn splitting).
  *   q, k, v: bf16 or fp16 (desc->dtype) in desc->layout; o: same type, shape of
  *   q with head dimension Dv. P is rounded to that type before P.V.
+ *   Head dimensions (section 4.1: D_q = D_k >= D_v; section 7: D up to 768): D
+ *   and Dv multiples of 8 with Dv <= D <= 256. Kernels exist for D = 64, 128
+ *   and 256; other sizes run on the next one up with zeros in place of the
+ *   missing columns (the scores are those of the problem's own D), and a Dv
+ *   above 128 runs as two launches over the column ranges [0, 128) and
+ *   [128, Dv) of V and O, which compute the same scores.
  *   softmax_max, softmax_sum: fp32 outputs (layouts above), each nullable.
  *   Causal modes and an explicit atten_mask may be combined (a pair is kept
  *   only when both keep it). atten_mask is not available with TND. A byte

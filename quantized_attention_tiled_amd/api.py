@@ -201,7 +201,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     BNSD: q [B, Nq, Sq, D], k/v [B, Nkv, Skv, D]; BSND: q [B, Sq, Nq, D], k/v [B, Skv, Nkv, D];
     BSH: q [B, Sq, Nq * D], SBH: q [Sq, B, Nq * D] (k/v alike, with head_num = Nq); m/l [B, Nq, Sq].
     TND:  q [T, Nq, D], k/v [Tk, Nkv, D] plus cumulative lengths; m/l [Nq, T].
-    v may have a smaller head dimension Dv (128 / 64); out then has Dv where q has D.
+    v may have a smaller head dimension Dv; out then has Dv where q has D. D and Dv: multiples of 8 with
+    Dv <= D <= 256.
     ``atten_mask`` (uint8 or bool, 1/True = masked) is SS, B1SS or BNSS (not with TND); an int32
     mask is bit-packed: ceil(Skv / 32) words per row, key j in bit j % 32 of word j // 32.
     With sparse_mode 0, ``pre_tokens`` / ``next_tokens`` keep key j for query i when
