@@ -73,7 +73,7 @@
  *     O = 0, m = -inf, l = 0.
  *   - q-head h reads kv-head h / (Nq / Nkv).
  *   - actual_seq_lengths / actual_seq_lengths_kv (EagleQBSA article, API call;
- *     BNSD, BSND and SBH; at most QATTN_MAX_SEQS batches): batch b is the
+ *     BNSD, BSND and SBH): batch b is the
  *     sequence of its first aq_b query rows and akv_b keys of the padded
  *     tensors; masks, causal anchors (Skv - Sq becomes akv_b - aq_b) and the
  *     band are counted inside it. Its rows aq_b .. Sq - 1 are written as rows
@@ -115,7 +115,10 @@ extern "C" {
  * with Skv replaced by ceil(Skv / 32) words; the mask must be 4-byte aligned. */
 #define QATTN_MASK_BITS 0x100
 
-#define QATTN_MAX_SEQS 256 /* TND: at most this many sequences per call */
+/* Sequences (TND) or padded batches (per-batch actual lengths) per kernel launch: their lengths
+ * travel in the kernel argument. A call with more runs as one launch per group of this many, with
+ * the same results; there is no limit per call. */
+#define QATTN_MAX_SEQS 256
 
 typedef uint16_t qattn_bf16; /* 16-bit element storage: bfloat16, or float16 per desc->dtype */
 

@@ -25,7 +25,7 @@ LAYOUT_SBH = 3
 MASK_SS, MASK_B1SS, MASK_BNSS = 0, 1, 2
 MASK_BITS = 0x100  # OR'ed into mask_kind: one bit per key
 DTYPE_BF16, DTYPE_FP16 = 0, 1
-MAX_SEQS = 256
+MAX_SEQS = 256  # QATTN_MAX_SEQS: sequences or padded batches per kernel launch (calls may hold more)
 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "MISALIGNED", 4: "HIP_ERROR"}
 

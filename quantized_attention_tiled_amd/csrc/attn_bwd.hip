@@ -635,9 +635,10 @@ void launch_bwd_mode(const BwdParams& pq, const BwdParams& pk, hipStream_t strea
 }
 
 template <typename E, int D>
-hipError_t launch_bwd_d(const BwdParams& p, int mode, hipStream_t stream) {
-  if (p.rows > 0)
+hipError_t launch_bwd_d(const BwdParams& p, int mode, int stages, hipStream_t stream) {
+  if ((stages & kBwdPrep) && p.rows > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((p.rows + 15) / 16)), dim3(256), 0, stream, p);
+  if (!(stages & kBwdProducts)) return hipGetLastError();
   BwdParams pq = p;
   pq.total_items = p.nseq > 0 ? p.Nq * p.q_tiles : p.B * p.Nq * ((p.Sq + kBlock - 1) / kBlock);
   BwdParams pk = p;
@@ -654,13 +655,13 @@ hipError_t launch_bwd_d(const BwdParams& p, int mode, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const BwdParams& p, int mode, hipStream_t stream) {
+hipError_t launch_attn_bwd(const BwdParams& p, int mode, int stages, hipStream_t stream) {
   if (p.f16) {
-    if (p.D == 64) return launch_bwd_d<_Float16, 64>(p, mode, stream);
-    if (p.D == 128) return launch_bwd_d<_Float16, 128>(p, mode, stream);
+    if (p.D == 64) return launch_bwd_d<_Float16, 64>(p, mode, stages, stream);
+    if (p.D == 128) return launch_bwd_d<_Float16, 128>(p, mode, stages, stream);
   } else {
-    if (p.D == 64) return launch_bwd_d<__bf16, 64>(p, mode, stream);
-    if (p.D == 128) return launch_bwd_d<__bf16, 128>(p, mode, stream);
+    if (p.D == 64) return launch_bwd_d<__bf16, 64>(p, mode, stages, stream);
+    if (p.D == 128) return launch_bwd_d<__bf16, 128>(p, mode, stages, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -221,8 +221,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
     // the whole kv range in its lifetime; with the start moving 1/64 of the range per row, the
     // workgroups running together walk through the same kv-blocks at the same time and share
     // them in the XCD's L2. The block-sparse result does not depend on the visit order, and the
-    // order is a function of (batch, head, q-block) alone, so subrange launches stay bit-identical.
-    const int64_t start_blk = (row * ((p.KB + 63) / 64)) % max(p.KB, 1);
+    // order is a function of (batch, head, q-block) alone, so subrange launches stay bit-identical
+    // (and so do launches over groups of batches, through the problem's batch index b0 + b).
+    const int64_t prow = ((int64_t)(p.b0 + b) * p.Nq + h) * p.QB + qblk;
+    const int64_t start_blk = (prow * ((p.KB + 63) / 64)) % max(p.KB, 1);
     kept0 = (int)((start_blk * nkept) / max(p.KB, 1));
   } else {
     ntiles = kv_end > t0 * kKT ? (kv_end - t0 * kKT + kKT - 1) / kKT : 0;

@@ -112,16 +112,12 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
     // per-batch actual lengths of a padded batch (each array optional)
     p.actual = d->actual_seq_lengths != nullptr || d->actual_seq_lengths_kv != nullptr;
     if (p.actual) {
-      if (d->B > qattn::kMaxSeqs)
-        return fail(QATTN_UNSUPPORTED, "actual sequence lengths for %d batches (max %d)", d->B, qattn::kMaxSeqs);
       for (int i = 0; i < d->B; i++) {
         const int lq = d->actual_seq_lengths ? d->actual_seq_lengths[i] : d->Sq;
         const int lk = d->actual_seq_lengths_kv ? d->actual_seq_lengths_kv[i] : d->Skv;
         if (lq < 0 || lq > d->Sq || lk < 0 || lk > d->Skv)
           return fail(QATTN_INVALID_ARGUMENT, "actual lengths (%d, %d) of batch %d outside [0, Sq=%d] x [0, Skv=%d]", lq,
                       lk, i, d->Sq, d->Skv);
-        p.cu_q[i] = lq;
-        p.cu_kv[i] = lk;
       }
     }
     if (d->atten_mask) {
@@ -134,7 +130,6 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   } else {
     if (d->actual_seq_lengths || d->actual_seq_lengths_kv)
       return fail(QATTN_INVALID_ARGUMENT, "TND takes cu_seqlens, not actual_seq_lengths");
-    if (d->B > qattn::kMaxSeqs) return fail(QATTN_UNSUPPORTED, "TND with %d sequences (max %d)", d->B, qattn::kMaxSeqs);
     if (!d->cu_seqlens_q || !d->cu_seqlens_kv) return fail(QATTN_INVALID_ARGUMENT, "TND needs cu_seqlens_q and cu_seqlens_kv");
     if (d->cu_seqlens_q[0] != 0 || d->cu_seqlens_kv[0] != 0)
       return fail(QATTN_INVALID_ARGUMENT, "cu_seqlens must start at 0");
@@ -148,10 +143,6 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
     if (d->cu_seqlens_q[d->B] != d->Sq || d->cu_seqlens_kv[d->B] != d->Skv)
       return fail(QATTN_INVALID_ARGUMENT, "cu_seqlens end (%d, %d) != (Sq, Skv) = (%d, %d)", d->cu_seqlens_q[d->B],
                   d->cu_seqlens_kv[d->B], d->Sq, d->Skv);
-    for (int i = 0; i <= d->B; i++) {
-      p.cu_q[i] = d->cu_seqlens_q[i];
-      p.cu_kv[i] = d->cu_seqlens_kv[i];
-    }
     p.nseq = d->B;
     p.q_sb = 0;
     p.q_sh = D;
@@ -255,6 +246,82 @@ int hip_status(hipError_t e, const char* what) {
   return QATTN_OK;
 }
 
+// Sequences (TND) or padded batches (per-batch actual lengths) of the problem, 0 for neither: their
+// lengths travel in the kernel argument, kMaxSeqs at a time.
+int length_groups_of(const qattn_desc* d, const qattn::FwdParams& full) {
+  return (d->layout == QATTN_LAYOUT_TND || full.actual) ? d->B : 0;
+}
+
+// The launch over sequences or batches [g0, g1) of the problem (g1 - g0 <= kMaxSeqs): TND keeps the
+// token offsets of the whole tensor (its cumulative lengths are the problem's, from g0 on) and
+// renumbers the q-block subrange from the group's first q-block, with *qb_pre the q-blocks of the
+// sequences before g0 (advanced past the group); padded batches offset every batch-indexed tensor
+// to batch g0. Returns false when the group has no q-block of the subrange.
+bool fill_group(const qattn_desc* d, const qattn::FwdParams& full, int g0, int g1, int* qb_pre,
+                qattn::FwdParams& p) {
+  p = full;
+  const int n = g1 - g0;
+  if (d->layout == QATTN_LAYOUT_TND) {
+    int nqb = 0;
+    for (int i = 0; i <= n; i++) {
+      p.cu_q[i] = d->cu_seqlens_q[g0 + i];
+      p.cu_kv[i] = d->cu_seqlens_kv[g0 + i];
+      if (i < n) nqb += (d->cu_seqlens_q[g0 + i + 1] - d->cu_seqlens_q[g0 + i] + qattn::kBlock - 1) / qattn::kBlock;
+    }
+    p.nseq = n;
+    p.qb0 = std::min(std::max(full.qb0 - *qb_pre, 0), nqb);
+    p.qb1 = std::min(std::max(full.qb1 - *qb_pre, 0), nqb);
+    *qb_pre += nqb;
+    return p.qb0 < p.qb1;
+  }
+  for (int i = 0; i < n; i++) {
+    p.cu_q[i] = d->actual_seq_lengths ? d->actual_seq_lengths[g0 + i] : d->Sq;
+    p.cu_kv[i] = d->actual_seq_lengths_kv ? d->actual_seq_lengths_kv[g0 + i] : d->Skv;
+  }
+  p.B = n;
+  p.b0 = g0;
+  if (g0 == 0) return true;
+  const int64_t b = g0;
+  auto at = [b](auto* ptr, int64_t per_batch) { return ptr ? ptr + b * per_batch : ptr; };
+  p.q = at(p.q, p.q_sb);
+  p.k = at(p.k, p.k_sb);
+  p.v = at(p.v, p.v_sb);
+  p.qi = at(p.qi, p.q_sb);
+  p.ki = at(p.ki, p.k_sb);
+  p.vf = at(p.vf, p.v_sb);
+  p.o = at(p.o, p.o_sb);
+  p.m_out = at(p.m_out, p.ml_sb);
+  p.l_out = at(p.l_out, p.ml_sb);
+  p.mask = at(p.mask, p.mask_sb);
+  p.counts = at(p.counts, (int64_t)p.Nq * p.QB);
+  p.idx = at(p.idx, (int64_t)p.Nq * p.QB * p.KB);
+  p.q_scale = at(p.q_scale, (int64_t)p.Nq * p.QB);
+  p.k_scale = at(p.k_scale, (int64_t)p.Nkv * p.KB);
+  p.v_scale = at(p.v_scale, (int64_t)p.Nkv * p.D);
+  return true;
+}
+
+// Every launch of a forward problem: one, or one per group of at most kMaxSeqs sequences or padded
+// batches, each with `per_tile` q-blocks per workgroup. `launch` starts the kernel(s) of one.
+template <typename Launch>
+int launch_forward(const qattn_desc* d, const qattn::FwdParams& full, int per_tile, Launch&& launch, const char* what) {
+  const int n = length_groups_of(d, full);
+  int qb_pre = 0;
+  for (int g0 = 0; g0 < std::max(n, 1); g0 += qattn::kMaxSeqs) {
+    qattn::FwdParams p;
+    if (n > 0) {
+      if (!fill_group(d, full, g0, std::min(n, g0 + qattn::kMaxSeqs), &qb_pre, p)) continue;
+    } else {
+      p = full;
+    }
+    int rc = finish_items(p, per_tile);
+    if (rc) return rc;
+    if (p.total_items == 0) continue;
+    if ((rc = hip_status(launch(p), what))) return rc;
+  }
+  return QATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -286,11 +353,14 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   if (desc->atten_mask) mode |= qattn::kMask;
   if (desc->atten_mask && (desc->mask_kind & QATTN_MASK_BITS)) mode |= qattn::kMaskTile | qattn::kMaskBits;
   if (desc->layout == QATTN_LAYOUT_TND) mode |= qattn::kVarlen;
-  if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(mode, qattn::fwd_kernel_dim(p.D))))) return rc;
-  if (p.total_items == 0) return QATTN_OK;
-  const hipError_t e = desc->dtype == QATTN_DTYPE_FP16 ? qattn::launch_attn_fwd_f16(p, mode, (hipStream_t)stream)
-                                                       : qattn::launch_attn_fwd_bf16(p, mode, (hipStream_t)stream);
-  return hip_status(e, "attn_fwd launch");
+  const bool f16 = desc->dtype == QATTN_DTYPE_FP16;
+  return launch_forward(
+      desc, p, qattn::fwd_qblocks_per_tile(mode, qattn::fwd_kernel_dim(p.D)),
+      [&](const qattn::FwdParams& g) {
+        return f16 ? qattn::launch_attn_fwd_f16(g, mode, (hipStream_t)stream)
+                   : qattn::launch_attn_fwd_bf16(g, mode, (hipStream_t)stream);
+      },
+      "attn_fwd launch");
 }
 
 int build_kv_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32_t* counts, int32_t* idx,
@@ -325,12 +395,14 @@ int attn_fwd_blocksparse(const qattn_desc* desc, const qattn_bf16* q, const qatt
   p.l_out = softmax_sum;
   p.counts = counts;
   p.idx = idx;
-  if ((rc = finish_items(p, qattn::fwd_qblocks_per_tile(qattn::kSparse, qattn::fwd_kernel_dim(p.D))))) return rc;
-  if (p.total_items == 0) return QATTN_OK;
-  const hipError_t e = desc->dtype == QATTN_DTYPE_FP16
-                           ? qattn::launch_attn_fwd_f16(p, qattn::kSparse, (hipStream_t)stream)
-                           : qattn::launch_attn_fwd_bf16(p, qattn::kSparse, (hipStream_t)stream);
-  return hip_status(e, "attn_fwd_blocksparse launch");
+  const bool f16 = desc->dtype == QATTN_DTYPE_FP16;
+  return launch_forward(
+      desc, p, qattn::fwd_qblocks_per_tile(qattn::kSparse, qattn::fwd_kernel_dim(p.D)),
+      [&](const qattn::FwdParams& g) {
+        return f16 ? qattn::launch_attn_fwd_f16(g, qattn::kSparse, (hipStream_t)stream)
+                   : qattn::launch_attn_fwd_bf16(g, qattn::kSparse, (hipStream_t)stream);
+      },
+      "attn_fwd_blocksparse launch");
 }
 
 int quantize_qk_perblock_int8(const qattn_bf16* x, int B, int N, int S, int D, int8_t* x_q, float* scale,
@@ -395,9 +467,9 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
   p.o = o;
   p.m_out = softmax_max;
   p.l_out = softmax_sum;
-  if ((rc = finish_items(p, 1))) return rc;
-  if (p.total_items == 0) return QATTN_OK;
-  return hip_status(qattn::launch_attn_qbsa(p, (hipStream_t)stream), "attn_fwd_qbsa launch");
+  return launch_forward(
+      desc, p, 1, [&](const qattn::FwdParams& g) { return qattn::launch_attn_qbsa(g, (hipStream_t)stream); },
+      "attn_fwd_qbsa launch");
 }
 
 size_t attn_bwd_workspace_bytes(const qattn_desc* desc) {
@@ -512,24 +584,14 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.rows = rows;
   p.nseq = tnd ? desc->B : 0;
   p.actual = f.actual;
-  if (f.actual)
-    for (int i = 0; i < desc->B; i++) {
-      p.cu_q[i] = f.cu_q[i];
-      p.cu_kv[i] = f.cu_kv[i];
-    }
-  int64_t items_q, items_k;
+  int64_t items_q = 0, items_k = 0;
   if (tnd) {
-    p.q_tiles = p.k_tiles = 0;
-    for (int i = 0; i <= desc->B; i++) {
-      p.cu_q[i] = f.cu_q[i];
-      p.cu_kv[i] = f.cu_kv[i];
-    }
     for (int i = 0; i < desc->B; i++) {
-      p.q_tiles += (f.cu_q[i + 1] - f.cu_q[i] + qattn::kBlock - 1) / qattn::kBlock;
-      p.k_tiles += (f.cu_kv[i + 1] - f.cu_kv[i] + qattn::kBlock - 1) / qattn::kBlock;
+      items_q += (desc->cu_seqlens_q[i + 1] - desc->cu_seqlens_q[i] + qattn::kBlock - 1) / qattn::kBlock;
+      items_k += (desc->cu_seqlens_kv[i + 1] - desc->cu_seqlens_kv[i] + qattn::kBlock - 1) / qattn::kBlock;
     }
-    items_q = (int64_t)desc->Nq * p.q_tiles;
-    items_k = (int64_t)desc->Nkv * p.k_tiles;
+    items_q *= desc->Nq;
+    items_k *= desc->Nkv;
   } else {
     items_q = (int64_t)desc->B * desc->Nq * ((desc->Sq + qattn::kBlock - 1) / qattn::kBlock);
     items_k = (int64_t)desc->B * desc->Nkv * ((desc->Skv + qattn::kBlock - 1) / qattn::kBlock);
@@ -550,7 +612,56 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
     p.lse2 = ws;
     p.delta = ws + rows;
   }
-  return hip_status(qattn::launch_attn_bwd(p, mode, (hipStream_t)stream), "attn_bwd launch");
+  // The per-row preparation runs once over every row. The dQ and dK/dV products run once per group
+  // of at most kMaxSeqs sequences (TND: their cumulative lengths, token offsets of the whole
+  // tensor) or padded batches (every batch-indexed tensor and the workspace offset to the group's
+  // first batch), the lengths travelling in the kernel argument.
+  if ((rc = hip_status(qattn::launch_attn_bwd(p, mode, qattn::kBwdPrep, (hipStream_t)stream), "attn_bwd launch")))
+    return rc;
+  const int n = (tnd || f.actual) ? desc->B : 0;
+  for (int g0 = 0; g0 < std::max(n, 1); g0 += qattn::kMaxSeqs) {
+    qattn::BwdParams g = p;
+    if (n > 0) {
+      const int m = std::min(n, g0 + qattn::kMaxSeqs) - g0;
+      if (tnd) {
+        g.nseq = m;
+        g.q_tiles = g.k_tiles = 0;
+        for (int i = 0; i <= m; i++) {
+          g.cu_q[i] = desc->cu_seqlens_q[g0 + i];
+          g.cu_kv[i] = desc->cu_seqlens_kv[g0 + i];
+        }
+        for (int i = 0; i < m; i++) {
+          g.q_tiles += (g.cu_q[i + 1] - g.cu_q[i] + qattn::kBlock - 1) / qattn::kBlock;
+          g.k_tiles += (g.cu_kv[i + 1] - g.cu_kv[i] + qattn::kBlock - 1) / qattn::kBlock;
+        }
+      } else {
+        g.B = m;
+        for (int i = 0; i < m; i++) {
+          g.cu_q[i] = desc->actual_seq_lengths ? desc->actual_seq_lengths[g0 + i] : desc->Sq;
+          g.cu_kv[i] = desc->actual_seq_lengths_kv ? desc->actual_seq_lengths_kv[g0 + i] : desc->Skv;
+        }
+        const int64_t b = g0;
+        auto at = [b](auto* ptr, int64_t per_batch) { return ptr ? ptr + b * per_batch : ptr; };
+        g.q = at(g.q, g.q_sb);
+        g.o = at(g.o, g.q_sb);
+        g.dout = at(g.dout, g.q_sb);
+        g.dq = at(g.dq, g.q_sb);
+        g.k = at(g.k, g.k_sb);
+        g.v = at(g.v, g.k_sb);
+        g.dk = at(g.dk, g.k_sb);
+        g.dv = at(g.dv, g.k_sb);
+        g.m_in = at(g.m_in, g.ml_sb);
+        g.l_in = at(g.l_in, g.ml_sb);
+        g.lse2 = at(g.lse2, g.ml_sb);
+        g.delta = at(g.delta, g.ml_sb);
+        g.mask = at(g.mask, g.mask_sb);
+      }
+    }
+    if ((rc = hip_status(qattn::launch_attn_bwd(g, mode, qattn::kBwdProducts, (hipStream_t)stream),
+                         "attn_bwd launch")))
+      return rc;
+  }
+  return QATTN_OK;
 }
 
 }  // namespace

@@ -63,8 +63,10 @@ struct FwdParams {
   int band_pre, band_next;  // causal-family key range i - band_pre <= j <= i + band_next (see the ABI)
   int nseq;
   int actual;  // BNSD family: cu_q / cu_kv hold per-batch actual lengths instead of Sq / Skv
-  // TND: cumulative query / key lengths (nseq + 1 entries); BNSD family with `actual`: the valid
-  // query / key length of each batch (B entries)
+  int b0;      // the problem's index of this launch's batch 0 (a launch over a group of batches)
+  // TND: cumulative query / key lengths (nseq + 1 entries, token offsets into the whole tensor);
+  // BNSD family with `actual`: the valid query / key length of each batch (B entries). A problem
+  // with more sequences or padded batches runs as one launch per group of at most kMaxSeqs.
   int cu_q[kMaxSeqs + 1];
   int cu_kv[kMaxSeqs + 1];
 };
@@ -105,7 +107,10 @@ struct BwdParams {
   int cu_kv[kMaxSeqs + 1];
 };
 
-hipError_t launch_attn_bwd(const BwdParams& p, int mode, hipStream_t stream);
+// Backward stages: the per-row preparation (over every row of the problem), and the dQ and dK/dV
+// products (over the sequences or batches in the parameters).
+enum BwdStages : int { kBwdPrep = 1, kBwdProducts = 2 };
+hipError_t launch_attn_bwd(const BwdParams& p, int mode, int stages, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, int mode, hipStream_t stream);
 hipError_t launch_attn_fwd_f16(const FwdParams& p, int mode, hipStream_t stream);
 // q-blocks per workgroup of the 16-bit kernels in `mode` (the host sets qblocks_per_tile to

@@ -124,8 +124,12 @@ def test_tnd_validation(q):
     assert tnd([0, 5, 3], [0, 5, 6]) == 1                # decreasing
     d = _desc(q, layout=1, B=2, Sq=10, Skv=10)           # missing arrays
     assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 1
-    big = list(range(0, 258))
-    assert tnd(big, big) == 2                            # 257 sequences > 256
+    # more sequences than one launch carries: still validated entry by entry (the call would run in
+    # groups of QATTN_MAX_SEQS; these fail validation before any launch)
+    big = list(range(0, 301))
+    bad = big[:280] + [big[279] - 1] + big[281:]
+    assert tnd(bad, big) == 1                            # decreasing at sequence 279
+    assert tnd(big, big[:290] + [big[289] - 2] + big[291:]) == 1   # kv lengths decreasing at sequence 289
     aq = (ctypes.c_int32 * 3)(0, 4, 9)
     d = _desc(q, layout=1, B=2, Sq=10, Skv=9)            # last entry != Sq
     d.cu_seqlens_q = ctypes.cast(aq, ctypes.POINTER(ctypes.c_int32))
@@ -157,10 +161,10 @@ def test_actual_lengths_validation(q):
     assert call([257, 3], None) == 1       # longer than Sq = 256
     assert call([3, -1], None) == 1
     assert call(None, [0, 257]) == 1
-    d = _desc(q, B=257, Nq=2, Nkv=2, Sq=4, Skv=4)
-    arr = (ctypes.c_int32 * 257)(*([1] * 257))
+    d = _desc(q, B=300, Nq=2, Nkv=2, Sq=4, Skv=4)   # more batches than one launch carries: every entry checked
+    arr = (ctypes.c_int32 * 300)(*([1] * 299 + [5]))
     d.actual_seq_lengths = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
-    assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 2   # > 256 batches
+    assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 1   # batch 299: 5 > Sq
     d = _desc(q, layout=1, B=1, Sq=5, Skv=5)  # TND takes cu_seqlens instead
     a5 = (ctypes.c_int32 * 2)(0, 5)
     d.cu_seqlens_q = ctypes.cast(a5, ctypes.POINTER(ctypes.c_int32))
