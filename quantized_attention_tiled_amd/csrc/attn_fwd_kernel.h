@@ -154,19 +154,44 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
   int64_t q_tok0 = 0, kv_tok0 = 0;
   if constexpr ((MODE & kVarlen) != 0) {
     h = p.h0 + item / p.total_tiles;
-    const int t = p.total_tiles - 1 - item % p.total_tiles;  // late (heavier) q-blocks first
-    int qbpre = 0, tpre = 0;
-    for (b = 0; b < p.nseq; b++) {
-      const int nqb = (p.cu_q[b + 1] - p.cu_q[b] + kBlock - 1) / kBlock;
-      const int lo = max(p.qb0, qbpre), hi = min(p.qb1, qbpre + nqb);
-      const int nt = (max(0, hi - lo) + NQB - 1) / NQB;
-      if (t < tpre + nt) {
-        qblk = lo - qbpre + (t - tpre) * NQB;
-        nsub = min(NQB, hi - qbpre - qblk);
-        break;
+    if (p.level_order) {
+      // Deepest tiles first, over all sequences of the head: level j holds tile j of every sequence
+      // with more than j tiles, and a later tile of a sequence sees at least as many keys (causal)
+      // or as many (no mask), so the heavy tiles start early and the light ones fill the end of
+      // the launch. With the sequences sorted by tile count (order), the levels between the
+      // counts of sorted sequences k + 1 and k hold k + 1 tiles each, in sorted order.
+      auto tiles_of = [&](int s) {
+        return ((p.cu_q[s + 1] - p.cu_q[s] + kBlock - 1) / kBlock + NQB - 1) / NQB;
+      };
+      const int t = item % p.total_tiles;
+      int base = 0, k = 0, ntk = 0;
+      for (; k < p.nseq; k++) {
+        ntk = tiles_of(p.order[k]);
+        const int ntn = k + 1 < p.nseq ? tiles_of(p.order[k + 1]) : 0;
+        const int band = (k + 1) * (ntk - ntn);
+        if (t < base + band) break;
+        base += band;
       }
-      tpre += nt;
-      qbpre += nqb;
+      k = min(k, p.nseq - 1);  // (t < total_tiles, the sum of all bands, always breaks first)
+      const int u = t - base;
+      b = p.order[u % (k + 1)];
+      qblk = (ntk - 1 - u / (k + 1)) * NQB;
+      nsub = min(NQB, (p.cu_q[b + 1] - p.cu_q[b] + kBlock - 1) / kBlock - qblk);
+    } else {
+      const int t = p.total_tiles - 1 - item % p.total_tiles;  // late (heavier) q-blocks first
+      int qbpre = 0, tpre = 0;
+      for (b = 0; b < p.nseq; b++) {
+        const int nqb = (p.cu_q[b + 1] - p.cu_q[b] + kBlock - 1) / kBlock;
+        const int lo = max(p.qb0, qbpre), hi = min(p.qb1, qbpre + nqb);
+        const int nt = (max(0, hi - lo) + NQB - 1) / NQB;
+        if (t < tpre + nt) {
+          qblk = lo - qbpre + (t - tpre) * NQB;
+          nsub = min(NQB, hi - qbpre - qblk);
+          break;
+        }
+        tpre += nt;
+        qbpre += nqb;
+      }
     }
     Lq = p.cu_q[b + 1] - p.cu_q[b];
     Lkv = p.cu_kv[b + 1] - p.cu_kv[b];

@@ -272,6 +272,17 @@ bool fill_group(const qattn_desc* d, const qattn::FwdParams& full, int g0, int g
     p.qb0 = std::min(std::max(full.qb0 - *qb_pre, 0), nqb);
     p.qb1 = std::min(std::max(full.qb1 - *qb_pre, 0), nqb);
     *qb_pre += nqb;
+    // a launch over all q-blocks of its sequences hands its tiles out deepest first: the sequences
+    // sorted by q-block count, descending (ties in sequence order)
+    p.level_order = 0;
+    if (p.qb0 == 0 && p.qb1 == nqb && nqb > 0) {
+      int seq[qattn::kMaxSeqs];
+      auto nqb_of = [&](int s) { return (p.cu_q[s + 1] - p.cu_q[s] + qattn::kBlock - 1) / qattn::kBlock; };
+      for (int s = 0; s < n; s++) seq[s] = s;
+      std::stable_sort(seq, seq + n, [&](int a, int b) { return nqb_of(a) > nqb_of(b); });
+      for (int s = 0; s < n; s++) p.order[s] = (uint8_t)seq[s];
+      p.level_order = 1;
+    }
     return p.qb0 < p.qb1;
   }
   for (int i = 0; i < n; i++) {

@@ -69,6 +69,10 @@ struct FwdParams {
   // with more sequences or padded batches runs as one launch per group of at most kMaxSeqs.
   int cu_q[kMaxSeqs + 1];
   int cu_kv[kMaxSeqs + 1];
+  // TND launches over every q-block: workgroup tiles are handed out deepest first (see the kernel),
+  // with the sequences in `order` by tile count, descending; 0 keeps the sequence order
+  int level_order;
+  uint8_t order[kMaxSeqs];
 };
 
 // Everything a backward launch needs (any layout, bf16 or fp16, D = Dv), passed by value.
