@@ -153,45 +153,73 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
   int b = 0, h, qblk = 0, nsub = NQB, Lq, Lkv;
   int64_t q_tok0 = 0, kv_tok0 = 0;
   if constexpr ((MODE & kVarlen) != 0) {
+    // The tile's sequence and q-blocks, found by the whole wave at once: lane i looks at sequence
+    // c0 + i of each pass of 64, an inclusive scan over the lanes counts the tiles up to it, and
+    // the first lane whose count passes t holds the tile (a serial walk over the sequences would
+    // chain a scalar load per sequence, about as long as the tiles of a short sequence).
     h = p.h0 + item / p.total_tiles;
+    auto nqb_of = [&](int s) { return (p.cu_q[s + 1] - p.cu_q[s] + kBlock - 1) / kBlock; };
     if (p.level_order) {
       // Deepest tiles first, over all sequences of the head: level j holds tile j of every sequence
       // with more than j tiles, and a later tile of a sequence sees at least as many keys (causal)
       // or as many (no mask), so the heavy tiles start early and the light ones fill the end of
       // the launch. With the sequences sorted by tile count (order), the levels between the
       // counts of sorted sequences k + 1 and k hold k + 1 tiles each, in sorted order.
-      auto tiles_of = [&](int s) {
-        return ((p.cu_q[s + 1] - p.cu_q[s] + kBlock - 1) / kBlock + NQB - 1) / NQB;
-      };
       const int t = item % p.total_tiles;
-      int base = 0, k = 0, ntk = 0;
-      for (; k < p.nseq; k++) {
-        ntk = tiles_of(p.order[k]);
-        const int ntn = k + 1 < p.nseq ? tiles_of(p.order[k + 1]) : 0;
-        const int band = (k + 1) * (ntk - ntn);
-        if (t < base + band) break;
-        base += band;
-      }
-      k = min(k, p.nseq - 1);  // (t < total_tiles, the sum of all bands, always breaks first)
-      const int u = t - base;
-      b = p.order[u % (k + 1)];
-      qblk = (ntk - 1 - u / (k + 1)) * NQB;
-      nsub = min(NQB, (p.cu_q[b + 1] - p.cu_q[b] + kBlock - 1) / kBlock - qblk);
-    } else {
-      const int t = p.total_tiles - 1 - item % p.total_tiles;  // late (heavier) q-blocks first
-      int qbpre = 0, tpre = 0;
-      for (b = 0; b < p.nseq; b++) {
-        const int nqb = (p.cu_q[b + 1] - p.cu_q[b] + kBlock - 1) / kBlock;
-        const int lo = max(p.qb0, qbpre), hi = min(p.qb1, qbpre + nqb);
-        const int nt = (max(0, hi - lo) + NQB - 1) / NQB;
-        if (t < tpre + nt) {
-          qblk = lo - qbpre + (t - tpre) * NQB;
-          nsub = min(NQB, hi - qbpre - qblk);
+      int kk = p.nseq - 1, base = 0, ntk_hit = 0, carry = 0;
+      for (int c0 = 0; c0 < p.nseq; c0 += 64) {
+        const int k = c0 + lane;
+        int ntk = 0, ntn = 0;
+        if (k < p.nseq) {
+          ntk = (nqb_of(p.order[k]) + NQB - 1) / NQB;
+          ntn = k + 1 < p.nseq ? (nqb_of(p.order[k + 1]) + NQB - 1) / NQB : 0;
+        }
+        const int band = (k + 1) * (ntk - ntn);  // 0 past the last sequence
+        const int incl = wave_incl_scan(band, lane) + carry;
+        const uint64_t hit = __ballot(incl > t);
+        if (hit != 0) {
+          const int L = __builtin_ctzll(hit);
+          kk = c0 + L;
+          base = __shfl(incl - band, L, 64);
+          ntk_hit = __shfl(ntk, L, 64);
           break;
         }
-        tpre += nt;
-        qbpre += nqb;
+        carry = __shfl(incl, 63, 64);
       }
+      kk = __builtin_amdgcn_readfirstlane(kk);
+      const int u = t - __builtin_amdgcn_readfirstlane(base);
+      b = p.order[u % (kk + 1)];
+      qblk = (__builtin_amdgcn_readfirstlane(ntk_hit) - 1 - u / (kk + 1)) * NQB;
+      nsub = min(NQB, nqb_of(b) - qblk);
+    } else {
+      // sequence by sequence, the last tile first (late q-blocks are the heavier ones); only the
+      // q-blocks of [qb0, qb1), numbered across the sequences, take part
+      const int t = p.total_tiles - 1 - item % p.total_tiles;
+      int qb_carry = 0, t_carry = 0, b_hit = 0, lo_hit = 0, hi_hit = 0, pre_hit = 0, tpre_hit = 0;
+      for (int c0 = 0; c0 < p.nseq; c0 += 64) {
+        const int s = c0 + lane;
+        const int nqb = s < p.nseq ? nqb_of(s) : 0;
+        const int qbpre = wave_incl_scan(nqb, lane) - nqb + qb_carry;  // q-blocks before sequence s
+        const int lo = max(p.qb0, qbpre), hi = min(p.qb1, qbpre + nqb);
+        const int nt = (max(0, hi - lo) + NQB - 1) / NQB;
+        const int incl = wave_incl_scan(nt, lane) + t_carry;
+        const uint64_t hit = __ballot(incl > t);
+        if (hit != 0) {
+          const int L = __builtin_ctzll(hit);
+          b_hit = c0 + L;
+          lo_hit = __shfl(lo, L, 64);
+          hi_hit = __shfl(hi, L, 64);
+          pre_hit = __shfl(qbpre, L, 64);
+          tpre_hit = __shfl(incl - nt, L, 64);
+          break;
+        }
+        qb_carry = __shfl(qbpre + nqb, 63, 64);
+        t_carry = __shfl(incl, 63, 64);
+      }
+      b = __builtin_amdgcn_readfirstlane(b_hit);
+      const int pre_b = __builtin_amdgcn_readfirstlane(pre_hit);
+      qblk = __builtin_amdgcn_readfirstlane(lo_hit) - pre_b + (t - __builtin_amdgcn_readfirstlane(tpre_hit)) * NQB;
+      nsub = min(NQB, __builtin_amdgcn_readfirstlane(hi_hit) - pre_b - qblk);
     }
     Lq = p.cu_q[b + 1] - p.cu_q[b];
     Lkv = p.cu_kv[b + 1] - p.cu_kv[b];

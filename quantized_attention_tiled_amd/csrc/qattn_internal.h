@@ -185,6 +185,16 @@ __device__ __forceinline__ void load_lds4(const rsrc4& rsrc, uint32_t lds, uint3
 }
 #pragma clang diagnostic pop
 
+// Inclusive prefix sum of x over the 64 lanes of a wave (lane = this lane's index).
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // Pipeline scaffolding shared by the attention kernels.
 // IC<V>: a compile-time int passed as a value, so one lambda serves every slot assignment.
 template <int V>
