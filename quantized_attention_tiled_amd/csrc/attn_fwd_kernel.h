@@ -779,29 +779,45 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
   }
 
   // ---- epilogue: O = acc / l, softmax max and sum ----
+  // A lane holds 4-column pieces of its row, so stores straight from the accumulators would touch
+  // 32 rows per instruction in 16-byte pieces. O goes through this wave's share of the LDS ring
+  // instead (free: every wave is past the last barrier, and no wave reads the ring again), as
+  // rows of 16-byte chunks XOR-swizzled by row, and leaves in wave-wide stores of whole rows:
+  // kRPI rows of kCPR chunks per 1 KiB store.
   const float lt = pair_sum(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   // softmax_sum relative to the true row max
   const float lout = (mtrue == kNegInf) ? 0.f : lt * __builtin_amdgcn_exp2f(mref - mtrue);
   const int q = wrow0 + l32;
-  if (q < row_limit) {
-    const bool pad = q >= row_end;  // (its lane computed a copy of the last valid row)
-    uint16_t* op = p.o + b * p.o_sb + h * p.o_sh + (q_tok0 + q) * p.o_ss;
+  const bool pad = q >= row_end;  // a row past the sequence (its lane computed a copy of the last valid row)
+  constexpr int kCPR = DV / 8;                    // 16-byte chunks per O row
+  constexpr int kRPI = 64 / kCPR;                 // rows per wave-wide store
+  constexpr int kSwz = (kCPR < 16 ? kCPR : 16) - 1;
+  static_assert(kWaves * 32 * DV * 2 <= 2 * T::kBytes + 2 * TV::kBytes, "O staging fits the ring");
+  uint8_t* const ostage = smem + wave * (32 * DV * 2);
 #pragma unroll
-    for (int db = 0; db < DB; db++)
+  for (int db = 0; db < DB; db++)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; g4++) {
-        if (db * 32 + 8 * g4 + 4 * hl >= p.Dv) continue;  // a padded column (p.Dv is a multiple of 8)
-        E v4[4];
+    for (int g4 = 0; g4 < 4; g4++) {
+      E v4[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) v4[e] = (E)(pad ? 0.f : o[db][4 * g4 + e] * inv);
-        *(uint2*)(op + db * 32 + 8 * g4 + 4 * hl) = __builtin_bit_cast(uint2, v4);
-      }
-    if (hl == 0) {
-      const int64_t mi = b * p.ml_sb + h * p.ml_sh + (q_tok0 + q) * p.ml_ss;
-      if (p.m_out) p.m_out[mi] = (mtrue == kNegInf || pad) ? kNegInf : mtrue * kLn2;
-      if (p.l_out) p.l_out[mi] = pad ? 0.f : lout;
+      for (int e = 0; e < 4; e++) v4[e] = (E)(pad ? 0.f : o[db][4 * g4 + e] * inv);
+      const int c = 4 * db + g4;  // columns 8 c + 4 hl .. + 3
+      *(uint2*)(ostage + l32 * (DV * 2) + ((c ^ (l32 & kSwz)) << 4) + 8 * hl) = __builtin_bit_cast(uint2, v4);
     }
+  // (a wave's LDS accesses complete in order, so its reads below see its writes above)
+  uint16_t* const obase = p.o + b * p.o_sb + h * p.o_sh + q_tok0 * p.o_ss;
+#pragma unroll
+  for (int i = 0; i < 32 / kRPI; i++) {
+    const int rr = i * kRPI + lane / kCPR, c = lane % kCPR;
+    const uint4 d = *(const uint4*)(ostage + rr * (DV * 2) + ((c ^ (rr & kSwz)) << 4));
+    const int r = wrow0 + rr;
+    if (r < row_limit && 8 * c < p.Dv) *(uint4*)(obase + (int64_t)r * p.o_ss + 8 * c) = d;
+  }
+  if (q < row_limit && hl == 0) {
+    const int64_t mi = b * p.ml_sb + h * p.ml_sh + (q_tok0 + q) * p.ml_ss;
+    if (p.m_out) p.m_out[mi] = (mtrue == kNegInf || pad) ? kNegInf : mtrue * kLn2;
+    if (p.l_out) p.l_out[mi] = pad ? 0.f : lout;
   }
 }
 
