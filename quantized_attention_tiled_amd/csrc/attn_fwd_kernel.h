@@ -135,10 +135,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
   static_assert(!kBits || kMT, "bit masks go through the mask tiles");
   constexpr int kMaskRow = kBits ? kKT / 8 : kKT;  // mask bytes per row and tile
   constexpr int kMaskSlot = kBlock * NQB * kMaskRow;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::kBytes + 2 * TV::kBytes + (kMT ? 2 * kMaskSlot : 0)];
+  // The second-pass flags, one int per wave: with one q-block per workgroup (two workgroups share
+  // a CU's LDS) at the start of V slot 1, which the epilogue's O staging does not reach and the
+  // second pass loads only after two barriers; with two, in words of their own after the tiles.
+  constexpr bool kFlagsInRing = NQB == 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::kBytes + 2 * TV::kBytes + (kMT ? 2 * kMaskSlot : 0) +
+                                                         (kFlagsInRing ? 0 : 4 * kWaves)];
   constexpr int kOffK = 0;
   constexpr int kOffV = 2 * T::kBytes;
   constexpr int kOffM = 2 * T::kBytes + 2 * TV::kBytes;
+  constexpr int kOffF = kFlagsInRing ? kOffV + TV::kBytes : kOffM + (kMT ? 2 * kMaskSlot : 0);
+  static_assert(!kFlagsInRing || kOffF >= kWaves * 32 * DV * 2, "the O staging leaves the flags alone");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -691,23 +698,45 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
       float mu;
       bool run;
       // prologue: K(0), K(1) and V(0) land; scores of half 0
+      // prologue: Q and K(0) (with its mask tile) land first. Outside block-sparse launches K(1)
+      // and V(0), first needed after the barrier of tile 0, load while the scores of half 0 and
+      // step 0 run (C2 -0.5%); a block-sparse tile comes from anywhere in the key range, whose
+      // load latency the first step cannot hide, so there all three tiles load at once.
+      // (Waiting for the older loads alone is no option: the compiler then waits for all loads
+      // before the first product, for Q's registers.)
+      constexpr bool kSplit = (MODE & kSparse) == 0;
       issue_k(0, 0);
-      if (ntiles > 1) issue_k(1, 1);
-      issue_v(0, 0);
-      if constexpr (kMT) {
-        issue_m(0, 0);
-        if (ntiles > 1) issue_m(1, 1);
+      if constexpr (kMT) issue_m(0, 0);
+      if constexpr (!kSplit) {
+        if (ntiles > 1) issue_k(1, 1);
+        issue_v(0, 0);
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
-      sy = f32x16{};
+      if constexpr (kSplit) {
+        if (ntiles > 1) issue_k(1, 1);
+        issue_v(0, 0);
+        if constexpr (kMT) {
+          if (ntiles > 1) issue_m(1, 1);
+        }
+      }
+      {
+        // all K operands of half 0 in flight at once, then the chain of score products
+        ev8 k0[DT];
 #pragma unroll
-      for (int t = 0; t < DT; t++) sy = Elem<E>::mfma(read_k(0, 0, t), qreg[t], sy);
+        for (int t = 0; t < DT; t++) k0[t] = read_k(0, 0, t);
+        __builtin_amdgcn_sched_barrier(0);
+        sy = f32x16{};
+#pragma unroll
+        for (int t = 0; t < DT; t++) sy = Elem<E>::mfma(k0[t], qreg[t], sy);
+      }
       mu = finish(0, sy, run);
       // step 0: softmax of half 0, scores of half 1 (K(0), second half), no P V yet
       step(IC<0>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{}, IC<0>{},
            sx, sy, pv, pu, carry, mu, run, 0u, 0u);
-      // barrier of tile 0: every wave is done with K(0); K(2) and V(1) are loaded during step 1
+      // barrier of tile 0: every wave is done with K(0), and K(1) and V(0) have landed everywhere;
+      // K(2) and V(1) are loaded during step 1
+      if constexpr (kSplit) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
       uint32_t dk = tile_soff(2, key_bytes), dv = tile_soff(1, vkey_bytes);
       dm = kMT ? tile_soff(2, 1) : 0u;
@@ -758,24 +787,26 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
       }
     }
 
-    // Does any wave of the workgroup need the second pass? The flags go through the first K slot:
-    // no load is in flight (each wave waits for its own) and after this barrier no wave reads it.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    int* const wave_flags = (int*)(smem + kOffK);
+    // Does any wave of the workgroup need the second pass? Each wave posts its flag in a word of
+    // its own (kOffF) and a barrier makes every flag visible and leaves every wave done with the
+    // tiles (no load is in flight: each wave waits for its own). Flags in V slot 1 are written only
+    // after a first barrier (another wave may still read that slot before it). Only the first
+    // pass writes the flags, and nothing else writes their words before every wave has read them.
+    int* const wave_flags = (int*)(smem + kOffF);
     if (pass == 0) {
       // the true max (c > 0 keeps the order) and whether it outgrew the reference by the slack
       mtrue = pair_max(lmax) * p.c;
       overflow = __any((mref != kNegInf) & (mtrue > mref + kRefSlack));
     }
-    if (lane == 0) wave_flags[wave] = pass == 0 ? (int)overflow : 0;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if constexpr (kFlagsInRing) __syncthreads();
+    if (pass == 0 && lane == 0) wave_flags[wave] = (int)overflow;
     __syncthreads();
+    if (pass == 1) break;
     int any_flag = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; w++) any_flag |= wave_flags[w];
-    const bool again = pass == 0 && any_flag != 0;
-    __syncthreads();
-    if (!again) break;
+    if (any_flag == 0) break;
   }
 
   // ---- epilogue: O = acc / l, softmax max and sum ----
