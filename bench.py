@@ -35,10 +35,10 @@ PEAK_BF16 = 2500.0   # TFLOP/s, MI355X published dense bf16 and fp16 MFMA
 PEAK_FP8 = 5000.0    # TFLOP/s (fp8) / TOP/s (int8), published dense
 HBM_PEAK = 8000.0    # GB/s
 KERNEL_SOURCES = {
-    "dense": ["attn_fwd_kernel.h", "attn_fwd_bf16.hip"],
-    "blocksparse": ["attn_fwd_kernel.h", "attn_fwd_bf16.hip", "quant.hip"],
-    "qbsa": ["attn_qbsa.hip", "quant.hip"],
-    "backward": ["attn_bwd.hip"],
+    "dense": ["attn_fwd_kernel.h", "attn_fwd_bf16.hip", "qattn_internal.h"],
+    "blocksparse": ["attn_fwd_kernel.h", "attn_fwd_bf16.hip", "quant.hip", "qattn_internal.h"],
+    "qbsa": ["attn_qbsa.hip", "quant.hip", "qattn_internal.h"],
+    "backward": ["attn_bwd.hip", "qattn_internal.h"],
 }
 
 
