@@ -590,11 +590,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
             issue_one_m((dma_ - 1) & 1, dm, j - LK - LV);  // the mask tile beside its K tile
         }
       }
-      if (k < DT) {
-        if (next_) sn = Elem<E>::mfma(op[k], qreg[k], k == 0 ? f32x16{} : sn);
-      } else {
-        if (prev_) o[(k - DT) % DB] = Elem<E>::mfma(op[k], pp[(k - DT) / DB], o[(k - DT) % DB]);
-      }
       if (cur_) {
         // The softmax of score pair q (registers 2 q, 2 q + 1) runs in three stages on consecutive
         // slots a(q), a(q) + 1, a(q) + 2: the two FMAs, the two exponentials, then the conversion
@@ -633,6 +628,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
         rm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(k == 0 ? lmax : rm, sc[2 * k]), sc[2 * k + 1]);
         pin_use(rm);
         if (k == 7) lmax = run ? rm : lmax;
+      }
+      // the slot's product comes after its vector work, which then issues while the product's
+      // LDS operand, read kPF slots ahead, may still be arriving (C2 -0.5%, same outputs)
+      if (k < DT) {
+        if (next_) sn = Elem<E>::mfma(op[k], qreg[k], k == 0 ? f32x16{} : sn);
+      } else {
+        if (prev_) o[(k - DT) % DB] = Elem<E>::mfma(op[k], pp[(k - DT) / DB], o[(k - DT) % DB]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
