@@ -577,19 +577,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
       } else if (pout_ && k + kPF - M < 2) {
         carry[k + kPF - M] = read_k(ks2_, kh2_, k + kPF - M);
       }
-      if constexpr (dma_ != 0) {
-        constexpr int LK = T::kLoadsPerWave, LV = TV::kLoadsPerWave, LA = LK + LV + kLoadsM;
-#pragma unroll
-        for (int j = 0; j < LA; j++) {
-          if ((j * M) / LA != k) continue;
-          if (j < LK)
-            issue_one_k(kOffK + ((dma_ - 1) & 1) * T::kBytes, dk, j);
-          else if (j < LK + LV)
-            issue_one_v(kOffV + ((dma_ - 1) >> 1) * TV::kBytes, dv, j - LK);
-          else
-            issue_one_m((dma_ - 1) & 1, dm, j - LK - LV);  // the mask tile beside its K tile
-        }
-      }
       if (cur_) {
         // The softmax of score pair q (registers 2 q, 2 q + 1) runs in three stages on consecutive
         // slots a(q), a(q) + 1, a(q) + 2: the two FMAs, the two exponentials, then the conversion
@@ -629,8 +616,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
         pin_use(rm);
         if (k == 7) lmax = run ? rm : lmax;
       }
-      // the slot's product comes after its vector work, which then issues while the product's
-      // LDS operand, read kPF slots ahead, may still be arriving (C2 -0.5%, same outputs)
+      // the slot's tile loads and product come after its vector work, which then issues while the
+      // product's LDS operand, read kPF slots ahead, may still be arriving (C2 -1%, same outputs)
+      if constexpr (dma_ != 0) {
+        constexpr int LK = T::kLoadsPerWave, LV = TV::kLoadsPerWave, LA = LK + LV + kLoadsM;
+#pragma unroll
+        for (int j = 0; j < LA; j++) {
+          if ((j * M) / LA != k) continue;
+          if (j < LK)
+            issue_one_k(kOffK + ((dma_ - 1) & 1) * T::kBytes, dk, j);
+          else if (j < LK + LV)
+            issue_one_v(kOffV + ((dma_ - 1) >> 1) * TV::kBytes, dv, j - LK);
+          else
+            issue_one_m((dma_ - 1) & 1, dm, j - LK - LV);  // the mask tile beside its K tile
+        }
+      }
       if (k < DT) {
         if (next_) sn = Elem<E>::mfma(op[k], qreg[k], k == 0 ? f32x16{} : sn);
       } else {
