@@ -283,8 +283,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
     // them in the XCD's L2. The block-sparse result does not depend on the visit order, and the
     // order is a function of (batch, head, q-block) alone, so subrange launches stay bit-identical
     // (and so do launches over groups of batches, through the problem's batch index b0 + b).
+    // Rows that keep more than 9/10 of their blocks walk from kv-block 0 instead: such rows take
+    // about equally long, so the workgroups of one generation start together, and rotated starts
+    // would then spread them over the whole kv range (full density, S = 64K: 83.3 -> 76.6 ms; at
+    // 0.9 kept both orders take the same time, below it the rotation wins).
     const int64_t prow = ((int64_t)(p.b0 + b) * p.Nq + h) * p.QB + qblk;
-    const int64_t start_blk = (prow * ((p.KB + 63) / 64)) % max(p.KB, 1);
+    const int64_t start_blk = 10 * nkept > 9 * p.KB ? 0 : (prow * ((p.KB + 63) / 64)) % max(p.KB, 1);
     kept0 = (int)((start_blk * nkept) / max(p.KB, 1));
   } else {
     ntiles = kv_end > t0 * kKT ? (kv_end - t0 * kKT + kKT - 1) / kKT : 0;
