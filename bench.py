@@ -7,7 +7,8 @@ One step is one pass of the hot path over resident synthetic inputs:
   * block-sparse: build the kept list, then attn_fwd_blocksparse;
   * quantised: quantise Q, K (INT8 per block) and V (FP8 per channel), build
     the kept list, then attn_fwd_qbsa.
-W untimed steps, then exactly K timed steps between two device
+Untimed steps first (a settling phase of --settle-s seconds, then the W
+warm-up steps), then exactly K timed steps between two device
 synchronisations; HIP events on the launch stream give the per-step times.
 Prints one JSON line. The default workload is the dense B=1 N=40 S=8192 D=128
 operator shape, on which the headline metric is quoted.
@@ -556,6 +557,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="untimed whole steps run before the warm-up until this many seconds (and at least 16 "
+                         "steps) have passed: the first launches of a process run slow while code loads and the "
+                         "clock and power settle")
     ap.add_argument("--config", default="c2_dense_8k")
     ap.add_argument("--seq", type=int, default=None, help="override S (dense BNSD configs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -714,7 +719,17 @@ def main(argv=None):
                 kb.record(stream)
         dtype, peak = "int8/fp8", PEAK_FP8
 
-    log(f"warmup {a.warmup}")
+    # Settling: the first launches of a process run slower (code loading, then about a dozen launches
+    # while the clock and power settle), so whole steps run untimed for a fixed time before the W
+    # warm-up steps; the timed region is unchanged.
+    settle_n, settle_t0 = 0, time.perf_counter()
+    while settle_n < 16 or time.perf_counter() - settle_t0 < a.settle_s:
+        for _ in range(8):
+            step()
+        settle_n += 8
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - settle_t0
+    log(f"settled after {settle_n} steps ({settle_s:.2f} s); warmup {a.warmup}")
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -722,7 +737,10 @@ def main(argv=None):
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
     log(f"timing {a.steps} steps")
     torch.cuda.synchronize()
-    sampler = None if a.no_smi else ClockSampler().start()
+    # amd-smi readings lag the load by up to a second: a timed region shorter than about two seconds
+    # gets none, and the sampling thread's process launches would only disturb the host's launches
+    expect_s = a.steps * settle_s / max(settle_n, 1)
+    sampler = None if a.no_smi or expect_s < 2.0 else ClockSampler().start()
     wall0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(a.steps):
@@ -784,7 +802,8 @@ def main(argv=None):
                    "min_ms": round(float(per.min()), 4), "cv": round(float(per.std() / per.mean()), 4),
                    "algorithmic_bytes": alg_bytes, "algorithmic_gbps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
                    "wall_s_timed": round(wall, 3), "kernel_source_sha": source_hash(kind),
-                   "clock_during_timed": clock},
+                   "clock_during_timed": clock,
+                   "settle": {"untimed_steps": settle_n, "seconds": round(settle_s, 3)}},
     }
     print(json.dumps(line), flush=True)
     return 0
