@@ -487,9 +487,10 @@ def power_study(S, gaps_ms, chunk_counts=(10,), seconds=3.0):
 def backward_bench(a):
     """The attention backward (dQ, dK, dV) on a dense BNSD config: the forward runs once, untimed,
     then W warm-up and K timed backward calls (all three kernels) between HIP events. Flops: the
-    usual 10 D per (q, k) pair (five products: S, dP, dV, dK, dQ; 2.5 times the forward's 4 D), and
-    the executed 14 D of these kernels (S and dP are formed once for dQ and once for dK / dV);
-    causal counts the pairs at or below the diagonal. Prints one JSON line."""
+    usual 6 D + 4 Dv per (q, k) pair (five products: S and dK, dQ over D, dP and dV over Dv; 10 D
+    when Dv = D, 2.5 times the forward's 4 D), and the executed 8 D + 6 Dv of these kernels (S and
+    dP are formed once for dQ and once for dK / dV); causal counts the pairs at or below the
+    diagonal. --head-dim and --dv set D and Dv. Prints one JSON line."""
     import torch
     import quantized_attention_tiled_amd as qa
     from workloads import CONFIGS, make_workload
@@ -497,7 +498,12 @@ def backward_bench(a):
     if CONFIGS[a.config]["kind"] != "dense":
         log("--backward takes a dense config (BNSD or TND)")
         return 2
-    w = make_workload(a.config, S=a.seq) if a.seq else make_workload(a.config)
+    w = make_workload(a.config, S=a.seq, D=a.head_dim)
+    Dv = a.dv or w.D
+    if not 0 < Dv <= w.D:
+        log(f"--dv must lie in [1, D = {w.D}]")
+        return 2
+    w.v = np.ascontiguousarray(w.v[..., :Dv])  # the first Dv channels of the same draw
     dev = torch.device("cuda:0")
 
     def up(bits):
@@ -508,7 +514,7 @@ def backward_bench(a):
 
     q, k, v = up(w.q), up(w.k), up(w.v)
     gen = torch.Generator(device=dev).manual_seed(77)
-    do = torch.randn(q.shape, generator=gen, device=dev).to(q.dtype)
+    do = torch.randn(q.shape[:-1] + (Dv,), generator=gen, device=dev).to(q.dtype)
     tnd = w.layout == "TND"
     mode = w.sparse_mode if tnd else a.bwd_mode
     kw = dict(scale=w.scale, sparse_mode=mode)
@@ -538,13 +544,13 @@ def backward_bench(a):
         pairs = w.Nq * int(sum(int(L) * (int(L) + 1) // 2 if mode in (2, 3) else int(L) * int(L) for L in lens))
     else:
         pairs = w.B * w.Nq * (w.Sq * (w.Sq + 1) // 2 if mode == 2 else w.Sq * w.Skv)
-    std, exe = 10 * w.D * pairs, 14 * w.D * pairs
-    line = {"metric": "attention bwd TFLOP/s (dQ, dK, dV; 10 D flops per pair), % bf16 MFMA peak",
+    std, exe = (6 * w.D + 4 * Dv) * pairs, (8 * w.D + 6 * Dv) * pairs
+    line = {"metric": "attention bwd TFLOP/s (dQ, dK, dV; 6 D + 4 Dv flops per pair), % bf16 MFMA peak",
             "value": round(std / ms / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
             "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": a.dtype,
             "data": "synthetic (seeded forward inputs; dO N(0,1) drawn on the GPU)",
-            "config": {"workload": f"{a.config}: {w.description}" + (f" (S {w.Sq})" if a.seq else ""),
-                       "sparse_mode": mode},
+            "config": {"workload": f"{a.config}: {w.description}" + (f" (S {w.Sq})" if a.seq else "") +
+                       (f" (D {w.D})" if a.head_dim else ""), "D": w.D, "Dv": Dv, "sparse_mode": mode},
             "detail": {"executed_tflops": round(exe / ms / 1e9, 2), "pct_mfma_peak_executed":
                        round(100 * exe / ms / 1e9 / PEAK_BF16, 2), "median_ms": round(float(np.median(per)), 4),
                        "cv": round(float(per.std() / per.mean()), 4), "kernel_source_sha": source_hash("backward")}}

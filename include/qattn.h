@@ -256,13 +256,15 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
  *   dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
  *   dQ = scale dS K, dK = scale dS^T Q,
  * with P recomputed from softmax_max / softmax_sum, never stored.
- *   desc: any layout (BNSD, BSND/BSH, SBH, TND), bf16 or fp16, Dv = D; the
- *   masks of attn_fwd (sparse_mode 0, 2 or 3, the band, atten_mask), GQA,
- *   actual lengths (padded rows and keys get zero gradients); no subrange
- *   (else QATTN_UNSUPPORTED).
+ *   desc: any layout (BNSD, BSND/BSH, SBH, TND), bf16 or fp16; head
+ *   dimensions D and Dv multiples of 8 with Dv <= D <= 128 (else
+ *   QATTN_UNSUPPORTED); the masks of attn_fwd (sparse_mode 0, 2 or 3, the
+ *   band, byte atten_mask), GQA, actual lengths (padded rows and keys get zero
+ *   gradients); no subrange (else QATTN_UNSUPPORTED).
  *   q, k, v, o, dout: inputs of desc->dtype (o and the softmax outputs from
- *   attn_fwd on the same description); dq, dk, dv: outputs of that type shaped
- *   like q, k, v (a kv-head's gradients sum over the q-heads that read it).
+ *   attn_fwd on the same description; v, o and dout have Dv columns per head);
+ *   dq, dk, dv: outputs of that type shaped like q, k, v (a kv-head's
+ *   gradients sum over the q-heads that read it).
  *   P and dS are rounded to that type before their products.
  *   workspace: device fp32 scratch of attn_bwd_workspace_bytes(desc) bytes
  *   (8 B Nq Sq; TND: 8 Nq T), owned by the caller; its contents on entry do

@@ -425,8 +425,10 @@ def _bwd_args(q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, 
     else:
         lay, B, Nq, Sq, Nkv, Skv, D = _dims(layout, q, k, head_num)
         ml_shape = (B, Nq, Sq)
-    if v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("v must match k, out and dout must match q")
+    Dv = _value_dim(layout, k, v, Nkv)
+    o_shape = q.shape[:-1] + (q.shape[-1] // D * Dv,)
+    if out.shape != o_shape or dout.shape != o_shape:
+        raise ValueError(f"out and dout must be {tuple(o_shape)} (q's shape with v's head dimension)")
     if tuple(softmax_max.shape) != ml_shape or tuple(softmax_sum.shape) != ml_shape:
         raise ValueError(f"softmax_max / softmax_sum must be {ml_shape}")
     kind = MASK_SS
@@ -448,7 +450,7 @@ def _bwd_args(q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, 
             _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv"))
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, dtype=dtype, atten_mask=atten_mask, mask_kind=kind,
-                     pre_tokens=pre_tokens, next_tokens=next_tokens, actual_q=keep[2], actual_kv=keep[3])
+                     pre_tokens=pre_tokens, next_tokens=next_tokens, actual_q=keep[2], actual_kv=keep[3], Dv=Dv)
     return desc, keep, atten_mask, dq, dk, dv
 
 
@@ -462,8 +464,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
              dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of attn_fwd on bfloat16 or float16 q, k, v (one type) in any layout
-    attn_fwd takes (shapes as there, D = Dv), given the forward's out and softmax_max / softmax_sum
-    and the output gradient dout (shaped like out). The masks are the forward's: sparse_mode,
+    attn_fwd takes (shapes as there; D and Dv multiples of 8 with Dv <= D <= 128), given the
+    forward's out and softmax_max / softmax_sum and the output gradient dout (shaped like out). The masks are the forward's: sparse_mode,
     ``atten_mask`` (not with TND), the ``pre_tokens`` / ``next_tokens`` band and per-batch
     ``actual_seq_lengths`` / ``actual_seq_lengths_kv`` (padded rows and keys get zero gradients).
     ``workspace``: optional fp32 device tensor of at least attn_bwd_workspace_bytes / 4 elements

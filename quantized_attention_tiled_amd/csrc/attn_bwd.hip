@@ -9,7 +9,11 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 // The forward's options carry over: every layout (batch/head/token strides; TND as per-sequence
 // work items), GQA, the causal modes and the sparse_mode 0 band (one key-range mask with tile
-// skipping), boolean masks (read per element) and per-batch actual lengths.
+// skipping), boolean masks (read per element) and per-batch actual lengths. Head dimensions: D of
+// q / k and Dv of v / o, multiples of 8 with Dv <= D <= 128, run on the kernels built for width
+// 64 or 128 (the next size up): every column past D (q, k) or Dv (v, o, dO) reads as zero, in
+// registers and in the LDS tiles, so the products see exact zeros there, and the gradients are
+// written up to D (dQ, dK) and Dv (dV).
 //
 // Three kernels, all on v_mfma_f32_32x32x16_{bf16,f16} where the work is a contraction:
 //   * bwd_prep_kernel: per query row, lse2 = log2(sum) + max log2(e) (+inf for a row with no
@@ -85,16 +89,19 @@ struct BTile {
 // wave w's load n fills the 1 KiB slab 4 n + w of a tile, i.e. rows (4 n + w) R .. + R - 1 with
 // R = 1024 / row bytes, lane l taking physical chunk l % chunks of row l / chunks, so the global
 // chunk it reads is the swizzled one. The swizzle repeats within 4 R rows, so one per-lane offset
-// serves every load; rows past the buffer's extent read as zeros.
+// serves every load; rows past the buffer's extent read as zeros, and so does a lane whose chunk
+// lies past the tensor's `width` columns (its offset is beyond every extent: the tile offsets stay
+// below 2^31).
 template <int D>
 struct TileLoad {
   using T = BTile<D>;
   static constexpr int kRowsPerLoad = 1024 / T::kRowBytes;
   static constexpr int kLoads = kTileRows / (4 * kRowsPerLoad);  // loads per wave per tile
   uint32_t lane_off, stride;  // stride: bytes between consecutive rows in HBM
-  __device__ TileLoad(int wave, int lane, uint32_t row_stride) : stride(row_stride) {
+  __device__ TileLoad(int wave, int lane, uint32_t row_stride, int width) : stride(row_stride) {
     const int row = wave * kRowsPerLoad + lane / T::kChunks;
-    lane_off = (uint32_t)row * stride + (uint32_t)(((lane % T::kChunks) ^ T::swz(row)) << 4);
+    const int chunk = (lane % T::kChunks) ^ T::swz(row);
+    lane_off = 8 * chunk >= width ? 0x80000000u : (uint32_t)row * stride + (uint32_t)(chunk << 4);
   }
   // tile whose first row is `row0` of the buffer, into LDS at `lds`
   __device__ void issue(const rsrc4& rsrc, uint8_t* lds, int row0, int wave) const {
@@ -149,13 +156,16 @@ __device__ __forceinline__ u32x4 read_row(const uint8_t* lds, int row, int t, in
 __device__ __forceinline__ int c_row(int r, int hl) { return 8 * (r >> 2) + 4 * hl + (r & 3); }
 
 // Store the 32 x D^T accumulators of one wave (lane = output row l32, registers = columns) as E
-// rows of a row-major [rows, D] matrix, times `mul`.
+// rows of a row-major matrix, times `mul`: the columns below `width` (a multiple of 8, so each
+// 4-column piece lies wholly inside or outside).
 template <typename E, int D>
-__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul, int hl) {
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul, int hl,
+                                           int width) {
 #pragma unroll
   for (int db = 0; db < D / 32; db++)
 #pragma unroll
     for (int g4 = 0; g4 < 4; g4++) {
+      if (db * 32 + 8 * g4 + 4 * hl >= width) continue;
       E v4[4];
 #pragma unroll
       for (int e = 0; e < 4; e++) v4[e] = (E)(acc[db][4 * g4 + e] * mul);
@@ -174,15 +184,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
     // row = (b Nq + h) Sq + i for BNSD, h T + t for TND (one "batch" of T tokens)
     const int64_t i = row % p.Sq, bh = row / p.Sq;
     const int64_t h = bh % p.Nq, b = bh / p.Nq;
-    const int64_t e0 = b * p.q_sb + h * p.q_sh + i * p.q_ss;
+    const int64_t e0 = b * p.o_sb + h * p.o_sh + i * p.o_ss;
     const uint16_t* o = p.o + e0;
     const uint16_t* g = p.dout + e0;
     constexpr int NE = D / 16;  // 8 (D = 128) or 4 (D = 64) elements per lane
     typedef E ev __attribute__((ext_vector_type(NE)));
-    const ev ov = *(const ev*)(o + sub * NE);
-    const ev gv = *(const ev*)(g + sub * NE);
+    // Dv is a multiple of 8, so a lane's NE elements lie wholly inside or past it
+    if (sub * NE < p.Dv) {
+      const ev ov = *(const ev*)(o + sub * NE);
+      const ev gv = *(const ev*)(g + sub * NE);
 #pragma unroll
-    for (int e = 0; e < NE; e++) acc += (float)ov[e] * (float)gv[e];
+      for (int e = 0; e < NE; e++) acc += (float)ov[e] * (float)gv[e];
+    }
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
@@ -243,20 +256,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   if constexpr (MASKED) mrow = p.mask + b * p.mask_sb + h * p.mask_sh + (int64_t)max(min(q, row_end - 1), 0) * p.mask_ss;
 
   const int64_t qo = b * p.q_sb + h * p.q_sh + q_tok0 * p.q_ss;
+  const int64_t go = b * p.o_sb + h * p.o_sh + q_tok0 * p.o_ss;
   const int64_t ko = b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
+  const int64_t vo = b * p.v_sb + g * p.v_sh + kv_tok0 * p.v_ss;
   const uint16_t* qp = p.q + qo;
-  const uint16_t* gp = p.dout + qo;
+  const uint16_t* gp = p.dout + go;
   const uint16_t* kp = p.k + ko;
-  const uint16_t* vp = p.v + ko;
+  const uint16_t* vp = p.v + vo;
 
-  // Q^T and dO^T as B operands: lane (hl, l32) holds row q's chunk 2 t + hl for k-step t
+  // Q^T and dO^T as B operands: lane (hl, l32) holds row q's chunk 2 t + hl for k-step t (zeros
+  // past D and Dv)
   u32x4 qreg[DT], greg[DT];
   {
     const int r = max(min(q, row_end - 1), 0);
 #pragma unroll
     for (int t = 0; t < DT; t++) {
-      qreg[t] = *(const u32x4*)(qp + (int64_t)r * p.q_ss + (2 * t + hl) * 8);
-      greg[t] = *(const u32x4*)(gp + (int64_t)r * p.q_ss + (2 * t + hl) * 8);
+      const int c0 = (2 * t + hl) * 8;
+      qreg[t] = c0 < p.D ? *(const u32x4*)(qp + (int64_t)r * p.q_ss + c0) : u32x4{};
+      greg[t] = c0 < p.Dv ? *(const u32x4*)(gp + (int64_t)r * p.o_ss + c0) : u32x4{};
     }
   }
   const int64_t ml = b * p.ml_sb + h * p.ml_sh + q_tok0 + max(min(q, row_end - 1), 0);
@@ -272,12 +289,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   const int t0 = CAUSAL ? max(qb * kBlock - pre, 0) / kTileRows : 0;
   const int ntiles =
       (row_end > qb * kBlock && kv_end > t0 * kTileRows) ? (kv_end - t0 * kTileRows + kTileRows - 1) / kTileRows : 0;
-  const TileLoad<D> ld(wave, lane, (uint32_t)p.k_ss * 2);
-  const rsrc4 k_rsrc = make_rsrc(kp, extent(Lkv, ld.stride, T::kRowBytes));
-  const rsrc4 v_rsrc = make_rsrc(vp, extent(Lkv, ld.stride, T::kRowBytes));
+  const TileLoad<D> ldk(wave, lane, (uint32_t)p.k_ss * 2, p.D), ldv(wave, lane, (uint32_t)p.v_ss * 2, p.Dv);
+  const rsrc4 k_rsrc = make_rsrc(kp, extent(Lkv, ldk.stride, 2 * p.D));
+  const rsrc4 v_rsrc = make_rsrc(vp, extent(Lkv, ldv.stride, 2 * p.Dv));
   if (ntiles > 0) {
-    ld.issue(k_rsrc, smem, t0 * kTileRows, wave);
-    ld.issue(v_rsrc, smem + 2 * T::kBytes, t0 * kTileRows, wave);
+    ldk.issue(k_rsrc, smem, t0 * kTileRows, wave);
+    ldv.issue(v_rsrc, smem + 2 * T::kBytes, t0 * kTileRows, wave);
   }
   for (int it = 0; it < ntiles; it++) {
     const int key0 = (t0 + it) * kTileRows;
@@ -286,8 +303,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     wait_loads();
     __syncthreads();
     if (it + 1 < ntiles) {
-      ld.issue(k_rsrc, smem + ((it + 1) & 1) * T::kBytes, key0 + kTileRows, wave);
-      ld.issue(v_rsrc, smem + (2 + ((it + 1) & 1)) * T::kBytes, key0 + kTileRows, wave);
+      ldk.issue(k_rsrc, smem + ((it + 1) & 1) * T::kBytes, key0 + kTileRows, wave);
+      ldv.issue(v_rsrc, smem + (2 + ((it + 1) & 1)) * T::kBytes, key0 + kTileRows, wave);
     }
     const uint8_t* kt = smem + (it & 1) * T::kBytes;
     const uint8_t* vt = smem + (2 + (it & 1)) * T::kBytes;
@@ -390,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     phase(IC<3>{}, IC<-1>{}, IC<-1>{}, true);
   }
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
-  if (q < row_limit) store_rows<E, D>(p.dq + qo + (int64_t)q * p.q_ss, acc, p.scale, hl);
+  if (q < row_limit) store_rows<E, D>(p.dq + qo + (int64_t)q * p.q_ss, acc, p.scale, hl, p.D);
 }
 
 // ---- dK, dV: one 128-key kv-block of kv-head g per workgroup, 4 waves x 32 keys ----
@@ -436,16 +453,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int pre = CAUSAL ? p.band_pre : 0;
 
   const int64_t ko = b * p.k_sb + g * p.k_sh + kv_tok0 * p.k_ss;
+  const int64_t vo = b * p.v_sb + g * p.v_sh + kv_tok0 * p.v_ss;
   const uint16_t* kp = p.k + ko;
-  const uint16_t* vp = p.v + ko;
-  // K^T and V^T as B operands: lane (hl, l32) holds key's chunk 2 t + hl for k-step t
+  const uint16_t* vp = p.v + vo;
+  // K^T and V^T as B operands: lane (hl, l32) holds key's chunk 2 t + hl for k-step t (zeros past
+  // D and Dv)
   u32x4 kreg[DT], vreg[DT];
   {
     const int r = max(min(key, key_end - 1), 0);
 #pragma unroll
     for (int t = 0; t < DT; t++) {
-      kreg[t] = *(const u32x4*)(kp + (int64_t)r * p.k_ss + (2 * t + hl) * 8);
-      vreg[t] = *(const u32x4*)(vp + (int64_t)r * p.k_ss + (2 * t + hl) * 8);
+      const int c0 = (2 * t + hl) * 8;
+      kreg[t] = c0 < p.D ? *(const u32x4*)(kp + (int64_t)r * p.k_ss + c0) : u32x4{};
+      vreg[t] = c0 < p.Dv ? *(const u32x4*)(vp + (int64_t)r * p.v_ss + c0) : u32x4{};
     }
   }
   f32x16 dk[DB], dv[DB];
@@ -461,17 +481,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   const int t_first = q_first / kTileRows;
   const int ntiles = (key_end > kb * kBlock && q_last >= q_first) ? q_last / kTileRows - t_first + 1 : 0;
   const int total = ntiles * p.group;  // tiles u = hh * ntiles + it over the group's q-heads
-  const TileLoad<D> ld(wave, lane, (uint32_t)p.q_ss * 2);
+  const TileLoad<D> ldq(wave, lane, (uint32_t)p.q_ss * 2, p.D), ldg(wave, lane, (uint32_t)p.o_ss * 2, p.Dv);
   const int64_t rows_all = p.rows;
   // lse2 and rowsum(dO * O) sit back to back in the workspace (delta = lse2 + rows_all)
   const rsrc4 ml_rsrc = make_rsrc(p.lse2, (uint32_t)(rows_all * 8));
-  const uint32_t q_bytes = extent(Lq, ld.stride, T::kRowBytes);
+  const uint32_t q_bytes = extent(Lq, ldq.stride, 2 * p.D), g_bytes = extent(Lq, ldg.stride, 2 * p.Dv);
   auto issue = [&](int u) __attribute__((always_inline)) {
     const int hh = u / ntiles, row0 = (t_first + u % ntiles) * kTileRows;
     const int h = g * p.group + hh;
     const int64_t qo = b * p.q_sb + h * p.q_sh + q_tok0 * p.q_ss;
-    ld.issue(make_rsrc(p.q + qo, q_bytes), smem + (u & 1) * T::kBytes, row0, wave);
-    ld.issue(make_rsrc(p.dout + qo, q_bytes), smem + (2 + (u & 1)) * T::kBytes, row0, wave);
+    const int64_t go = b * p.o_sb + h * p.o_sh + q_tok0 * p.o_ss;
+    ldq.issue(make_rsrc(p.q + qo, q_bytes), smem + (u & 1) * T::kBytes, row0, wave);
+    ldg.issue(make_rsrc(p.dout + go, g_bytes), smem + (2 + (u & 1)) * T::kBytes, row0, wave);
     if (wave == 0) {
       // lanes 0..15: 4 lse2 values each, lanes 16..31: 4 rowsum values, lanes 32..63 read past
       // the extent (zeros into the unused half of the 1 KiB)
@@ -620,8 +641,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   wait_loads();  // nothing may still be loading into LDS when the workgroup ends
   if (key < key_limit) {
     const bool pad = key >= key_end;  // (its lane computed a copy of the last valid key)
-    store_rows<E, D>(p.dk + ko + (int64_t)key * p.k_ss, dk, pad ? 0.f : p.scale, hl);
-    store_rows<E, D>(p.dv + ko + (int64_t)key * p.k_ss, dv, pad ? 0.f : 1.f, hl);
+    store_rows<E, D>(p.dk + ko + (int64_t)key * p.k_ss, dk, pad ? 0.f : p.scale, hl, p.D);
+    store_rows<E, D>(p.dv + vo + (int64_t)key * p.v_ss, dv, pad ? 0.f : 1.f, hl, p.Dv);
   }
 }
 
@@ -656,14 +677,14 @@ hipError_t launch_bwd_d(const BwdParams& p, int mode, int stages, hipStream_t st
 }  // namespace
 
 hipError_t launch_attn_bwd(const BwdParams& p, int mode, int stages, hipStream_t stream) {
+  // the kernels built for the next width up; the ABI admits multiples of 8 with Dv <= D <= 128
+  if (p.D < 8 || p.D > 128 || p.Dv < 8 || p.Dv > p.D || p.D % 8 != 0 || p.Dv % 8 != 0) return hipErrorInvalidValue;
   if (p.f16) {
-    if (p.D == 64) return launch_bwd_d<_Float16, 64>(p, mode, stages, stream);
-    if (p.D == 128) return launch_bwd_d<_Float16, 128>(p, mode, stages, stream);
-  } else {
-    if (p.D == 64) return launch_bwd_d<__bf16, 64>(p, mode, stages, stream);
-    if (p.D == 128) return launch_bwd_d<__bf16, 128>(p, mode, stages, stream);
+    if (p.D <= 64) return launch_bwd_d<_Float16, 64>(p, mode, stages, stream);
+    return launch_bwd_d<_Float16, 128>(p, mode, stages, stream);
   }
-  return hipErrorInvalidValue;
+  if (p.D <= 64) return launch_bwd_d<__bf16, 64>(p, mode, stages, stream);
+  return launch_bwd_d<__bf16, 128>(p, mode, stages, stream);
 }
 
 }  // namespace qattn

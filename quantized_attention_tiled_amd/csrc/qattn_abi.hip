@@ -195,7 +195,7 @@ int check_dims_16bit(const qattn::FwdParams& p) {
   return QATTN_OK;
 }
 
-// Head dimensions the quantised forward and the backward take: D = Dv = 64 or 128.
+// Head dimensions the quantised forward takes: D = Dv = 64 or 128.
 int check_dims_fixed(const qattn::FwdParams& p, const char* who) {
   if ((p.D != 64 && p.D != 128) || p.Dv != p.D)
     return fail(QATTN_UNSUPPORTED, "%s needs D = Dv = 64 or 128 (D=%d, Dv=%d)", who, p.D, p.Dv);
@@ -536,7 +536,9 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   int total_qb = 0;
   int rc = setup_common(desc, f, true, true, &total_qb);
   if (rc) return rc;
-  if ((rc = check_dims_fixed(f, "attn_bwd"))) return rc;
+  if (f.D % 8 != 0 || f.Dv % 8 != 0 || f.D > 128 || f.Dv < 8)
+    return fail(QATTN_UNSUPPORTED, "attn_bwd head dimensions D=%d, Dv=%d (supported: multiples of 8 with Dv <= D <= 128)",
+                f.D, f.Dv);
   if (desc->atten_mask && (desc->mask_kind & QATTN_MASK_BITS))
     return fail(QATTN_UNSUPPORTED, "attn_bwd takes byte masks (no QATTN_MASK_BITS)");
   if (!(desc->head_begin == -1 && desc->head_end == -1 && desc->qblock_begin == -1 && desc->qblock_end == -1))
@@ -573,7 +575,8 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.group = desc->Nq / desc->Nkv;
   p.Sq = desc->Sq;
   p.Skv = desc->Skv;
-  p.D = desc->D;
+  p.D = f.D;
+  p.Dv = f.Dv;
   p.causal = desc->sparse_mode;
   p.band_pre = f.band_pre;
   p.band_next = f.band_next;
@@ -590,6 +593,12 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.k_sb = f.k_sb;
   p.k_sh = f.k_sh;
   p.k_ss = f.k_ss;
+  p.v_sb = f.v_sb;
+  p.v_sh = f.v_sh;
+  p.v_ss = f.v_ss;
+  p.o_sb = f.o_sb;
+  p.o_sh = f.o_sh;
+  p.o_ss = f.o_ss;
   p.ml_sb = f.ml_sb;
   p.ml_sh = f.ml_sh;
   p.rows = rows;
@@ -607,10 +616,11 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
     items_q = (int64_t)desc->B * desc->Nq * ((desc->Sq + qattn::kBlock - 1) / qattn::kBlock);
     items_k = (int64_t)desc->B * desc->Nkv * ((desc->Skv + qattn::kBlock - 1) / qattn::kBlock);
   }
-  // the kernels address the workspace (8 bytes per row) and the query rows of one head through
-  // 32-bit byte offsets
+  // the kernels address the workspace (8 bytes per row) and the rows of one head of q, k, v, o
+  // and dO through 32-bit byte offsets, tile offsets (up to a tile past the last row) below 2^31
+  const int64_t row_stride = std::max(std::max(f.q_ss, f.k_ss), std::max(f.v_ss, f.o_ss));
   if (items_q > (int64_t)0x7fffff00 || items_k > (int64_t)0x7fffff00 || rows * 8 >= ((int64_t)1 << 32) ||
-      ((int64_t)std::max(desc->Sq, 1) - 1) * f.q_ss * 2 + 2 * desc->D > (int64_t)INT32_MAX)
+      ((int64_t)std::max(desc->Sq, desc->Skv) + 2 * qattn::kBlock) * row_stride * 2 > (int64_t)INT32_MAX)
     return fail(QATTN_UNSUPPORTED, "problem too large for one launch");
   int mode = 0;
   if (desc->sparse_mode == 2 || desc->sparse_mode == 3 || desc->pre_tokens != INT32_MAX ||
@@ -654,13 +664,13 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
         const int64_t b = g0;
         auto at = [b](auto* ptr, int64_t per_batch) { return ptr ? ptr + b * per_batch : ptr; };
         g.q = at(g.q, g.q_sb);
-        g.o = at(g.o, g.q_sb);
-        g.dout = at(g.dout, g.q_sb);
+        g.o = at(g.o, g.o_sb);
+        g.dout = at(g.dout, g.o_sb);
         g.dq = at(g.dq, g.q_sb);
         g.k = at(g.k, g.k_sb);
-        g.v = at(g.v, g.k_sb);
+        g.v = at(g.v, g.v_sb);
         g.dk = at(g.dk, g.k_sb);
-        g.dv = at(g.dv, g.k_sb);
+        g.dv = at(g.dv, g.v_sb);
         g.m_in = at(g.m_in, g.ml_sb);
         g.l_in = at(g.l_in, g.ml_sb);
         g.lse2 = at(g.lse2, g.ml_sb);

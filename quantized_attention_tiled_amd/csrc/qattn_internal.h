@@ -75,7 +75,7 @@ struct FwdParams {
   uint8_t order[kMaxSeqs];
 };
 
-// Everything a backward launch needs (any layout, bf16 or fp16, D = Dv), passed by value.
+// Everything a backward launch needs (any layout, bf16 or fp16), passed by value.
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -89,13 +89,16 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  // element strides of batch, head and token: q_* for q, o, dout and dq; k_* for k, v, dk and dv;
-  // ml_* for softmax max / sum and the workspace rows (token stride 1)
+  // element strides of batch, head and token: q_* for q and dq; k_* for k and dk; v_* for v and
+  // dv; o_* for o and dout; ml_* for softmax max / sum and the workspace rows (token stride 1)
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
   int64_t ml_sb, ml_sh;
   int64_t rows;       // rows of softmax max / sum: B Nq Sq (BNSD) or Nq T (TND)
-  int B, Nq, Nkv, group, Sq, Skv, D;
+  int B, Nq, Nkv, group, Sq, Skv;
+  int D, Dv;          // head dimensions of q / k and of v / o (multiples of 8, Dv <= D <= 128)
   int causal;         // 0 (none or the band), 2 top-left, 3 bottom-right
   int band_pre, band_next;  // causal-family key range i - band_pre <= j <= i + band_next (as forward)
   const uint8_t* mask;      // boolean atten_mask (1 = masked) or NULL, with its element strides

@@ -182,8 +182,11 @@ def test_backward_validation(q):
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(_desc(q, B=2, Nq=4, Sq=100))) == 8 * 2 * 4 * 100
     assert lib.attn_bwd_workspace_bytes(None) == 0
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(_desc(q, layout=1, B=3, Nq=4, Sq=100))) == 8 * 4 * 100  # TND
-    for kw in (dict(Dv=64), dict(D=96), dict(D=256), dict(head_begin=0, head_end=1), dict(qblock_begin=0, qblock_end=1)):
+    # head dimensions: multiples of 8 with Dv <= D <= 128 (D = 96, Dv = 64 and the like are taken)
+    for kw in (dict(Dv=60), dict(D=100), dict(D=256), dict(D=136, Dv=64), dict(D=4),
+               dict(head_begin=0, head_end=1), dict(qblock_begin=0, qblock_end=1)):
         assert bwd(_desc(q, **kw)) == 2, kw
+    assert bwd(_desc(q, Dv=136)) == 1  # Dv > D
     assert bwd(_desc(q), ws=None) == 1
     assert bwd(_desc(q), m=FAKE + 2) == 3
     assert bwd(_desc(q, sparse_mode=1)) == 1
@@ -196,7 +199,7 @@ def test_backward_validation(q):
 
     assert noalloc(_desc(q, Nq=64, Nkv=64, Sq=65538, Skv=128)) == 2
     assert b"static buffer" in lib.qattn_last_error()
-    assert noalloc(_desc(q, Dv=64)) == 2
+    assert noalloc(_desc(q, Dv=60)) == 2
     assert noalloc(_desc(q, sparse_mode=1)) == 1
     assert lib.attn_bwd_noalloc(ctypes.byref(_desc(q)), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                                 None) == 1

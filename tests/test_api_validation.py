@@ -137,3 +137,10 @@ def test_backward_buffers():
     raises_shape("softmax_max", api.attn_bwd, q, k, v, o, do, z((1, 2, 255), f32), l)
     raises_shape("atten_mask", api.attn_bwd, q, k, v, o, do, m, l, atten_mask=z((1, 3, 256, 256), u8))
     raises_shape("actual_seq_lengths", api.attn_bwd, q, k, v, o, do, m, l, actual_seq_lengths=[1, 2])
+    # Dv < D: out, dout and dv take v's head dimension
+    v32 = o32 = z((1, 2, 256, 32), bf16)
+    raises_device(api.attn_bwd, q, k, v32, o32, o32, m, l)
+    raises_shape("out and dout", api.attn_bwd, q, k, v32, o, o32, m, l)
+    raises_shape("out and dout", api.attn_bwd, q, k, v32, o32, do, m, l)
+    raises_shape("dv", api.attn_bwd, q, k, v32, o32, o32, m, l, dv=z((1, 2, 256, 64), bf16))
+    raises_shape("does not match k", api.attn_bwd, q, k, z((1, 2, 255, 32), bf16), o32, o32, m, l)

@@ -137,3 +137,25 @@ def test_actual_lengths_finite_differences():
     for a, b in ((dq, fq), (dk, fk), (dv, fv)):
         np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-8)
     assert np.all(dq[0, :, 3:] == 0) and np.all(dk[1, :, 2:] == 0) and np.all(dv[1, :, 2:] == 0)
+
+
+@pytest.mark.parametrize("layout,kw", [("BNSD", dict(sparse_mode=2)), ("BNSD", dict(sparse_mode=0)),
+                                       ("TND", dict(sparse_mode=3))])
+def test_finite_differences_value_dim_below_d(layout, kw):
+    """Dv < D (v, O and dO narrower than q and k; the fused-attention guide allows D_v <= D_k):
+    finite differences through the forward oracle, GQA 2."""
+    D, Dv, Nq, Nkv = 3, 2, 2, 1
+    if layout == "TND":
+        lq, lk = [3, 2], [2, 4]
+        cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+        q, k = RNG.normal(size=(cq[-1], Nq, D)), RNG.normal(size=(ck[-1], Nkv, D))
+        v, do = RNG.normal(size=(ck[-1], Nkv, Dv)), RNG.normal(size=(cq[-1], Nq, Dv))
+        kw = dict(kw, layout="TND", cu_seqlens_q=cq, cu_seqlens_kv=ck)
+    else:
+        q, k = RNG.normal(size=(1, Nq, 4, D)), RNG.normal(size=(1, Nkv, 5, D))
+        v, do = RNG.normal(size=(1, Nkv, 5, Dv)), RNG.normal(size=(1, Nq, 4, Dv))
+    dq, dk, dv = attention_backward(q, k, v, do, 0.75, **kw)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    fq, fk, fv = _finite_diff(q, k, v, do, 0.75, **kw)
+    for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+        np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-8)
