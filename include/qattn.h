@@ -149,9 +149,10 @@ typedef struct qattn_desc {
   int32_t dtype;                /* QATTN_DTYPE_BF16 (default) or _FP16: type of q, k, v and o; the
                                    quantised entry point takes BF16 only */
   int32_t Dv;                   /* value / output head dimension, 1 <= Dv <= D; 0 means D. The 16-bit
-                                   forward entry points take D and Dv multiples of 8 up to 256; the
-                                   quantised forward and the backward take D = Dv = 64 or 128; other
-                                   dimensions in [1, 768] return QATTN_UNSUPPORTED */
+                                   forward entry points take D and Dv multiples of 8 up to 256, the
+                                   backward multiples of 8 up to 128, the quantised forward
+                                   D = Dv = 64 or 128; other dimensions in [1, 768] return
+                                   QATTN_UNSUPPORTED */
   const int32_t* actual_seq_lengths;    /* not TND: host [B] valid query rows per batch, or NULL (= Sq);
                                            the library reads exactly B entries */
   const int32_t* actual_seq_lengths_kv; /* not TND: host [B] valid keys per batch, or NULL (= Skv); B entries */
