@@ -261,7 +261,11 @@ int attn_fwd_qbsa(const qattn_desc* desc, const int8_t* q, const int8_t* k, cons
  *   dimensions D and Dv multiples of 8 with Dv <= D <= 128 (else
  *   QATTN_UNSUPPORTED); the masks of attn_fwd (sparse_mode 0, 2 or 3, the
  *   band, byte atten_mask), GQA, actual lengths (padded rows and keys get zero
- *   gradients); no subrange (else QATTN_UNSUPPORTED).
+ *   gradients). A head range [head_begin, head_end) that holds whole groups of
+ *   Nq / Nkv q-heads, with every q-block, writes dq of those q-heads and dk, dv
+ *   of their kv-heads [head_begin / g, head_end / g), bit for bit as the full
+ *   call does, and nothing else; other head ranges and any q-block range
+ *   return QATTN_UNSUPPORTED (dk and dv sum over every query row).
  *   q, k, v, o, dout: inputs of desc->dtype (o and the softmax outputs from
  *   attn_fwd on the same description; v, o and dout have Dv columns per head);
  *   dq, dk, dv: outputs of that type shaped like q, k, v (a kv-head's

@@ -13,7 +13,7 @@ Python binding of the qattn C ABI (include/qattn.h). The kernels live in
 * ``attn_fwd_qbsa``              INT8 Q.K / FP8 P.V quantised block-sparse attention
 * ``attn_bwd``                   dQ, dK, dV of the dense forward (bf16 / fp16, every layout, GQA,
                                  causal, band, boolean masks, actual lengths; D, Dv multiples
-                                 of 8 with Dv <= D <= 128)
+                                 of 8 with Dv <= D <= 128; head ranges of whole GQA groups)
 * ``attn_bwd_noalloc``           attn_bwd for callers that cannot allocate: its workspace is a
                                  static per-GPU buffer of the library
 

@@ -403,7 +403,7 @@ def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scal
 
 def _bwd_args(q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, layout, cu_seqlens_q,
               cu_seqlens_kv, head_num, atten_mask, pre_tokens, next_tokens, actual_seq_lengths,
-              actual_seq_lengths_kv, dq, dk, dv, allocate_grads: bool):
+              actual_seq_lengths_kv, dq, dk, dv, allocate_grads: bool, head_range=None):
     """Checked arguments of the backward entry points: (desc, host arrays kept alive, mask, dq, dk, dv)."""
     dtype = _check_dtypes(q, k, v)
     for t, n in ((out, "out"), (dout, "dout")):
@@ -450,7 +450,8 @@ def _bwd_args(q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, 
             _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv"))
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale, sparse_mode=sparse_mode,
                      cu_q=cu_q, cu_kv=cu_kv, dtype=dtype, atten_mask=atten_mask, mask_kind=kind,
-                     pre_tokens=pre_tokens, next_tokens=next_tokens, actual_q=keep[2], actual_kv=keep[3], Dv=Dv)
+                     pre_tokens=pre_tokens, next_tokens=next_tokens, actual_q=keep[2], actual_kv=keep[3], Dv=Dv,
+                     head_range=head_range)
     return desc, keep, atten_mask, dq, dk, dv
 
 
@@ -462,19 +463,21 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
              actual_seq_lengths: Optional[Sequence[int]] = None,
              actual_seq_lengths_kv: Optional[Sequence[int]] = None, dq: Optional[torch.Tensor] = None,
              dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None):
+             workspace: Optional[torch.Tensor] = None, head_range: Optional[Tuple[int, int]] = None):
     """Gradients (dq, dk, dv) of attn_fwd on bfloat16 or float16 q, k, v (one type) in any layout
     attn_fwd takes (shapes as there; D and Dv multiples of 8 with Dv <= D <= 128), given the
     forward's out and softmax_max / softmax_sum and the output gradient dout (shaped like out). The masks are the forward's: sparse_mode,
     ``atten_mask`` (not with TND), the ``pre_tokens`` / ``next_tokens`` band and per-batch
     ``actual_seq_lengths`` / ``actual_seq_lengths_kv`` (padded rows and keys get zero gradients).
     ``workspace``: optional fp32 device tensor of at least attn_bwd_workspace_bytes / 4 elements
-    (2 B Nq Sq; TND: 2 Nq T)."""
+    (2 B Nq Sq; TND: 2 Nq T). ``head_range`` (h0, h1): whole groups of Nq / Nkv q-heads; only dq of
+    those q-heads and dk, dv of their kv-heads are written, bit for bit as by the full call."""
     lib = load()
     dev = q.device
     desc, _keep, atten_mask, dq, dk, dv = _bwd_args(
         q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, layout, cu_seqlens_q, cu_seqlens_kv,
-        head_num, atten_mask, pre_tokens, next_tokens, actual_seq_lengths, actual_seq_lengths_kv, dq, dk, dv, True)
+        head_num, atten_mask, pre_tokens, next_tokens, actual_seq_lengths, actual_seq_lengths_kv, dq, dk, dv, True,
+        head_range)
     need = lib.attn_bwd_workspace_bytes(ctypes.byref(desc)) // 4
     if workspace is None:
         workspace = torch.empty(max(1, need), dtype=torch.float32, device=dev)

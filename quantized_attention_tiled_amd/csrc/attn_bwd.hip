@@ -173,17 +173,19 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[D 
     }
 }
 
-// ---- per-row preparation: lse2 = m log2(e) + log2(l) (+inf when l = 0) and D = dO . O ----
+// ---- per-row preparation: lse2 = m log2(e) + log2(l) (+inf when l = 0) and D = dO . O, over the
+// `rows` rows of the launch's heads ----
 template <typename E, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
-  const int64_t rows = p.rows;
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p, int64_t rows) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;  // 16 lanes per row, D / 16 elements each
   float acc = 0.f;
+  // row = (b Nq + h) Sq + i for BNSD, h T + t for TND (one "batch" of T tokens); softmax max / sum
+  // and the workspace rows are addressed through their batch and head strides
+  const int64_t i = row % p.Sq, bh = row / p.Sq;
+  const int64_t h = bh % p.Nq, b = bh / p.Nq;
+  const int64_t mi = b * p.ml_sb + h * p.ml_sh + i;
   if (row < rows) {
-    // row = (b Nq + h) Sq + i for BNSD, h T + t for TND (one "batch" of T tokens)
-    const int64_t i = row % p.Sq, bh = row / p.Sq;
-    const int64_t h = bh % p.Nq, b = bh / p.Nq;
     const int64_t e0 = b * p.o_sb + h * p.o_sh + i * p.o_ss;
     const uint16_t* o = p.o + e0;
     const uint16_t* g = p.dout + e0;
@@ -200,12 +202,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
   if (row < rows && sub == 0) {
-    const float m = p.m_in[row], l = p.l_in[row];
+    const float m = p.m_in[mi], l = p.l_in[mi];
     // a row with no key (l = 0, also the padding past an actual length) gets P = 0 and rowsum 0,
     // whatever its O and dO rows hold
     const bool live = l > 0.f && m != kNegInf;
-    p.lse2[row] = live ? m * kLog2e + __builtin_log2f(l) : kPosInf;
-    p.delta[row] = live ? acc : 0.f;
+    p.lse2[mi] = live ? m * kLog2e + __builtin_log2f(l) : kPosInf;
+    p.delta[mi] = live ? acc : 0.f;
   }
 }
 
@@ -657,8 +659,10 @@ void launch_bwd_mode(const BwdParams& pq, const BwdParams& pk, hipStream_t strea
 
 template <typename E, int D>
 hipError_t launch_bwd_d(const BwdParams& p, int mode, int stages, hipStream_t stream) {
-  if ((stages & kBwdPrep) && p.rows > 0)
-    hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((p.rows + 15) / 16)), dim3(256), 0, stream, p);
+  const int64_t prep_rows = (int64_t)(p.nseq > 0 ? 1 : p.B) * p.Nq * p.Sq;  // this launch's heads
+  if ((stages & kBwdPrep) && prep_rows > 0)
+    hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((prep_rows + 15) / 16)), dim3(256), 0, stream, p,
+                       prep_rows);
   if (!(stages & kBwdProducts)) return hipGetLastError();
   BwdParams pq = p;
   pq.total_items = p.nseq > 0 ? p.Nq * p.q_tiles : p.B * p.Nq * ((p.Sq + kBlock - 1) / kBlock);

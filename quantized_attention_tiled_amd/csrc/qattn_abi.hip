@@ -541,8 +541,13 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
                 f.D, f.Dv);
   if (desc->atten_mask && (desc->mask_kind & QATTN_MASK_BITS))
     return fail(QATTN_UNSUPPORTED, "attn_bwd takes byte masks (no QATTN_MASK_BITS)");
-  if (!(desc->head_begin == -1 && desc->head_end == -1 && desc->qblock_begin == -1 && desc->qblock_end == -1))
-    return fail(QATTN_UNSUPPORTED, "attn_bwd covers the whole problem (no head or q-block subrange)");
+  // a head subrange holds whole groups of q-heads (those that share kv-heads) and every q-block:
+  // dK and dV of a kv-head sum over every query row of its q-heads
+  if (f.qb0 != 0 || f.qb1 != total_qb)
+    return fail(QATTN_UNSUPPORTED, "attn_bwd takes a head range, not a q-block range");
+  if (f.h0 % f.group != 0 || f.nh % f.group != 0)
+    return fail(QATTN_UNSUPPORTED, "attn_bwd head range [%d, %d) must hold whole groups of %d q-heads", f.h0,
+                f.h0 + f.nh, f.group);
   const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
   const char* names[] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};
   if ((rc = check_ptrs(ptrs, names, 8))) return rc;
@@ -604,17 +609,18 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
   p.rows = rows;
   p.nseq = tnd ? desc->B : 0;
   p.actual = f.actual;
+  const int nh = f.nh, nkv = f.nh / f.group;  // heads of this call
   int64_t items_q = 0, items_k = 0;
   if (tnd) {
     for (int i = 0; i < desc->B; i++) {
       items_q += (desc->cu_seqlens_q[i + 1] - desc->cu_seqlens_q[i] + qattn::kBlock - 1) / qattn::kBlock;
       items_k += (desc->cu_seqlens_kv[i + 1] - desc->cu_seqlens_kv[i] + qattn::kBlock - 1) / qattn::kBlock;
     }
-    items_q *= desc->Nq;
-    items_k *= desc->Nkv;
+    items_q *= nh;
+    items_k *= nkv;
   } else {
-    items_q = (int64_t)desc->B * desc->Nq * ((desc->Sq + qattn::kBlock - 1) / qattn::kBlock);
-    items_k = (int64_t)desc->B * desc->Nkv * ((desc->Skv + qattn::kBlock - 1) / qattn::kBlock);
+    items_q = (int64_t)desc->B * nh * ((desc->Sq + qattn::kBlock - 1) / qattn::kBlock);
+    items_k = (int64_t)desc->B * nkv * ((desc->Skv + qattn::kBlock - 1) / qattn::kBlock);
   }
   // the kernels address the workspace (8 bytes per row) and the rows of one head of q, k, v, o
   // and dO through 32-bit byte offsets, tile offsets (up to a tile past the last row) below 2^31
@@ -632,6 +638,26 @@ int bwd_impl(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
     if (!ws) return rc;
     p.lse2 = ws;
     p.delta = ws + rows;
+  }
+  if (nh < desc->Nq) {
+    // a head subrange: the same kernels on q-heads [h0, h0 + nh) and kv-heads [h0 / group, ..);
+    // the workspace keeps the whole problem's row layout
+    const int64_t h0 = f.h0, g0 = f.h0 / f.group;
+    p.q += h0 * p.q_sh;
+    p.dq += h0 * p.q_sh;
+    p.o += h0 * p.o_sh;
+    p.dout += h0 * p.o_sh;
+    p.m_in += h0 * p.ml_sh;
+    p.l_in += h0 * p.ml_sh;
+    p.lse2 += h0 * p.ml_sh;
+    p.delta += h0 * p.ml_sh;
+    if (p.mask) p.mask += h0 * p.mask_sh;
+    p.k += g0 * p.k_sh;
+    p.dk += g0 * p.k_sh;
+    p.v += g0 * p.v_sh;
+    p.dv += g0 * p.v_sh;
+    p.Nq = nh;
+    p.Nkv = nkv;
   }
   // The per-row preparation runs once over every row. The dQ and dK/dV products run once per group
   // of at most kMaxSeqs sequences (TND: their cumulative lengths, token offsets of the whole

@@ -84,8 +84,9 @@ struct BwdParams {
   const uint16_t* dout;
   const float* m_in;  // forward softmax max / sum [B, Nq, Sq]
   const float* l_in;
-  float* lse2;        // workspace [B, Nq, Sq]: log2 of the softmax denominator, +inf for empty rows
-  float* delta;       // workspace [B, Nq, Sq]: rowsum(dO * O)
+  float* lse2;        // workspace rows, laid out as softmax max / sum: log2 of the softmax
+                      // denominator, +inf for empty rows
+  float* delta;       // the same rows of rowsum(dO * O), `rows` floats after lse2
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -96,7 +97,7 @@ struct BwdParams {
   int64_t v_sb, v_sh, v_ss;
   int64_t o_sb, o_sh, o_ss;
   int64_t ml_sb, ml_sh;
-  int64_t rows;       // rows of softmax max / sum: B Nq Sq (BNSD) or Nq T (TND)
+  int64_t rows;       // rows of the whole problem's softmax max / sum: B Nq Sq (BNSD) or Nq T (TND)
   int B, Nq, Nkv, group, Sq, Skv;
   int D, Dv;          // head dimensions of q / k and of v / o (multiples of 8, Dv <= D <= 128)
   int causal;         // 0 (none or the band), 2 top-left, 3 bottom-right

@@ -184,8 +184,11 @@ def test_backward_validation(q):
     assert lib.attn_bwd_workspace_bytes(ctypes.byref(_desc(q, layout=1, B=3, Nq=4, Sq=100))) == 8 * 4 * 100  # TND
     # head dimensions: multiples of 8 with Dv <= D <= 128 (D = 96, Dv = 64 and the like are taken)
     for kw in (dict(Dv=60), dict(D=100), dict(D=256), dict(D=136, Dv=64), dict(D=4),
-               dict(head_begin=0, head_end=1), dict(qblock_begin=0, qblock_end=1)):
+               dict(head_begin=0, head_end=1), dict(head_begin=1, head_end=3), dict(qblock_begin=0, qblock_end=1),
+               dict(head_begin=0, head_end=2, qblock_begin=0, qblock_end=1)):
+        # head ranges must hold whole groups (Nq / Nkv = 2 q-heads) and every q-block
         assert bwd(_desc(q, **kw)) == 2, kw
+    assert bwd(_desc(q, head_begin=2, head_end=5)) == 1  # past Nq
     assert bwd(_desc(q, Dv=136)) == 1  # Dv > D
     assert bwd(_desc(q), ws=None) == 1
     assert bwd(_desc(q), m=FAKE + 2) == 3
