@@ -499,16 +499,19 @@ def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
                      head_num: Optional[int] = None, atten_mask: Optional[torch.Tensor] = None,
                      pre_tokens: int = NO_LIMIT, next_tokens: int = NO_LIMIT,
                      actual_seq_lengths: Optional[Sequence[int]] = None,
-                     actual_seq_lengths_kv: Optional[Sequence[int]] = None):
+                     actual_seq_lengths_kv: Optional[Sequence[int]] = None,
+                     head_range: Optional[Tuple[int, int]] = None):
     """attn_bwd for callers that cannot allocate: the caller passes every input and the outputs
     dq, dk, dv; the workspace is the library's static per-GPU buffer (at most
     NOALLOC_WORKSPACE_BYTES, i.e. 4194304 query rows). Allocates no device memory. Calls that
-    overlap on one GPU share that buffer and must be serialised by the caller."""
+    overlap on one GPU share that buffer and must be serialised by the caller. ``head_range`` as
+    for attn_bwd."""
     lib = load()
     dev = q.device
     desc, _keep, atten_mask, dq, dk, dv = _bwd_args(
         q, k, v, out, dout, softmax_max, softmax_sum, scale, sparse_mode, layout, cu_seqlens_q, cu_seqlens_kv,
-        head_num, atten_mask, pre_tokens, next_tokens, actual_seq_lengths, actual_seq_lengths_kv, dq, dk, dv, False)
+        head_num, atten_mask, pre_tokens, next_tokens, actual_seq_lengths, actual_seq_lengths_kv, dq, dk, dv, False,
+        head_range)
     _placed(dev, q=q, k=k, v=v, out=out, dout=dout, softmax_max=softmax_max, softmax_sum=softmax_sum,
             atten_mask=atten_mask, dq=dq, dk=dk, dv=dv)
     with torch.cuda.device(dev):
