@@ -101,10 +101,13 @@ struct Tile {
 };
 
 // Workgroups per CU the kernel is built for: two waves per SIMD (two workgroups of one q-block or
-// one of two) up to D = 128; one wave per SIMD beyond, where a wave's Q^T and O^T registers alone
-// take 192 of the 256 a two-wave budget leaves.
+// one of two) at D = 128; three at D = 64, whose kernels need at most 168 registers per lane (three
+// one-q-block workgroups per CU: against two q-blocks per workgroup at two waves per SIMD, C2's
+// shape at D = 64 0.7145 -> 0.7047 ms, at S = 32K 11.36 -> 10.94 ms, same box); one wave per
+// SIMD beyond D = 128, where a wave's Q^T and O^T registers alone take 192 of the 256 a two-wave
+// budget leaves.
 template <int D, int NQB>
-constexpr int fwd_blocks_per_cu() { return D > 128 ? 1 : 2 / NQB; }
+constexpr int fwd_blocks_per_cu() { return D > 128 ? 1 : (D <= 64 && NQB == 1 ? 3 : 2 / NQB); }
 
 // NQB q-blocks per workgroup share every K/V tile (4 NQB waves). D and DV are the query/key and
 // value head dimensions the kernel is built for (DV <= D); the problem's own p.D <= D and

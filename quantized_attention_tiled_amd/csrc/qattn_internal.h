@@ -121,14 +121,16 @@ enum BwdStages : int { kBwdPrep = 1, kBwdProducts = 2 };
 hipError_t launch_attn_bwd(const BwdParams& p, int mode, int stages, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, int mode, hipStream_t stream);
 hipError_t launch_attn_fwd_f16(const FwdParams& p, int mode, hipStream_t stream);
-// q-blocks per workgroup of the 16-bit kernels in `mode` (the host sets qblocks_per_tile to
-// match): two consecutive q-blocks share the K/V tiles when both see the same keys (no causal
-// mask or band, no kept list); causal, band and block-sparse launches take one q-block each.
-// q-blocks per workgroup of the 16-bit forward: two share the K/V tiles of unmasked, masked and
-// varlen launches up to head dimension 128 (D = the kernel's padded head dimension)
 // the head dimension the 16-bit forward kernel is built for, for a problem's D (a multiple of 8)
 constexpr int fwd_kernel_dim(int D) { return D <= 64 ? 64 : D <= 128 ? 128 : 256; }
-constexpr int fwd_qblocks_per_tile(int mode, int D) { return (mode & (kCausal | kSparse)) || D > 128 ? 1 : 2; }
+// q-blocks per workgroup of the 16-bit forward in `mode`, for the kernel's head dimension D (the
+// host sets qblocks_per_tile to match): at D = 128 two consecutive q-blocks share the K/V tiles
+// when both see the same keys (no causal mask or band, no kept list); causal, band and
+// block-sparse launches take one q-block each, and so does every launch at D = 64, whose
+// registers leave room for three one-q-block workgroups per CU (three waves per SIMD), or D = 256.
+constexpr int fwd_qblocks_per_tile(int mode, int D) {
+  return (mode & (kCausal | kSparse)) || D > 128 || D <= 64 ? 1 : 2;
+}
 hipError_t launch_attn_qbsa(const FwdParams& p, hipStream_t stream);
 hipError_t launch_quant_qk(const uint16_t* x, int B, int N, int S, int D, int8_t* xq, float* scale,
                            hipStream_t stream);
