@@ -12,10 +12,10 @@
 //
 // Work decomposition: 4 waves per 128-row q-block of one (batch, head); each wave owns 32 query
 // rows and needs at most 256 VGPRs per lane, so every SIMD runs two waves whose matrix and vector
-// work interleave. A workgroup holds 4 K/V tiles of LDS (64 KiB at D = 128). Causal and
-// block-sparse launches take one q-block per workgroup (two workgroups per CU); the other modes
-// take two consecutive q-blocks, eight waves sharing every K/V tile, which halves the tile loads
-// per query row.
+// work interleave (three at D = 64, one at D = 256). A workgroup holds 4 K/V tiles of LDS (64 KiB
+// at D = 128). Causal and block-sparse launches take one q-block per workgroup (two workgroups per
+// CU); at D = 128 the other modes take two consecutive q-blocks, eight waves sharing every K/V
+// tile, which halves the tile loads per query row.
 //   * Q^T, the B operand of S^T = K Q^T, stays in registers for the whole kernel;
 //   * K and V stream through LDS in 64-key tiles, each in a ring of two slots, straight from
 //     HBM with buffer_load ... lds (16 bytes per lane, no staging registers) into XOR-swizzled
