@@ -33,7 +33,8 @@
 // end of that block, so every p lies in [0, 1] and is rounded to FP8 at the same scale as in the
 // page's schedule. Between two steps one compare tells whether any row's max grew; only then are
 // l and O rescaled, and when the second half of a block raised it, the first half's P (not yet
-// multiplied with V) is formed again from its scores against the block's max.
+// multiplied with V) is formed again against the block's max: its binary32 p, kept in place of its
+// scores, times 2^(old max - new max), then the FP8 pack.
 // A row's arithmetic depends only on its own q-block and the kept list, so head or q-block
 // subrange launches reproduce the full call bit for bit.
 #include "qattn_internal.h"
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     // 2 VD spreads the loads of the next K tile (into K slot KD, from byte offset dk) and V tile
     // (V slot VD, from dv) over the step's slots; DMA = 0 issues none.
     auto step = [&](auto KS, auto KH, auto VS, auto VH, auto NEXT, auto CUR, auto PREV, auto PIN, auto POUT,
-                    auto KS2, auto KH2, auto DMA, i32x16 (&sn)[2], const i32x16 (&sc)[2], const i32x8& pp,
+                    auto KS2, auto KH2, auto DMA, i32x16 (&sn)[2], i32x16 (&sc)[2], const i32x8& pp,
                     i32x8& pc, i32x4 (&carry)[2], float ct, float cc, int& mm, uint32_t dk, uint32_t dv)
                     __attribute__((always_inline)) {
       constexpr int dma_ = decltype(DMA)::value;
@@ -347,6 +348,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
             if (aq + 1 == k) {
               x[2 * q] = __builtin_amdgcn_exp2f(x[2 * q]);
               x[2 * q + 1] = __builtin_amdgcn_exp2f(x[2 * q + 1]);
+              // p takes the place of its score (which nothing reads again): a first half's P is
+              // formed again from it if the block's second half raises the max
+              sc[kb][r0] = __float_as_int(x[2 * q]);
+              sc[kb][r0 + 1] = __float_as_int(x[2 * q + 1]);
               pin_use(x[2 * q]);
               pin_use(x[2 * q + 1]);
             }
@@ -439,14 +444,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     auto tile_plain = [&](int blk) __attribute__((always_inline)) -> bool {
       return blk_valid(blk) && (blk + 1) * kTK <= Lkv;
     };
-    // P of one step from its scores, against the offset cc: the same operations, in the same
-    // order, as the softmax stages of `step` (P only; the row sum is not formed again).
-    auto form_p = [&](const i32x16 (&s)[2], i32x8& pc, float ct, float cc) __attribute__((always_inline)) {
+    // P of a step formed again for a larger reference max: its p (left in the score registers by
+    // the step's softmax, binary32) times alpha = 2^(old max - new max), then the same FP8 pack.
+    auto form_p = [&](const i32x16 (&pv32)[2], i32x8& pc, float alpha) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < 16; q++) {
         const int kb = q >> 3, r0 = 2 * (q & 7);
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[kb][r0]), ct, -cc));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[kb][r0 + 1]), ct, -cc));
+        const float x0 = __int_as_float(pv32[kb][r0]) * alpha;
+        const float x1 = __int_as_float(pv32[kb][r0 + 1]) * alpha;
         if (q & 1)
           pc[q >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, pc[q >> 1], true);
         else
@@ -458,8 +463,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
     // P is the running max over all keys up to the end of that block, as in the tiled loop with
     // 128 x 128 tiles: the first half (HALF 0) is formed against the max through its own 64 keys;
     // when the second half (HALF 1) raises a row's max, the first half's P is formed again from
-    // its scores s0 (untouched until the following step) into p0, before the step that issues its
-    // P V. After a first half, O is rescaled one step late (the P V issued meanwhile still belongs
+    // its binary32 p (left in s0 by its softmax, untouched until the following step) times
+    // alpha = 2^(old max - new max) into p0, before the step that issues its P V. After a first half, O is rescaled one step late (the P V issued meanwhile still belongs
     // to the old max); after a second half at once, together with any pending factor.
     auto bookkeep = [&](bool fast, int blk, auto HALF, i32x16 (&s)[2], int mm, float ct, const i32x16 (&s0)[2],
                         i32x8& p0) __attribute__((always_inline)) -> float {
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
 #pragma unroll
           for (int db = 0; db < DB; db++) o[db] *= f;
           pending = false;
-          form_p(s0, p0, ct, __builtin_fmaf(kMagic, ct, mrun));
+          form_p(s0, p0, alpha);
         }
       }
       if constexpr (half == 1) {
