@@ -184,6 +184,21 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
              qattn_bf16* o, float* softmax_max, float* softmax_sum, void* stream);
 
 /*
+ * pack_atten_mask_bits -- a byte atten_mask (fused-attention guide, section 4.2: 1 = masked;
+ * here any nonzero byte) in the bit-packed form attn_fwd takes with QATTN_MASK_BITS (the
+ * guide's compressed atten_mask, section 8 tuning advice): each row as ceil(Skv / 32) 32-bit
+ * words, key j in bit j % 32 of word j / 32, bits past Skv zero.
+ *   mask: device uint8, `rows` rows of Skv bytes, `mask_row_stride` bytes apart (>= Skv);
+ *   rows = Sq (SS), B Sq (B1SS) or B Nq Sq (BNSS) for a contiguous mask.
+ *   bits: device int32 [rows, ceil(Skv / 32)], 4-byte aligned, owned by the caller; every word
+ *   is written. 1 <= Skv < 2^28.
+ * A mask reused across calls (every layer of a step) is packed once; the forward then reads one
+ * bit per key instead of one byte. Asynchronous on `stream`; errors as the other entry points.
+ */
+int pack_atten_mask_bits(const uint8_t* mask, int64_t rows, int Skv, int64_t mask_row_stride, int32_t* bits,
+                         void* stream);
+
+/*
  * build_kv_block_list -- compact a 128 x 128 block keep mask into, per
  * (batch, q-head, q-block), the ascending kept kv-block indices (EagleQBSA
  * article, API call: block_sparse_mask with block_shape [128, 128]).

@@ -257,6 +257,30 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float 
     return out, softmax_max, softmax_sum
 
 
+def pack_atten_mask_bits(atten_mask: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The bit-packed form of a byte atten_mask (uint8 or bool, nonzero / True = masked, shape
+    [..., Sq, Skv] with contiguous rows): int32 [..., Sq, ceil(Skv / 32)], key j in bit j % 32 of
+    word j // 32. attn_fwd takes the result as an atten_mask of the same kind (SS, B1SS, BNSS)."""
+    lib = load()
+    if atten_mask.dtype == torch.bool:
+        atten_mask = atten_mask.view(torch.uint8)
+    _require(atten_mask, "atten_mask", torch.uint8)
+    if atten_mask.dim() < 2:
+        raise ValueError(f"atten_mask must be [..., Sq, Skv], got shape {tuple(atten_mask.shape)}")
+    Skv = atten_mask.shape[-1]
+    if Skv < 1:
+        raise ValueError("atten_mask needs at least one key")
+    shape = tuple(atten_mask.shape[:-1]) + ((Skv + 31) // 32,)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=atten_mask.device)
+    _require(out, "out", torch.int32, shape)
+    _placed(atten_mask.device, atten_mask=atten_mask, out=out)
+    rows = atten_mask.numel() // Skv
+    with torch.cuda.device(atten_mask.device):
+        check(lib.pack_atten_mask_bits(_vp(atten_mask), rows, Skv, Skv, _vp(out), _stream(atten_mask.device)))
+    return out
+
+
 def build_kv_block_list(keep: torch.Tensor, counts: Optional[torch.Tensor] = None,
                         idx: Optional[torch.Tensor] = None):
     """Kept-block list of a block keep mask uint8 [B, N, QB, KB] (nonzero = keep).
@@ -520,5 +544,6 @@ def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
     return dq, dk, dv
 
 
-__all__ = ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_qbsa", "build_kv_block_list", "quantize_qk_perblock_int8",
+__all__ = ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_qbsa", "build_kv_block_list",
+           "pack_atten_mask_bits", "quantize_qk_perblock_int8",
            "quantize_v_perchannel_fp8", "make_desc", "_lib"]

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
-SOURCES = ["qattn_abi.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_qbsa.hip", "quant.hip", "attn_bwd.hip"]
+SOURCES = ["qattn_abi.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_qbsa.hip", "quant.hip", "attn_bwd.hip",
+           "mask_pack.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are switched off for all device code; the host

@@ -10,6 +10,12 @@
 
 #include "qattn_internal.h"
 
+namespace qattn {
+// mask_pack.hip: byte atten_mask rows -> rows of 32-bit words, one bit per key
+hipError_t launch_mask_pack(const uint8_t* mask, int64_t rows, int Skv, int64_t stride, int32_t* bits,
+                            hipStream_t stream);
+}  // namespace qattn
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -372,6 +378,20 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
                    : qattn::launch_attn_fwd_bf16(g, mode, (hipStream_t)stream);
       },
       "attn_fwd launch");
+}
+
+int pack_atten_mask_bits(const uint8_t* mask, int64_t rows, int Skv, int64_t mask_row_stride, int32_t* bits,
+                         void* stream) {
+  if (rows < 0 || Skv < 1 || Skv >= (1 << 28))
+    return fail(QATTN_INVALID_ARGUMENT, "rows=%lld must be >= 0 and Skv=%d in [1, 2^28)", (long long)rows, Skv);
+  if (mask_row_stride < Skv)
+    return fail(QATTN_INVALID_ARGUMENT, "mask_row_stride=%lld is below Skv=%d", (long long)mask_row_stride, Skv);
+  if (rows == 0) return QATTN_OK;
+  if (!mask || !bits) return fail(QATTN_INVALID_ARGUMENT, "mask and bits must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(bits) & 3u) return fail(QATTN_MISALIGNED, "bits must be 4-byte aligned");
+  if (rows > ((int64_t)1 << 40) / ((Skv + 31) / 32)) return fail(QATTN_UNSUPPORTED, "mask too large for one launch");
+  return hip_status(qattn::launch_mask_pack(mask, rows, Skv, mask_row_stride, bits, (hipStream_t)stream),
+                    "pack_atten_mask_bits launch");
 }
 
 int build_kv_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32_t* counts, int32_t* idx,

@@ -173,6 +173,23 @@ def test_actual_lengths_validation(q):
     assert lib.attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 1
 
 
+def test_pack_mask_validation(q):
+    lib = q.load()
+
+    def pack(mask=FAKE, rows=4, Skv=33, stride=33, bits=FAKE):
+        return lib.pack_atten_mask_bits(mask, rows, Skv, stride, bits, None)
+
+    assert pack(rows=0) == 0                 # nothing to do, nothing launched
+    assert pack(mask=None) == 1
+    assert pack(bits=None) == 1
+    assert pack(Skv=0) == 1
+    assert pack(rows=-1) == 1
+    assert pack(stride=32) == 1              # rows overlap
+    assert pack(Skv=1 << 28, stride=1 << 28) == 1
+    assert pack(bits=FAKE + 2) == 3          # words need 4-byte alignment
+    assert b"aligned" in lib.qattn_last_error()
+
+
 def test_backward_validation(q):
     lib = q.load()
 

@@ -144,3 +144,12 @@ def test_backward_buffers():
     raises_shape("out and dout", api.attn_bwd, q, k, v32, o32, do, m, l)
     raises_shape("dv", api.attn_bwd, q, k, v32, o32, o32, m, l, dv=z((1, 2, 256, 64), bf16))
     raises_shape("does not match k", api.attn_bwd, q, k, z((1, 2, 255, 32), bf16), o32, o32, m, l)
+
+
+def test_pack_mask_buffers():
+    m = z((4, 70), u8)
+    raises_device(api.pack_atten_mask_bits, m)
+    raises_shape("out", api.pack_atten_mask_bits, m, out=z((4, 2), i32))
+    with pytest.raises(TypeError):
+        api.pack_atten_mask_bits(z((4, 70), f32))
+    raises_shape("Sq, Skv", api.pack_atten_mask_bits, z((70,), u8))
