@@ -591,6 +591,9 @@ def main(argv=None):
     ap.add_argument("--mask", choices=["none", "bytes", "bits"], default="none",
                     help="dense BNSD configs: an SS atten_mask [S, S], one byte per key or bit-packed")
     ap.add_argument("--mask-density", type=float, default=0.0, help="fraction of masked keys of --mask (i.i.d.)")
+    ap.add_argument("--no-qblock-order", action="store_true",
+                    help="block-sparse and quantised configs: launch the q-blocks of each head in index order "
+                         "instead of by kept count (build_qblock_order)")
     ap.add_argument("--q-gain", type=float, default=1.0,
                     help="dense configs: multiply Q by this factor (a peaked softmax: rows whose max outgrows the "
                          "16-bit kernel's reference take its second key pass)")
@@ -646,6 +649,8 @@ def main(argv=None):
         from workloads import bf16_bits_to_f32, f32_to_bf16_bits
         w.q = f32_to_bf16_bits(bf16_bits_to_f32(w.q) * np.float32(a.q_gain))
         name += f"_qgain{a.q_gain:g}"
+    if a.no_qblock_order and kind != "dense":
+        name += "_unordered"
     dev = torch.device("cuda:0")
 
     def up(bits):
@@ -691,12 +696,16 @@ def main(argv=None):
         keep = torch.from_numpy(w.keep).to(dev)
         counts = torch.empty(w.keep.shape[:3], dtype=torch.int32, device=dev)
         idx = torch.empty(w.keep.shape, dtype=torch.int32, device=dev)
+        order = None if a.no_qblock_order else torch.empty(w.keep.shape[:3], dtype=torch.int32, device=dev)
 
         def step(ka=None, kb=None):
             qa.build_kv_block_list(keep, counts, idx)
+            if order is not None:
+                qa.build_qblock_order(counts, order)
             if ka is not None:
                 ka.record(stream)
-            qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=w.scale, out=o, softmax_max=m, softmax_sum=l)
+            qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=w.scale, out=o, softmax_max=m, softmax_sum=l,
+                                    qblock_order=order)
             if kb is not None:
                 kb.record(stream)
         dtype, peak = a.dtype, PEAK_BF16
@@ -711,16 +720,19 @@ def main(argv=None):
         qs = torch.empty((w.B, w.Nq, nb), dtype=torch.float32, device=dev)
         ks = torch.empty((w.B, w.Nkv, nb), dtype=torch.float32, device=dev)
         vs = torch.empty((w.B, w.Nkv, w.D), dtype=torch.float32, device=dev)
+        order = None if a.no_qblock_order else torch.empty(w.keep.shape[:3], dtype=torch.int32, device=dev)
 
         def step(ka=None, kb=None):
             qa.quantize_qk_perblock_int8(q, qq, qs)
             qa.quantize_qk_perblock_int8(k, kq, ks)
             qa.quantize_v_perchannel_fp8(v, vq, vs)
             qa.build_kv_block_list(keep, counts, idx)
+            if order is not None:
+                qa.build_qblock_order(counts, order)
             if ka is not None:
                 ka.record(stream)
             qa.attn_fwd_qbsa(qq, kq, vq, qs, ks, vs, counts, idx, scale=w.scale, out=o, softmax_max=m,
-                             softmax_sum=l)
+                             softmax_sum=l, qblock_order=order)
             if kb is not None:
                 kb.record(stream)
         dtype, peak = "int8/fp8", PEAK_FP8
@@ -797,6 +809,7 @@ def main(argv=None):
                                   "bytes": int(amask.numel() * amask.element_size())}
         if w.keep is not None:
             conf["kept_fraction"] = round(float(w.keep.mean()), 4)
+            conf["qblock_order"] = "index" if a.no_qblock_order else "by kept count (build_qblock_order)"
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",

@@ -156,6 +156,16 @@ typedef struct qattn_desc {
   const int32_t* actual_seq_lengths;    /* not TND: host [B] valid query rows per batch, or NULL (= Sq);
                                            the library reads exactly B entries */
   const int32_t* actual_seq_lengths_kv; /* not TND: host [B] valid keys per batch, or NULL (= Skv); B entries */
+  const int32_t* qblock_order;  /* block-sparse and quantised entry points only (else NULL): device
+                                   int32 [B, Nq, QB], per (batch, q-head) a permutation of its q-blocks
+                                   as build_qblock_order writes it, or NULL. The launch takes the
+                                   q-blocks of each head in this order (the work of a q-block
+                                   outside the q-block subrange is skipped); the block-sparse
+                                   kernel then walks each row's kept blocks in ascending order.
+                                   Each row's result does not depend on when it runs, so a subrange
+                                   launch with the same order reproduces the full call bit for bit;
+                                   the block-sparse result's last bits differ from an unordered
+                                   call's, whose walk starts at a rotated block. */
 } qattn_desc;
 
 /*
@@ -197,6 +207,19 @@ int attn_fwd(const qattn_desc* desc, const qattn_bf16* q, const qattn_bf16* k, c
  */
 int pack_atten_mask_bits(const uint8_t* mask, int64_t rows, int Skv, int64_t mask_row_stride, int32_t* bits,
                          void* stream);
+
+/*
+ * build_qblock_order -- per (batch, head) row of `counts` (kept kv-blocks per q-block, as
+ * build_kv_block_list writes it; B x N rows of QB), the q-blocks sorted by kept count, largest
+ * first, ties in ascending q-block order: order[b, n, i] is the q-block of rank i. For the
+ * descriptor's qblock_order: a launch whose concurrently running q-blocks keep about as many
+ * blocks starts and finishes them together, so they walk the key range in step and share its K/V
+ * blocks in the L2 (EagleQBSA article, API call: the 128 x 128 block mask and the kept lists
+ * this scheduling serves).
+ *   counts: device int32 [B, N, QB]; order: device int32 [B, N, QB], 4-byte aligned, every entry
+ *   written. QB <= 16384.
+ */
+int build_qblock_order(const int32_t* counts, int B, int N, int QB, int32_t* order, void* stream);
 
 /*
  * build_kv_block_list -- compact a 128 x 128 block keep mask into, per

@@ -16,7 +16,8 @@ EagleQBSA article, "EagleQBSA quantised block-sparse attention"):
 * ``quant``          INT8 per-128-token-block Q/K and FP8 E4M3 per-channel V
                      quantisers in exact float32 steps; E4M3 encode/decode from
                      the format's definition; the kept-block list (EagleQBSA
-                     article, scheme-design section and the API call at its end).
+                     article, scheme-design section and the API call at its end)
+                     and the q-block order by kept count.
 * ``backward``       the gradients dQ, dK, dV of the ``attention`` definition,
                      written out in float64 (the guide presents the operator
                      as a training operator but gives no backward algorithm).
@@ -37,6 +38,7 @@ from .attention import (  # noqa: F401
     softmax_attention,
 )
 from .quant import (  # noqa: F401
+    qblock_order,
     E4M3_MAX,
     e4m3_decode,
     e4m3_encode,

@@ -134,3 +134,18 @@ def kept_block_list(keep: np.ndarray):
                 counts[b, n, qb] = len(kept)
                 idx[b, n, qb, :len(kept)] = kept
     return counts, idx
+
+
+def qblock_order(counts: np.ndarray) -> np.ndarray:
+    """Per (batch, head) row of kept counts [B, N, QB], the q-block indices sorted by kept count,
+    largest first, ties in ascending q-block index: order[b, n, i] is the q-block of rank i.
+    A scheduling order for the block-sparse launches (the kept lists of the EagleQBSA API call
+    decide how much work each q-block has); written out as the plain sort by key
+    (-count, index)."""
+    counts = np.asarray(counts)
+    B, N, QB = counts.shape
+    order = np.zeros((B, N, QB), dtype=np.int32)
+    for b in range(B):
+        for n in range(N):
+            order[b, n] = sorted(range(QB), key=lambda j: (-int(counts[b, n, j]), j))
+    return order

@@ -8,6 +8,7 @@ Python binding of the qattn C ABI (include/qattn.h). The kernels live in
                                  causal, band, boolean masks, actual lengths, Dv <= D
 * ``pack_atten_mask_bits``       byte atten_mask -> the bit-packed atten_mask attn_fwd takes
 * ``build_kv_block_list``        128 x 128 block keep mask -> kept kv-block list
+* ``build_qblock_order``         kept counts -> the order in which the sparse kernels take q-blocks
 * ``attn_fwd_blocksparse``       bf16 / fp16 block-sparse attention over a kept list
 * ``quantize_qk_perblock_int8``  Q/K INT8 per 128-token block
 * ``quantize_v_perchannel_fp8``  V FP8 E4M3 per channel
@@ -30,6 +31,7 @@ from .api import (  # noqa: F401
     attn_fwd_blocksparse,
     attn_fwd_qbsa,
     build_kv_block_list,
+    build_qblock_order,
     make_desc,
     pack_atten_mask_bits,
     quantize_qk_perblock_int8,

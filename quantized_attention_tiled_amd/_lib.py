@@ -30,7 +30,7 @@ MAX_SEQS = 256  # QATTN_MAX_SEQS: sequences or padded batches per kernel launch 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "MISALIGNED", 4: "HIP_ERROR"}
 
 # Every symbol include/qattn.h declares.
-EXPORTS = ("attn_fwd", "pack_atten_mask_bits", "build_kv_block_list", "attn_fwd_blocksparse",
+EXPORTS = ("attn_fwd", "pack_atten_mask_bits", "build_qblock_order", "build_kv_block_list", "attn_fwd_blocksparse",
            "quantize_qk_perblock_int8", "quantize_v_perchannel_fp8", "attn_fwd_qbsa", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_bwd_noalloc", "qattn_last_error", "qattn_version")
 NOALLOC_WORKSPACE_BYTES = 32 << 20  # QATTN_NOALLOC_WORKSPACE_BYTES
@@ -70,6 +70,7 @@ class QattnDesc(ctypes.Structure):
         ("Dv", ctypes.c_int32),
         ("actual_seq_lengths", ctypes.POINTER(ctypes.c_int32)),
         ("actual_seq_lengths_kv", ctypes.POINTER(ctypes.c_int32)),
+        ("qblock_order", ctypes.c_void_p),
     ]
 
 
@@ -93,6 +94,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [desc_p, vp, vp, vp, vp, f32p, f32p, vp]
     lib.build_kv_block_list.argtypes = [vp, i32, i32, i32, i32, i32p, i32p, vp]
     lib.pack_atten_mask_bits.argtypes = [vp, ctypes.c_int64, i32, ctypes.c_int64, i32p, vp]
+    lib.build_qblock_order.argtypes = [i32p, i32, i32, i32, i32p, vp]
     lib.attn_fwd_blocksparse.argtypes = [desc_p, vp, vp, vp, vp, f32p, f32p, i32p, i32p, vp]
     lib.attn_bwd.argtypes = [desc_p, vp, vp, vp, vp, vp, f32p, f32p, vp, vp, vp, f32p, vp]
     lib.attn_bwd_noalloc.argtypes = [desc_p, vp, vp, vp, vp, vp, f32p, f32p, vp, vp, vp, vp]
@@ -101,7 +103,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.quantize_qk_perblock_int8.argtypes = [vp, i32, i32, i32, i32, vp, f32p, vp]
     lib.quantize_v_perchannel_fp8.argtypes = [vp, i32, i32, i32, i32, vp, f32p, vp]
     lib.attn_fwd_qbsa.argtypes = [desc_p, vp, vp, vp, f32p, f32p, f32p, i32p, i32p, vp, f32p, f32p, vp]
-    for name in ("attn_fwd", "pack_atten_mask_bits", "build_kv_block_list", "attn_fwd_blocksparse",
+    for name in ("attn_fwd", "pack_atten_mask_bits", "build_qblock_order", "build_kv_block_list", "attn_fwd_blocksparse",
                  "quantize_qk_perblock_int8", "quantize_v_perchannel_fp8", "attn_fwd_qbsa", "attn_bwd",
                  "attn_bwd_noalloc", "qattn_version"):
         getattr(lib, name).restype = ctypes.c_int

@@ -81,7 +81,7 @@ def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: i
               sparse_mode: int = 0, cu_q=None, cu_kv=None, atten_mask: Optional[torch.Tensor] = None,
               mask_kind: int = MASK_SS, head_range=None, qblock_range=None, pre_tokens: int = NO_LIMIT,
               next_tokens: int = NO_LIMIT, dtype: int = DTYPE_BF16, Dv: int = 0, actual_q=None,
-              actual_kv=None) -> QattnDesc:
+              actual_kv=None, qblock_order: Optional[torch.Tensor] = None) -> QattnDesc:
     d = QattnDesc()
     d.struct_size = ctypes.sizeof(QattnDesc)
     d.layout, d.B, d.Nq, d.Nkv, d.Sq, d.Skv, d.D = layout, B, Nq, Nkv, Sq, Skv, D
@@ -96,6 +96,7 @@ def make_desc(*, layout: int, B: int, Nq: int, Nkv: int, Sq: int, Skv: int, D: i
     d.dtype, d.Dv = int(dtype), int(Dv)
     d.actual_seq_lengths = ctypes.cast(actual_q, ctypes.POINTER(ctypes.c_int32)) if actual_q is not None else None
     d.actual_seq_lengths_kv = ctypes.cast(actual_kv, ctypes.POINTER(ctypes.c_int32)) if actual_kv is not None else None
+    d.qblock_order = qblock_order.data_ptr() if qblock_order is not None else None
     return d
 
 
@@ -281,6 +282,24 @@ def pack_atten_mask_bits(atten_mask: torch.Tensor, out: Optional[torch.Tensor] =
     return out
 
 
+def build_qblock_order(counts: torch.Tensor, order: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per (batch, head) of the kept counts int32 [B, N, QB] (from build_kv_block_list) the
+    q-blocks by kept count, largest first, ties in ascending order: int32 [B, N, QB], the
+    ``qblock_order`` of attn_fwd_blocksparse and attn_fwd_qbsa. QB <= 16384."""
+    lib = load()
+    _require(counts, "counts", torch.int32)
+    if counts.dim() != 3:
+        raise ValueError(f"counts must be 3-D [B, N, QB], got shape {tuple(counts.shape)}")
+    B, N, QB = counts.shape
+    if order is None:
+        order = torch.empty((B, N, QB), dtype=torch.int32, device=counts.device)
+    _require(order, "order", torch.int32, (B, N, QB))
+    _placed(counts.device, counts=counts, order=order)
+    with torch.cuda.device(counts.device):
+        check(lib.build_qblock_order(_vp(counts), B, N, QB, _vp(order), _stream(counts.device)))
+    return order
+
+
 def build_kv_block_list(keep: torch.Tensor, counts: Optional[torch.Tensor] = None,
                         idx: Optional[torch.Tensor] = None):
     """Kept-block list of a block keep mask uint8 [B, N, QB, KB] (nonzero = keep).
@@ -307,9 +326,12 @@ def build_kv_block_list(keep: torch.Tensor, counts: Optional[torch.Tensor] = Non
 
 def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range=None, qblock_range=None,
                          out=None, softmax_max=None, softmax_sum=None, layout: str = "BNSD",
-                         head_num: Optional[int] = None, actual_seq_lengths=None, actual_seq_lengths_kv=None):
+                         head_num: Optional[int] = None, actual_seq_lengths=None, actual_seq_lengths_kv=None,
+                         qblock_order: Optional[torch.Tensor] = None):
     """Block-sparse attention over a kept-block list on bfloat16 or float16 q, k, v (BNSD, BSND,
-    BSH or SBH, shapes and Dv as for attn_fwd); returns (out, m [B, Nq, Sq], l)."""
+    BSH or SBH, shapes and Dv as for attn_fwd); returns (out, m [B, Nq, Sq], l).
+    ``qblock_order``: optional int32 [B, Nq, QB] from build_qblock_order (the order in which each
+    head's q-blocks are taken; each row then walks its kept blocks from the first)."""
     lib = load()
     dev = q.device
     dtype = _check_dtypes(q, k, v)
@@ -319,6 +341,8 @@ def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range
     QB, KB = (Sq + BLOCK - 1) // BLOCK, (Skv + BLOCK - 1) // BLOCK
     _require(counts, "counts", torch.int32, (B, Nq, QB))
     _require(idx, "idx", torch.int32, (B, Nq, QB, KB))
+    if qblock_order is not None:
+        _require(qblock_order, "qblock_order", torch.int32, (B, Nq, QB))
     out, softmax_max, softmax_sum = _outputs(q, out, softmax_max, softmax_sum, (B, Nq, Sq), o_shape)
     _require(out, "out", q.dtype, o_shape)
     _require(softmax_max, "softmax_max", torch.float32, (B, Nq, Sq))
@@ -326,10 +350,11 @@ def attn_fwd_blocksparse(q, k, v, counts, idx, *, scale: float = 1.0, head_range
     # host arrays, alive until the call returns
     aq_arr = _lengths(actual_seq_lengths, B, "actual_seq_lengths")
     akv_arr = _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv")
-    _placed(dev, q=q, k=k, v=v, counts=counts, idx=idx, out=out, softmax_max=softmax_max, softmax_sum=softmax_sum)
+    _placed(dev, q=q, k=k, v=v, counts=counts, idx=idx, out=out, softmax_max=softmax_max, softmax_sum=softmax_sum,
+            qblock_order=qblock_order)
     desc = make_desc(layout=lay, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
                      head_range=head_range, qblock_range=qblock_range, dtype=dtype, Dv=Dv,
-                     actual_q=aq_arr, actual_kv=akv_arr)
+                     actual_q=aq_arr, actual_kv=akv_arr, qblock_order=qblock_order)
     with torch.cuda.device(dev):
         check(lib.attn_fwd_blocksparse(ctypes.byref(desc), _vp(q), _vp(k), _vp(v), _vp(out), _vp(softmax_max),
                                        _vp(softmax_sum), _vp(counts), _vp(idx), _stream(dev)))
@@ -380,9 +405,12 @@ def quantize_v_perchannel_fp8(v: torch.Tensor, v_q: Optional[torch.Tensor] = Non
 
 def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scale: float,
                   head_range=None, qblock_range=None, out=None, softmax_max=None, softmax_sum=None,
-                  return_softmax: bool = True, actual_seq_lengths=None, actual_seq_lengths_kv=None):
+                  return_softmax: bool = True, actual_seq_lengths=None, actual_seq_lengths_kv=None,
+                  qblock_order: Optional[torch.Tensor] = None):
     """Quantised block-sparse attention (BNSD); returns (out, m, l) or (out, None, None).
-    ``actual_seq_lengths`` / ``actual_seq_lengths_kv``: per-batch valid lengths, as for attn_fwd."""
+    ``actual_seq_lengths`` / ``actual_seq_lengths_kv``: per-batch valid lengths, as for attn_fwd.
+    ``qblock_order``: optional int32 [B, Nq, QB] from build_qblock_order (the order in which each
+    head's q-blocks are taken; the results are the same bits either way)."""
     lib = load()
     dev = q_q.device
     _require(q_q, "q_q", torch.int8)
@@ -400,6 +428,8 @@ def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scal
     _require(v_scale, "v_scale", torch.float32, (B, Nkv, D))
     _require(counts, "counts", torch.int32, (B, Nq, QB))
     _require(idx, "idx", torch.int32, (B, Nq, QB, KB))
+    if qblock_order is not None:
+        _require(qblock_order, "qblock_order", torch.int32, (B, Nq, QB))
     if out is None:
         out = torch.empty(q_q.shape, dtype=torch.bfloat16, device=dev)
     _require(out, "out", torch.bfloat16, (B, Nq, Sq, D))
@@ -415,9 +445,10 @@ def attn_fwd_qbsa(q_q, k_q, v_q, q_scale, k_scale, v_scale, counts, idx, *, scal
     aq_arr = _lengths(actual_seq_lengths, B, "actual_seq_lengths")
     akv_arr = _lengths(actual_seq_lengths_kv, B, "actual_seq_lengths_kv")
     _placed(dev, q_q=q_q, k_q=k_q, v_q=v_q, q_scale=q_scale, k_scale=k_scale, v_scale=v_scale, counts=counts,
-            idx=idx, out=out, softmax_max=softmax_max, softmax_sum=softmax_sum)
+            idx=idx, out=out, softmax_max=softmax_max, softmax_sum=softmax_sum, qblock_order=qblock_order)
     desc = make_desc(layout=LAYOUT_BNSD, B=B, Nq=Nq, Nkv=Nkv, Sq=Sq, Skv=Skv, D=D, scale=scale,
-                     head_range=head_range, qblock_range=qblock_range, actual_q=aq_arr, actual_kv=akv_arr)
+                     head_range=head_range, qblock_range=qblock_range, actual_q=aq_arr, actual_kv=akv_arr,
+                     qblock_order=qblock_order)
     with torch.cuda.device(dev):
         check(lib.attn_fwd_qbsa(ctypes.byref(desc), _vp(q_q), _vp(k_q), _vp(v_q), _vp(q_scale), _vp(k_scale),
                                 _vp(v_scale), _vp(counts), _vp(idx), _vp(out), _vp(softmax_max), _vp(softmax_sum),
@@ -545,5 +576,5 @@ def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
 
 
 __all__ = ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_qbsa", "build_kv_block_list",
-           "pack_atten_mask_bits", "quantize_qk_perblock_int8",
+           "build_qblock_order", "pack_atten_mask_bits", "quantize_qk_perblock_int8",
            "quantize_v_perchannel_fp8", "make_desc", "_lib"]

@@ -241,6 +241,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
     const int rem = item - b * per_b;
     h = p.h0 + rem / p.tiles_per_head;
     qblk = p.qb0 + (rem % p.tiles_per_head) * NQB;
+    if constexpr ((MODE & kSparse) != 0) {
+      // a q-block order: the head's q-blocks in that order, the ones outside the subrange skipped
+      if (p.qb_order) {
+        qblk = p.qb_order[((int64_t)b * p.Nq + h) * p.QB + rem % p.tiles_per_head];
+        if (qblk < p.qb0 || qblk >= p.qb1) return;
+      }
+    }
     nsub = min(NQB, p.qb1 - qblk);
     Lq = p.actual ? p.cu_q[b] : p.Sq;  // per-batch actual lengths of a padded batch
     Lkv = p.actual ? p.cu_kv[b] : p.Skv;
@@ -290,8 +297,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
     // about equally long, so the workgroups of one generation start together, and rotated starts
     // would then spread them over the whole kv range (full density, S = 64K: 83.3 -> 76.6 ms; at
     // 0.9 kept both orders take the same time, below it the rotation wins).
+    // With a q-block order (q-blocks of similar kept counts running together, started together)
+    // every row walks from kv-block 0, so rows that run together move through the same blocks.
     const int64_t prow = ((int64_t)(p.b0 + b) * p.Nq + h) * p.QB + qblk;
-    const int64_t start_blk = 10 * nkept > 9 * p.KB ? 0 : (prow * ((p.KB + 63) / 64)) % max(p.KB, 1);
+    const int64_t start_blk =
+        (p.qb_order || 10 * nkept > 9 * p.KB) ? 0 : (prow * ((p.KB + 63) / 64)) % max(p.KB, 1);
     kept0 = (int)((start_blk * nkept) / max(p.KB, 1));
   } else {
     ntiles = kv_end > t0 * kKT ? (kv_end - t0 * kKT + kKT - 1) / kKT : 0;

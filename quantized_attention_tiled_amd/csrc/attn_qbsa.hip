@@ -121,7 +121,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_qbsa_kernel(const FwdParams 
   const int b = item / per_b;
   const int rem = item - b * per_b;
   const int h = p.h0 + rem / p.tiles_per_head;
-  const int qb = p.qb0 + rem % p.tiles_per_head;
+  // a q-block order: the head's q-blocks in that order, the ones outside the subrange skipped
+  const int qb = p.qb_order ? p.qb_order[((int64_t)b * p.Nq + h) * p.QB + rem % p.tiles_per_head]
+                            : p.qb0 + rem % p.tiles_per_head;
+  if (qb < p.qb0 || qb >= p.qb1) return;
   const int g = h / p.group;
   // per-batch actual lengths of a padded batch; rows from row_end to row_limit are padding and
   // come out as rows with no key

@@ -54,6 +54,10 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
     return fail(QATTN_INVALID_ARGUMENT, "pre_tokens / next_tokens set the sparse_mode 0 range only");
   if (!allow_masks && (d->sparse_mode != 0 || d->atten_mask != nullptr || band))
     return fail(QATTN_UNSUPPORTED, "block-sparse entry points take no causal mode, band or atten_mask");
+  if (d->qblock_order && allow_masks)
+    return fail(QATTN_INVALID_ARGUMENT, "qblock_order applies to the block-sparse entry points only");
+  if (reinterpret_cast<uintptr_t>(d->qblock_order) & 3u)
+    return fail(QATTN_MISALIGNED, "qblock_order must be 4-byte aligned");
   const int mask_shape = d->mask_kind & ~QATTN_MASK_BITS;
   const bool mask_bits = (d->mask_kind & QATTN_MASK_BITS) != 0;
   if (d->atten_mask != nullptr) {
@@ -184,6 +188,7 @@ int setup_common(const qattn_desc* d, qattn::FwdParams& p, bool allow_tnd, bool 
   if (h0 < 0 || h1 > d->Nq || h0 > h1) return fail(QATTN_INVALID_ARGUMENT, "head range [%d, %d) outside [0, %d)", h0, h1, d->Nq);
   if (b0 < 0 || b1 > qblocks || b0 > b1)
     return fail(QATTN_INVALID_ARGUMENT, "q-block range [%d, %d) outside [0, %d)", b0, b1, qblocks);
+  p.qb_order = d->qblock_order;
   p.h0 = h0;
   p.nh = h1 - h0;
   p.qb0 = b0;
@@ -238,7 +243,9 @@ int finish_items(qattn::FwdParams& p, int per_tile) {
     p.tiles_per_head = 0;
     items = (int64_t)tiles * p.nh;
   } else {
-    p.tiles_per_head = (nqb + per_tile - 1) / per_tile;
+    // with a q-block order the grid covers every q-block of a head (those outside the subrange
+    // exit at once), so that the order, not the subrange, decides which run together
+    p.tiles_per_head = p.qb_order ? p.QB : (nqb + per_tile - 1) / per_tile;
     p.total_tiles = 0;
     items = (int64_t)p.B * p.nh * p.tiles_per_head;
   }
@@ -312,6 +319,7 @@ bool fill_group(const qattn_desc* d, const qattn::FwdParams& full, int g0, int g
   p.mask = at(p.mask, p.mask_sb);
   p.counts = at(p.counts, (int64_t)p.Nq * p.QB);
   p.idx = at(p.idx, (int64_t)p.Nq * p.QB * p.KB);
+  p.qb_order = at(p.qb_order, (int64_t)p.Nq * p.QB);
   p.q_scale = at(p.q_scale, (int64_t)p.Nq * p.QB);
   p.k_scale = at(p.k_scale, (int64_t)p.Nkv * p.KB);
   p.v_scale = at(p.v_scale, (int64_t)p.Nkv * p.D);
@@ -392,6 +400,17 @@ int pack_atten_mask_bits(const uint8_t* mask, int64_t rows, int Skv, int64_t mas
   if (rows > ((int64_t)1 << 40) / ((Skv + 31) / 32)) return fail(QATTN_UNSUPPORTED, "mask too large for one launch");
   return hip_status(qattn::launch_mask_pack(mask, rows, Skv, mask_row_stride, bits, (hipStream_t)stream),
                     "pack_atten_mask_bits launch");
+}
+
+int build_qblock_order(const int32_t* counts, int B, int N, int QB, int32_t* order, void* stream) {
+  if (B < 0 || N < 0 || QB < 0) return fail(QATTN_INVALID_ARGUMENT, "negative size");
+  if (QB > 16384) return fail(QATTN_UNSUPPORTED, "QB=%d above 16384", QB);
+  if ((int64_t)B * N * QB == 0) return QATTN_OK;
+  if (!counts || !order) return fail(QATTN_INVALID_ARGUMENT, "counts and order must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(counts) & 3u) || (reinterpret_cast<uintptr_t>(order) & 3u))
+    return fail(QATTN_MISALIGNED, "counts and order must be 4-byte aligned");
+  return hip_status(qattn::launch_qblock_order(counts, B, N, QB, order, (hipStream_t)stream),
+                    "build_qblock_order launch");
 }
 
 int build_kv_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32_t* counts, int32_t* idx,

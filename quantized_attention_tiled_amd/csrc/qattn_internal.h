@@ -73,6 +73,10 @@ struct FwdParams {
   // with the sequences in `order` by tile count, descending; 0 keeps the sequence order
   int level_order;
   uint8_t order[kMaxSeqs];
+  // block-sparse and quantised launches: per (batch, head) the order in which its q-blocks are
+  // taken ([B, Nq, QB], NULL = ascending; the grid then covers every q-block of a head and the
+  // work of one outside [qb0, qb1) is skipped)
+  const int32_t* qb_order;
 };
 
 // Everything a backward launch needs (any layout, bf16 or fp16), passed by value.
@@ -138,6 +142,7 @@ hipError_t launch_quant_v(const uint16_t* v, int B, int N, int S, int D, uint8_t
                           hipStream_t stream);
 hipError_t launch_block_list(const uint8_t* keep, int B, int N, int QB, int KB, int32_t* counts, int32_t* idx,
                              hipStream_t stream);
+hipError_t launch_qblock_order(const int32_t* counts, int B, int N, int QB, int32_t* order, hipStream_t stream);
 
 // Workgroups are handed to the 8 XCDs round-robin by block index. Give every
 // XCD a contiguous run of work items so the items that run together on one

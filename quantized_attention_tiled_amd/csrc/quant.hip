@@ -180,7 +180,36 @@ __global__ __launch_bounds__(kThreads) void block_list_kernel(const uint8_t* __r
   if (lane == 0) counts[row] = n;
 }
 
+// One workgroup per (batch, head) row of the kept counts: the q-blocks sorted by count, largest
+// first, ties in ascending q-block order, by counting for each q-block the ones that go before it
+// (QB <= 16384 counts staged in LDS, read by every thread in the same order).
+__global__ __launch_bounds__(kThreads) void qblock_order_kernel(const int32_t* __restrict__ counts, int QB,
+                                                                int32_t* __restrict__ order) {
+  extern __shared__ int32_t cnt[];
+  const int32_t* c = counts + (int64_t)blockIdx.x * QB;
+  int32_t* out = order + (int64_t)blockIdx.x * QB;
+  for (int i = threadIdx.x; i < QB; i += kThreads) cnt[i] = c[i];
+  __syncthreads();
+  for (int j = threadIdx.x; j < QB; j += kThreads) {
+    const int cj = cnt[j];
+    int rank = 0;
+    for (int i = 0; i < QB; i++) {
+      const int ci = cnt[i];
+      rank += (ci > cj) || (ci == cj && i < j);
+    }
+    out[rank] = j;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_qblock_order(const int32_t* counts, int B, int N, int QB, int32_t* order, hipStream_t stream) {
+  const int64_t rows = (int64_t)B * N;
+  if (rows == 0 || QB == 0) return hipSuccess;
+  hipLaunchKernelGGL(qblock_order_kernel, dim3((unsigned)rows), dim3(kThreads), (size_t)QB * sizeof(int32_t), stream,
+                     counts, QB, order);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_qk(const uint16_t* x, int B, int N, int S, int D, int8_t* xq, float* scale,
                            hipStream_t stream) {

@@ -19,6 +19,7 @@ hipError_t launch_quant_v(const uint16_t*, int, int, int, int, uint8_t*, float*,
 hipError_t launch_block_list(const uint8_t*, int, int, int, int, int32_t*, int32_t*, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t launch_qblock_order(const int32_t*, int, int, int, int32_t*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_mask_pack(const uint8_t*, int64_t, int, int64_t, int32_t*, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace qattn

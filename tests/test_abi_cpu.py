@@ -190,6 +190,24 @@ def test_pack_mask_validation(q):
     assert b"aligned" in lib.qattn_last_error()
 
 
+def test_qblock_order_validation(q):
+    lib = q.load()
+    assert lib.build_qblock_order(FAKE, 0, 4, 8, FAKE, None) == 0      # nothing to do
+    assert lib.build_qblock_order(None, 1, 4, 8, FAKE, None) == 1
+    assert lib.build_qblock_order(FAKE, 1, 4, 8, None, None) == 1
+    assert lib.build_qblock_order(FAKE, -1, 4, 8, FAKE, None) == 1
+    assert lib.build_qblock_order(FAKE, 1, 4, 16385, FAKE, None) == 2   # QB above 16384
+    assert lib.build_qblock_order(FAKE + 2, 1, 4, 8, FAKE, None) == 3
+    # the descriptor's qblock_order: block-sparse entry points only, 4-byte aligned
+    d = _desc(q)
+    d.qblock_order = FAKE
+    assert _fwd(q, d) == 1 and b"block-sparse" in lib.qattn_last_error()
+    assert lib.attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    d = _desc(q, Nkv=4)
+    d.qblock_order = FAKE + 2
+    assert lib.attn_fwd_blocksparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 3
+
+
 def test_backward_validation(q):
     lib = q.load()
 

@@ -153,3 +153,13 @@ def test_pack_mask_buffers():
     with pytest.raises(TypeError):
         api.pack_atten_mask_bits(z((4, 70), f32))
     raises_shape("Sq, Skv", api.pack_atten_mask_bits, z((70,), u8))
+
+
+def test_qblock_order_buffers():
+    c = z((1, 2, 4), i32)
+    raises_device(api.build_qblock_order, c)
+    raises_shape("order", api.build_qblock_order, c, order=z((1, 2, 5), i32))
+    raises_shape("3-D", api.build_qblock_order, z((2, 4), i32))
+    q = k = v = z((1, 2, 512, 64), bf16)
+    counts, idx = z((1, 2, 4), i32), z((1, 2, 4, 4), i32)
+    raises_shape("qblock_order", api.attn_fwd_blocksparse, q, k, v, counts, idx, qblock_order=z((1, 2, 3), i32))

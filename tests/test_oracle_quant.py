@@ -161,3 +161,28 @@ def test_kept_list_properties():
         row = idx[b, n, qb]
         assert np.all(np.diff(row[:c]) > 0) and np.all(row[c:] == -1)
         assert np.all(keep[b, n, qb, row[:c]] == 1)
+
+
+def test_qblock_order_hand_worked():
+    """Counts 3, 7, 3, 0, 7 -> q-blocks 1, 4 (count 7, in index order), 0, 2 (count 3), 3."""
+    from oracle import qblock_order
+    o = qblock_order(np.array([[[3, 7, 3, 0, 7]]]))
+    assert o.tolist() == [[[1, 4, 0, 2, 3]]]
+
+
+def test_qblock_order_properties_and_stable_argsort():
+    """A permutation per row, counts non-increasing along it, ties in ascending index; equal to
+    numpy's stable argsort of the negated counts (an independent library routine)."""
+    from oracle import qblock_order
+    rng = np.random.default_rng(12)
+    c = rng.integers(0, 6, size=(2, 3, 40))
+    o = qblock_order(c)
+    for b in range(2):
+        for n in range(3):
+            row = o[b, n]
+            assert sorted(row.tolist()) == list(range(40))
+            cs = c[b, n][row]
+            assert np.all(cs[:-1] >= cs[1:])
+            ties = cs[:-1] == cs[1:]
+            assert np.all(row[:-1][ties] < row[1:][ties])
+            np.testing.assert_array_equal(row, np.argsort(-c[b, n], kind="stable"))
