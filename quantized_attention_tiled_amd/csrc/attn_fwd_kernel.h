@@ -156,7 +156,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock * NQB, (fwd_blocks_per_cu<D, NQ
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  const int item = xcd_remap(blockIdx.x, gridDim.x, p.total_items);
+  const int item = (MODE & kSparse) != 0 ? xcd_remap_chunks(blockIdx.x, p.total_items)
+                                         : xcd_remap(blockIdx.x, gridDim.x, p.total_items);
   if (item < 0) return;
 
   // ---- which (batch, head) and q-blocks qblk .. qblk + nsub - 1 this workgroup owns ----
@@ -875,7 +876,7 @@ template <typename E, int D, int DV, int MODE, int NQB>
 hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   static_assert(NQB == 1 || D <= 128, "beyond D = 128 a workgroup holds one q-block");
   if (p.qblocks_per_tile != NQB) return hipErrorInvalidValue;
-  const int grid = grid_for_items(p.total_items);
+  const int grid = (MODE & kSparse) != 0 ? grid_for_chunks(p.total_items) : grid_for_items(p.total_items);
   hipLaunchKernelGGL((attn_fwd_kernel<E, D, DV, MODE, NQB>), dim3(grid), dim3(64 * kWavesPerBlock * NQB), 0, stream,
                      p);
   return hipGetLastError();

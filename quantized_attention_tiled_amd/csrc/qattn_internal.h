@@ -156,6 +156,23 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid, int total) {
 
 inline int grid_for_items(int total) { return ((total + 7) / 8) * 8; }
 
+// The block-sparse bf16 launches deal items out in chunks of 64, about the
+// workgroups one XCD runs at once: chunk c of all 8 XCDs covers items
+// [512 c, 512 c + 512), XCD x taking the 64 that start at ((x + c) mod 8) * 64.
+// The whole chip then works on about 512 consecutive items (one or two heads),
+// whose K/V stay in the memory-side cache, where a contiguous share per XCD has
+// the 8 XCDs on 8 different heads; each XCD still runs consecutive items
+// together. The rotation moves each slice of a chunk to another XCD from one
+// chunk to the next, so no XCD always draws the heaviest rows of a q-block
+// order by kept count. The grid is a multiple of 512; returns -1 past `total`.
+__device__ __forceinline__ int xcd_remap_chunks(int bid, int total) {
+  const int x = bid & 7, s = bid >> 3, c = s >> 6;
+  const int item = (c * 8 + ((x + c) & 7)) * 64 + (s & 63);
+  return item < total ? item : -1;
+}
+
+inline int grid_for_chunks(int total) { return ((total + 511) / 512) * 512; }
+
 // Raw buffer resource of the gfx9 family as four SGPRs: base address, no stride, `bytes` valid
 // bytes (reads past them return zeros), dword data format.
 typedef int rsrc4 __attribute__((ext_vector_type(4)));
