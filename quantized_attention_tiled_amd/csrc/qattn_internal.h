@@ -156,22 +156,22 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid, int total) {
 
 inline int grid_for_items(int total) { return ((total + 7) / 8) * 8; }
 
-// The block-sparse bf16 launches deal items out in chunks of 64, about the
+// The block-sparse bf16 launches deal items out in chunks of 32, half of the
 // workgroups one XCD runs at once: chunk c of all 8 XCDs covers items
-// [512 c, 512 c + 512), XCD x taking the 64 that start at ((x + c) mod 8) * 64.
+// [256 c, 256 c + 256), XCD x taking the 32 that start at ((x + c) mod 8) * 32.
 // The whole chip then works on about 512 consecutive items (one or two heads),
 // whose K/V stay in the memory-side cache, where a contiguous share per XCD has
-// the 8 XCDs on 8 different heads; each XCD still runs consecutive items
-// together. The rotation moves each slice of a chunk to another XCD from one
-// chunk to the next, so no XCD always draws the heaviest rows of a q-block
-// order by kept count. The grid is a multiple of 512; returns -1 past `total`.
+// the 8 XCDs on 8 different heads; each XCD still works on runs of consecutive
+// items at once. The rotation moves each slice of a chunk to another XCD from
+// one chunk to the next, so no XCD always draws the heaviest rows of a q-block
+// order by kept count. The grid is a multiple of 256; returns -1 past `total`.
 __device__ __forceinline__ int xcd_remap_chunks(int bid, int total) {
-  const int x = bid & 7, s = bid >> 3, c = s >> 6;
-  const int item = (c * 8 + ((x + c) & 7)) * 64 + (s & 63);
+  const int x = bid & 7, s = bid >> 3, c = s >> 5;
+  const int item = (c * 8 + ((x + c) & 7)) * 32 + (s & 31);
   return item < total ? item : -1;
 }
 
-inline int grid_for_chunks(int total) { return ((total + 511) / 512) * 512; }
+inline int grid_for_chunks(int total) { return ((total + 255) / 256) * 256; }
 
 // Raw buffer resource of the gfx9 family as four SGPRs: base address, no stride, `bytes` valid
 // bytes (reads past them return zeros), dword data format.
