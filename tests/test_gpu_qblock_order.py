@@ -7,6 +7,8 @@
 * The bf16 block-sparse kernel walks each row's kept blocks from the first when given the order:
   its outputs match the oracle, and subrange launches with the order reproduce the full ordered
   call bit for bit and write nothing outside their slice.
+* A bf16 block-sparse launch of 350 items (more than one chunk of 256 over the 8 XCDs, not a
+  multiple of it) writes every row and matches the oracle, with and without the order.
 """
 
 import numpy as np
@@ -141,3 +143,35 @@ def test_bsa_with_order_against_oracle_and_subranges(qa):
                                     qblock_range=qr, out=out, softmax_max=m, softmax_sum=l)
             torch.cuda.synchronize()
     _same(full, (out, m, l))
+
+
+@pytest.mark.parametrize("ordered", [False, True])
+def test_bsa_ragged_item_count(qa, ordered):
+    """350 items (5 heads of 70 q-blocks, the last one ragged): more than one chunk of 256 items
+    over the 8 XCDs and not a multiple of it. Every row is written, and sampled q-blocks of every
+    head match the oracle."""
+    B, N, D = 1, 5, 128
+    S = 70 * 128 - 37
+    QB = (S + 127) // 128
+    banner(f"BSA over {N * QB} items, S={S}, q-block order {ordered}")
+    qb_, kb_, vb_ = (random_bf16(340 + i, (B, N, S, D)) for i in range(3))
+    keep_np = make_block_keep(343, B, N, QB, QB, 0.1)
+    q, k, v = dev_bf16(qb_), dev_bf16(kb_), dev_bf16(vb_)
+    counts, idx = qa.build_kv_block_list(torch.from_numpy(keep_np).cuda())
+    order = qa.build_qblock_order(counts) if ordered else None
+    out = torch.full((B, N, S, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    m = torch.full((B, N, S), float("nan"), dtype=torch.float32, device="cuda")
+    l = torch.full((B, N, S), float("nan"), dtype=torch.float32, device="cuda")
+    qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=0.09, qblock_order=order, out=out, softmax_max=m,
+                            softmax_sum=l)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any() and not torch.isnan(m).any() and not torch.isnan(l).any()
+    o_np = out.float().cpu().numpy().astype(np.float64)
+    m_np, l_np = to_np(m), to_np(l)
+    sample = [0, 1, 33, QB - 2, QB - 1]
+    rows = np.concatenate([np.arange(j * 128, min(S, (j + 1) * 128)) for j in sample])
+    for h in range(N):
+        ro, rm, rl = oracle.attention_block_sparse(f64(qb_[0, h]), f64(kb_[0, h]), f64(vb_[0, h]), 0.09,
+                                                   keep_np[0, h], qblocks=sample)
+        check_o(o_np[0, h][rows], ro, O_TOL_BF16)
+        check_ml(m_np[0, h][rows], l_np[0, h][rows], rm, rl)
