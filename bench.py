@@ -309,7 +309,7 @@ def sustained_clock_power(step, step_ms, seconds=3.0, settle=1.0):
             "samples_t_s_mhz_w": samples}
 
 
-def operator_sweep(seqs, sparsities=(0.0, 0.5, 0.9), reps=5):
+def operator_sweep(seqs, sparsities=(0.0, 0.5, 0.9), reps=5, qblock_order=True):
     """The single-operator sweep of the EagleQBSA article (section 4, Fig. 4.1) on this GPU: B=1,
     N=40, D=128, for each S and block sparsity: bf16 dense attention, bf16 block-sparse attention
     (BSA) and the quantised block-sparse kernel (QBSA; Q, K, V quantised beforehand, untimed).
@@ -358,12 +358,13 @@ def operator_sweep(seqs, sparsities=(0.0, 0.5, 0.9), reps=5):
             keep = (torch.rand(B, N, QB, QB, generator=gen, device=dev) >= sp).to(torch.uint8)
             keep[:, :, torch.arange(QB), torch.arange(QB)] = 1
             counts, idx = qa.build_kv_block_list(keep)
+            order = qa.build_qblock_order(counts) if qblock_order else None
             kept = float(keep.float().mean())
             ex = 4 * D * 128 * 128 * int(keep.sum())
             t_bsa = timed(lambda: qa.attn_fwd_blocksparse(q, k, v, counts, idx, scale=scale, out=o, softmax_max=m,
-                                                          softmax_sum=l))
+                                                          softmax_sum=l, qblock_order=order))
             t_q = timed(lambda: qa.attn_fwd_qbsa(qq, kq, vq, qs, ks, vs, counts, idx, scale=scale, out=o, softmax_max=m,
-                                                 softmax_sum=l))
+                                                 softmax_sum=l, qblock_order=order))
             for kern, t, peak in (("bf16_bsa", t_bsa, PEAK_BF16), ("qbsa", t_q, PEAK_FP8)):
                 print(json.dumps({"sweep": "operator", "S": S, "sparsity": sp, "kept_fraction": round(kept, 4),
                                   "kernel": kern, "ms": round(t, 4), "executed_tflops": round(ex / t / 1e9, 1),
@@ -610,7 +611,7 @@ def main(argv=None):
         copy_calibration(a.copy_calibration)
         return 0
     if a.sweep:
-        return operator_sweep([int(x) for x in a.sweep_seqs.split(",") if x])
+        return operator_sweep([int(x) for x in a.sweep_seqs.split(",") if x], qblock_order=not a.no_qblock_order)
     if a.backward:
         return backward_bench(a)
     if a.power_study:
